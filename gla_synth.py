@@ -1,0 +1,98 @@
+"""Seeded synthetic inputs for the key-only GLA token mixer.
+
+This module only draws random numbers. It holds none of the mixer's arithmetic,
+and both sides of every parity check (the HIP path and the fp64 oracle) take
+their inputs from here.
+
+The workloads stand in for GTR's activations. The pages measure the operator in
+isolation at 256, 1.6K and 16.4K tokens (GTR summary page, section 实验结果 and
+its table of results; the 0539edu.com page, section 3.3), and real activations
+would need trained weights and images, so every input here is synthetic.
+Tokens are the positions of the stride-16 patch grid, so L = grid_h * grid_w.
+
+Recipe (numpy PCG64, ``default_rng(seed)``). q, k, v and g are drawn in that
+order, each standard normal float32 in layout [B, L, H, d].
+  * fp16 workloads: q, k, v are scaled by ``qkv_std`` (1/8 = 1/sqrt(64));
+    log_gamma = logsigmoid(g + gate_mu) / 16, evaluated in float32.
+    The 1/16 is the gate temperature tau = 16 of the low-rank gate
+    gamma = sigmoid(.)^(1/tau) (summary page, section 核心方法).
+    Everything is then rounded to fp16 (round-to-nearest-even).
+  * fp32 workload ("tiny"): the same, without the 1/8 and without rounding.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+from typing import Dict, Tuple
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    grid_h: int
+    grid_w: int
+    d_k: int
+    d_v: int
+    dtype: str          # "fp16" or "fp32"
+    seed: int
+    qkv_std: float = 0.125
+    gate_mu: float = 0.0
+    chunk: int = 64
+    note: str = ""
+
+    @property
+    def L(self) -> int:
+        return self.grid_h * self.grid_w
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w for w in [
+        Workload("tiny", 1, 1, 16, 16, 32, 32, "fp32", 0, qkv_std=1.0,
+                 note="256-token oracle check, fp32"),
+        Workload("img640", 1, 6, 40, 40, 64, 64, "fp16", 1,
+                 note="640x640 image, 1600 tokens, 6 heads"),
+        Workload("img1024", 1, 12, 64, 64, 64, 64, "fp16", 2,
+                 note="1024x1024 image, 4096 tokens, 12 heads"),
+        Workload("batched640", 8, 6, 40, 40, 64, 64, "fp16", 3,
+                 note="batch 8 of 640x640 images"),
+        Workload("long2048", 1, 12, 128, 128, 64, 64, "fp16", 4,
+                 note="2048x2048 image, 16384 tokens, 12 heads"),
+        Workload("long2048_near1", 1, 12, 128, 128, 64, 64, "fp16", 5, gate_mu=3.0,
+                 note="16384 tokens with gates near 1 (long memory)"),
+    ]
+}
+
+
+def _logsigmoid_f32(x: np.ndarray) -> np.ndarray:
+    x = x.astype(np.float32)
+    return (np.minimum(x, np.float32(0)) - np.log1p(np.exp(-np.abs(x)))).astype(np.float32)
+
+
+def generate(w: Workload) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Return (q, k, v, log_gamma) as numpy arrays in [B, L, H, d] layout and w.dtype."""
+    rng = np.random.default_rng(w.seed)
+    shp_k = (w.B, w.L, w.H, w.d_k)
+    shp_v = (w.B, w.L, w.H, w.d_v)
+    q = rng.standard_normal(shp_k, dtype=np.float32)
+    k = rng.standard_normal(shp_k, dtype=np.float32)
+    v = rng.standard_normal(shp_v, dtype=np.float32)
+    g = rng.standard_normal(shp_k, dtype=np.float32)
+    lg = _logsigmoid_f32(g + np.float32(w.gate_mu)) / np.float32(16.0)
+    if w.dtype == "fp16":
+        s = np.float32(w.qkv_std)
+        return ((q * s).astype(np.float16), (k * s).astype(np.float16),
+                (v * s).astype(np.float16), lg.astype(np.float16))
+    if w.dtype == "fp32":
+        s = np.float32(w.qkv_std)
+        return (q * s), (k * s), (v * s), lg
+    raise ValueError(f"unknown dtype {w.dtype}")
+
+
+def np_dtype(w: Workload):
+    return np.float16 if w.dtype == "fp16" else np.float32
