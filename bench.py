@@ -1,0 +1,265 @@
+"""Benchmark of the key-only GLA forward (libgtrgla) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload img640]
+
+A step is one pass of the hot path over one batch: the four scan-order calls
+(left->right, right->left, top->bottom, bottom->top) that four consecutive GTR
+blocks make, each on its own input tensors. Inputs are synthetic
+(gla_synth, seeded) and already resident in HBM when timing starts. They are
+rotated over at least 512 MiB of distinct buffers so that the 256 MB Infinity
+Cache cannot serve them from a previous call.
+
+Prints ONE JSON line. `value` is tokens/s over the timed steps: calls x B x L
+tokens divided by the wall time between two events on the stream the kernels
+run on. `roofline` covers the dominant kernel: algorithmic bytes per launch
+(inputs read once, outputs written once) divided by the mean launch duration
+from per-call HIP events, against the 8 TB/s HBM peak. `cpu_baseline` times
+the fp64 oracle on this host for a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0
+ROTATE_BYTES = 512 << 20     # 2x the Infinity Cache
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+DIRS = (0, 1, 2, 3)
+
+
+def alg_bytes(w) -> int:
+    """Bytes the method must move per call: read q, k, v, log_gamma, write o and final_state."""
+    s = 2 if w.dtype == "fp16" else 4
+    rows = w.B * w.L * w.H
+    return rows * (3 * w.d_k + 2 * w.d_v) * s + w.B * w.H * w.d_k * w.d_v * 4
+
+
+def mfma_flops(w) -> int:
+    """Full-tile MFMA FLOPs per call: scores, A.V, Q.S and K^T.V per 64-token chunk."""
+    C = w.chunk
+    return w.B * w.H * w.L * (2 * C * (w.d_k + w.d_v) + 4 * w.d_k * w.d_v)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "chunkwise_gated_recurrence_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None if
+    they were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_hash") != kernel_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def run_workload(w, steps: int, warmup: int, rotate: bool):
+    import numpy as np
+    import torch
+
+    import chunkwise_gated_recurrence_amd as gla
+    import gla_synth
+
+    arrays = gla_synth.generate(w)
+    per_call = alg_bytes(w)
+    nsets = max(len(DIRS), math.ceil(ROTATE_BYTES / per_call)) if rotate else len(DIRS)
+    dev = torch.device("cuda:0")
+    base = [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in arrays]
+    sets = []
+    for i in range(nsets):
+        ins = base if i == 0 else [t.clone() for t in base]
+        out = torch.empty((w.B, w.L, w.H, w.d_v), dtype=base[0].dtype, device=dev)
+        fs = torch.empty((w.B, w.H, w.d_k, w.d_v), dtype=torch.float32, device=dev)
+        sets.append((ins, out, fs))
+    fn = gla.gtr_gla_fwd if w.dtype == "fp16" else gla.gtr_gla_fwd_f32
+    stream = torch.cuda.current_stream()
+
+    def call(i, d):
+        (q, k, v, lg), out, fs = sets[i % nsets]
+        fn(q, k, v, lg, w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, d, w.chunk, out, fs, stream)
+
+    n = 0
+    for _ in range(warmup):
+        for d in DIRS:
+            call(n, d)
+            n += 1
+    torch.cuda.synchronize()
+
+    ncalls = steps * len(DIRS)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(ncalls)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    c = 0
+    for _ in range(steps):
+        for d in DIRS:
+            ev[c][0].record(stream)
+            call(n, d)
+            ev[c][1].record(stream)
+            n += 1
+            c += 1
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    call_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_call_us = 1e3 * sum(call_ms) / len(call_ms)
+    kern, span, grid = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, w.chunk,
+                                        int(w.dtype == "fp32"))
+    return {
+        "total_ms": total_ms,
+        "ms_per_step": total_ms / steps,
+        "tokens_per_s": ncalls * w.B * w.L / (total_ms * 1e-3),
+        "call_us_mean": mean_call_us,
+        "call_us_median": 1e3 * call_ms[len(call_ms) // 2],
+        "call_us_p10": 1e3 * call_ms[len(call_ms) // 10],
+        "call_us_p90": 1e3 * call_ms[(9 * len(call_ms)) // 10],
+        "alg_bytes_per_call": per_call,
+        "rotating_sets": nsets,
+        "kernel": {1: "generic", 2: "fused"}.get(kern, str(kern)),
+        "span": span,
+        "grid": grid,
+    }
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle as it stands, on this host, for as many single-direction
+    calls of the workload as fit in about `budget_s` seconds (at least one)."""
+    import gla_synth
+    import oracle
+
+    arrays = gla_synth.generate(w)
+    threads = min(oracle.default_threads(), w.B * w.H)
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.recurrent(*arrays, w.grid_h, w.grid_w, DIRS[calls % 4], threads=threads)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / calls * (calls + 1) > 2.5 * budget_s:
+            break
+    return {
+        "value": calls * w.B * w.L / el,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{calls} single-direction calls of {w.name} "
+                  f"(B={w.B}, {w.grid_h}x{w.grid_w}, H={w.H}, d_k={w.d_k}, d_v={w.d_v}) "
+                  f"in {el:.1f} s, fp64 token-by-token recurrence, one thread per (batch, head)",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="img640")
+    ap.add_argument("--secondary", default="img1024,long2048",
+                    help="comma-separated extra workloads reported beside the main one")
+    ap.add_argument("--warm", action="store_true", help="reuse one input set (cache-warm)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the B*H sequences "
+              "shard across GPUs with no communication, so run one process per GPU.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import chunkwise_gated_recurrence_amd as gla
+    import gla_synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if not os.path.exists(gla.LIB_PATH):
+        from chunkwise_gated_recurrence_amd import build as _b
+        _b.build()
+    gla.load_library()
+
+    w = gla_synth.WORKLOADS[args.workload]
+    r = run_workload(w, args.steps, args.warmup, rotate=not args.warm)
+    achieved = r["alg_bytes_per_call"] / (r["call_us_mean"] * 1e-6) / 1e9
+    traffic = measured_traffic(w.name)
+    secondary = []
+    for name in [s for s in args.secondary.split(",") if s and s != w.name]:
+        ws = gla_synth.WORKLOADS[name]
+        rs = run_workload(ws, max(10, args.steps // 2), args.warmup, rotate=not args.warm)
+        gbs = rs["alg_bytes_per_call"] / (rs["call_us_mean"] * 1e-6) / 1e9
+        secondary.append({
+            "workload": name, "tokens_per_s": rs["tokens_per_s"], "ms_per_step": rs["ms_per_step"],
+            "call_us_mean": rs["call_us_mean"], "call_us_median": rs["call_us_median"],
+            "achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "mfma_frac": mfma_flops(ws) / (rs["call_us_mean"] * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "kernel": rs["kernel"], "span": rs["span"], "grid": rs["grid"],
+        })
+
+    line = {
+        "metric": "key-only GLA fwd tokens/s",
+        "value": r["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if w.dtype == "fp16" else "f32",
+        "data": "synthetic (seeded gla_synth inputs, rotated over >=512 MiB of HBM buffers)"
+                if not args.warm else "synthetic (seeded gla_synth inputs, one warm set)",
+        "config": {
+            "workload": w.name, "B": w.B, "grid": f"{w.grid_h}x{w.grid_w}", "L": w.L, "H": w.H,
+            "d_k": w.d_k, "d_v": w.d_v, "chunk": w.chunk, "calls_per_step": len(DIRS),
+            "input_dtype": w.dtype, "kernel": r["kernel"], "span": r["span"], "grid_wg": r["grid"],
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "gla_fused_kernel" if r["kernel"] == "fused" else "generic (3 kernels)",
+            "alg_bytes_per_launch": r["alg_bytes_per_call"],
+            "launch_us_mean": r["call_us_mean"],
+            "launch_us_median": r["call_us_median"],
+            "mfma_frac": mfma_flops(w) / (r["call_us_mean"] * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+        },
+        "secondary": secondary,
+        "kernel_hash": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

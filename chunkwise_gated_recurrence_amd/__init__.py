@@ -1,0 +1,223 @@
+"""Python binding of libgtrgla: key-only gated linear attention forward on MI355X.
+
+Thin ctypes marshalling over the C ABI in ``include/gtr_gla.h``. The functions
+have the C names and argument order. They take torch tensors that live on the
+GPU, check dtype, device, contiguity and element count against the sizes
+passed, and pass raw pointers plus the current HIP stream. Every step of the
+computation runs in the HIP kernels of ``libgtrgla.so``. If the library is not
+built, importing works but every call raises.
+
+Operation (GTR summary page "GTR:门控Token循环实现高效稠密预测", section
+前置知识 › 门控线性注意力(GLA)): S_t = Diag(gamma_t) S_{t-1} + k_t^T v_t,
+o_t = d_k^{-1/2} q_t S_t, S_0 = 0, along one of four scan orders over the
+patch grid, evaluated chunkwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgtrgla.so")
+
+# status codes (gtr_gla_status)
+OK, ERR_NULL, ERR_SHAPE, ERR_DIR, ERR_CHUNK, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, \
+    ERR_ALIAS, ERR_POLICY = range(10)
+# scan orders (gtr_gla_dir)
+L2R, R2L, T2B, B2T = 0, 1, 2, 3
+DIRS = {"l2r": L2R, "r2l": R2L, "t2b": T2B, "b2t": B2T}
+# policies (gtr_gla_policy)
+POLICY_AUTO, POLICY_GENERIC, POLICY_FUSED, POLICY_FUSED_ONE = 0, 1, 2, 3
+
+EXPORTED = (
+    "gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_workspace_bytes", "gtr_gla_workspace_init",
+    "gtr_gla_fwd_ws", "gtr_gla_fwd_f32_ws", "gtr_gla_set_policy", "gtr_gla_get_policy",
+    "gtr_gla_plan", "gtr_gla_status_str",
+)
+
+
+class GtrGlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {gtr_gla_status_str(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgtrgla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m chunkwise_gated_recurrence_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    fwd = [P, P, P, P, I, I, I, I, I, I, I, I, P, P]
+    lib.gtr_gla_fwd.argtypes = fwd + [P]
+    lib.gtr_gla_fwd_f32.argtypes = fwd + [P]
+    lib.gtr_gla_fwd_ws.argtypes = fwd + [P, Z, P]
+    lib.gtr_gla_fwd_f32_ws.argtypes = fwd + [P, Z, P]
+    for f in (lib.gtr_gla_fwd, lib.gtr_gla_fwd_f32, lib.gtr_gla_fwd_ws, lib.gtr_gla_fwd_f32_ws):
+        f.restype = I
+    lib.gtr_gla_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.gtr_gla_workspace_bytes.restype = Z
+    lib.gtr_gla_workspace_init.argtypes = [P, Z, P]
+    lib.gtr_gla_workspace_init.restype = I
+    lib.gtr_gla_set_policy.argtypes = [I]
+    lib.gtr_gla_set_policy.restype = I
+    lib.gtr_gla_get_policy.argtypes = []
+    lib.gtr_gla_get_policy.restype = I
+    IP = ctypes.POINTER(ctypes.c_int)
+    lib.gtr_gla_plan.argtypes = [I, I, I, I, I, I, I, I, IP, IP, IP]
+    lib.gtr_gla_plan.restype = I
+    lib.gtr_gla_status_str.argtypes = [I]
+    lib.gtr_gla_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+def _check(t, name: str, dtype, numel: int):
+    if t is None:
+        return
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def _check_all(q, k, v, lg, B, H, gh, gw, dk, dv, out, fs, dtype):
+    import torch
+    if min(B, H, gh, gw, dk, dv) < 1:
+        return  # let the library report the invalid size
+    rows = B * gh * gw * H
+    for t, n in ((q, "q"), (k, "k"), (lg, "log_gamma")):
+        _check(t, n, dtype, rows * dk)
+    _check(v, "v", dtype, rows * dv)
+    _check(out, "out", dtype, rows * dv)
+    _check(fs, "final_state", torch.float32, B * H * dk * dv)
+
+
+def _raise(status: int, where: str):
+    if status != OK:
+        raise GtrGlaError(status, where)
+
+
+def gtr_gla_fwd(q, k, v, log_gamma, B: int, H: int, grid_h: int, grid_w: int, d_k: int, d_v: int,
+                dir: int, chunk: int, out, final_state=None, stream=None) -> None:
+    """fp16 forward; writes `out` [B,L,H,d_v] fp16 and `final_state` [B,H,d_k,d_v] fp32."""
+    import torch
+    _check_all(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, out, final_state, torch.float16)
+    r = load_library().gtr_gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), B, H, grid_h,
+                                   grid_w, d_k, d_v, dir, chunk, _ptr(out), _ptr(final_state),
+                                   _stream(stream))
+    _raise(r, "gtr_gla_fwd")
+
+
+def gtr_gla_fwd_f32(q, k, v, log_gamma, B: int, H: int, grid_h: int, grid_w: int, d_k: int,
+                    d_v: int, dir: int, chunk: int, out, final_state=None, stream=None) -> None:
+    """fp32 forward (generic kernels)."""
+    import torch
+    _check_all(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, out, final_state, torch.float32)
+    r = load_library().gtr_gla_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), B, H, grid_h,
+                                       grid_w, d_k, d_v, dir, chunk, _ptr(out), _ptr(final_state),
+                                       _stream(stream))
+    _raise(r, "gtr_gla_fwd_f32")
+
+
+def gtr_gla_workspace_bytes(B: int, H: int, grid_h: int, grid_w: int, d_k: int, d_v: int,
+                            chunk: int, is_fp32: int) -> int:
+    return int(load_library().gtr_gla_workspace_bytes(B, H, grid_h, grid_w, d_k, d_v, chunk,
+                                                      int(is_fp32)))
+
+
+def gtr_gla_workspace_init(workspace, workspace_bytes: int, stream=None) -> None:
+    r = load_library().gtr_gla_workspace_init(_ptr(workspace), workspace_bytes, _stream(stream))
+    _raise(r, "gtr_gla_workspace_init")
+
+
+def gtr_gla_fwd_ws(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, dir, chunk, out,
+                   final_state, workspace, workspace_bytes: int, stream=None) -> None:
+    import torch
+    _check_all(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, out, final_state, torch.float16)
+    r = load_library().gtr_gla_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), B, H, grid_h,
+                                      grid_w, d_k, d_v, dir, chunk, _ptr(out), _ptr(final_state),
+                                      _ptr(workspace), workspace_bytes, _stream(stream))
+    _raise(r, "gtr_gla_fwd_ws")
+
+
+def gtr_gla_fwd_f32_ws(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, dir, chunk, out,
+                       final_state, workspace, workspace_bytes: int, stream=None) -> None:
+    import torch
+    _check_all(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, out, final_state, torch.float32)
+    r = load_library().gtr_gla_fwd_f32_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), B, H,
+                                          grid_h, grid_w, d_k, d_v, dir, chunk, _ptr(out),
+                                          _ptr(final_state), _ptr(workspace), workspace_bytes,
+                                          _stream(stream))
+    _raise(r, "gtr_gla_fwd_f32_ws")
+
+
+def gtr_gla_set_policy(policy: int) -> None:
+    _raise(load_library().gtr_gla_set_policy(int(policy)), "gtr_gla_set_policy")
+
+
+def gtr_gla_get_policy() -> int:
+    return int(load_library().gtr_gla_get_policy())
+
+
+def gtr_gla_plan(B, H, grid_h, grid_w, d_k, d_v, chunk, is_fp32) -> Tuple[int, int, int]:
+    """(kernel, span, grid) of the launch a call would make: kernel 1 generic, 2 fused."""
+    kern, span, grid = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    r = load_library().gtr_gla_plan(B, H, grid_h, grid_w, d_k, d_v, chunk, int(is_fp32),
+                                    ctypes.byref(kern), ctypes.byref(span), ctypes.byref(grid))
+    _raise(r, "gtr_gla_plan")
+    return kern.value, span.value, grid.value
+
+
+def gtr_gla_status_str(status: int) -> str:
+    try:
+        return load_library().gtr_gla_status_str(int(status)).decode()
+    except RuntimeError:
+        return f"status {status}"
+
+
+def forward(q, k, v, log_gamma, grid_h: int, grid_w: int, dir, chunk: int = 64,
+            out=None, final_state=None, stream=None):
+    """Allocate outputs (if not given) and run the forward for [B, L, H, d] tensors.
+
+    Returns (out, final_state). fp16 inputs take gtr_gla_fwd, fp32 gtr_gla_fwd_f32.
+    """
+    import torch
+    if isinstance(dir, str):
+        dir = DIRS[dir]
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, L, H, dv), dtype=q.dtype, device=q.device)
+    if final_state is None:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    fn = gtr_gla_fwd_f32 if q.dtype == torch.float32 else gtr_gla_fwd
+    fn(q, k, v, log_gamma, B, H, grid_h, grid_w, dk, dv, int(dir), chunk, out, final_state, stream)
+    return out, final_state

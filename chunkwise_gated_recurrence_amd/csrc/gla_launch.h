@@ -1,0 +1,30 @@
+// gla_launch.h -- host-side launchers of the kernels, called by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+#include "gla_common.h"
+
+namespace gtrgla {
+
+// Generic three-phase path (gla_generic.hip).
+size_t generic_workspace_bytes(const Shape& s);
+hipError_t launch_generic(const void* q, const void* k, const void* v, const void* lg,
+                          bool is_fp32, const Shape& s, void* out, float* final_state, void* ws,
+                          hipStream_t st);
+
+// Fused fp16 MFMA path (gla_fused.hip).
+struct FusedPlan {
+    int span;        // chunks per workgroup
+    int n_spans;     // spans per (batch, head) sequence
+    int grid;        // workgroups launched
+};
+bool fused_supported(const Shape& s);
+FusedPlan fused_plan(const Shape& s, int span_override);
+size_t fused_workspace_bytes(const Shape& s, const FusedPlan& p);
+hipError_t launch_fused(const void* q, const void* k, const void* v, const void* lg,
+                        const Shape& s, const FusedPlan& p, void* out, float* final_state,
+                        void* ws, hipStream_t st);
+
+}  // namespace gtrgla

@@ -1,0 +1,274 @@
+// gtr_gla_api.cpp -- the C ABI of libgtrgla (declared in include/gtr_gla.h):
+// argument validation, launch policy, workspace management and dispatch to the
+// generic and fused kernels. Nothing here throws across the ABI.
+#include "gtr_gla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "gla_launch.h"
+
+namespace {
+
+using gtrgla::FusedPlan;
+using gtrgla::Shape;
+
+std::atomic<int> g_policy{-1};   // -1: not yet read from the environment
+
+int current_policy()
+{
+    int p = g_policy.load(std::memory_order_relaxed);
+    if (p >= 0) return p;
+    p = GTR_GLA_POLICY_AUTO;
+    if (const char* env = std::getenv("GTR_GLA_POLICY")) {
+        const int v = std::atoi(env);
+        if (v >= GTR_GLA_POLICY_AUTO && v <= GTR_GLA_POLICY_FUSED_ONE) p = v;
+    }
+    int expected = -1;
+    g_policy.compare_exchange_strong(expected, p);
+    return g_policy.load(std::memory_order_relaxed);
+}
+
+int span_override_from_env()
+{
+    if (const char* env = std::getenv("GTR_GLA_SPAN")) return std::atoi(env);
+    return 0;
+}
+
+bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
+
+// Validation of sizes and scalars (pointers are checked separately).
+int validate_sizes(int B, int H, int gh, int gw, int dk, int dv, int dir, int chunk, Shape* s)
+{
+    if (B < 1 || H < 1 || gh < 1 || gw < 1 || dk < 1 || dv < 1) return GTR_GLA_ERR_SHAPE;
+    const long long L = (long long)gh * gw;
+    const long long rows = (long long)B * L * H;
+    if (L >= (1LL << 31) || rows >= (1LL << 31) || rows * (long long)(dk > dv ? dk : dv) >= (1LL << 40))
+        return GTR_GLA_ERR_SHAPE;
+    if (dir < 0 || dir > 3) return GTR_GLA_ERR_DIR;
+    if (!chunk_ok(chunk)) return GTR_GLA_ERR_CHUNK;
+    if (dk > 128 || dv > 512) return GTR_GLA_ERR_UNSUPPORTED;
+    const long long nc = (L + chunk - 1) / chunk;
+    if ((long long)B * H * nc >= (1LL << 31)) return GTR_GLA_ERR_SHAPE;
+    if (s) {
+        s->B = B;
+        s->H = H;
+        s->grid_h = gh;
+        s->grid_w = gw;
+        s->L = (int)L;
+        s->d_k = dk;
+        s->d_v = dv;
+        s->dir = dir;
+        s->chunk = chunk;
+        s->n_chunks = (int)nc;
+        s->scale = (float)(1.0 / std::sqrt((double)dk));
+    }
+    return GTR_GLA_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+int validate_pointers(const void* q, const void* k, const void* v, const void* lg, const void* out,
+                      const void* fs, const Shape& s, size_t elt)
+{
+    if (!q || !k || !v || !lg || !out) return GTR_GLA_ERR_NULL;
+    const size_t rows = (size_t)s.B * s.L * s.H;
+    const size_t nk = rows * s.d_k * elt, nv = rows * s.d_v * elt;
+    const size_t nf = (size_t)s.B * s.H * s.d_k * s.d_v * sizeof(float);
+    const void* ins[4] = {q, k, v, lg};
+    const size_t ns[4] = {nk, nk, nv, nk};
+    for (int i = 0; i < 4; ++i) {
+        if (overlaps(out, nv, ins[i], ns[i])) return GTR_GLA_ERR_ALIAS;
+        if (fs && overlaps(fs, nf, ins[i], ns[i])) return GTR_GLA_ERR_ALIAS;
+    }
+    if (fs && overlaps(fs, nf, out, nv)) return GTR_GLA_ERR_ALIAS;
+    return GTR_GLA_OK;
+}
+
+enum Kernel { kGeneric = 1, kFused = 2 };
+
+struct Choice {
+    Kernel kernel;
+    FusedPlan plan;
+    size_t ws_bytes;
+};
+
+Choice choose(const Shape& s, bool is_fp32, int policy)
+{
+    Choice c;
+    c.kernel = kGeneric;
+    c.plan = FusedPlan{1, s.n_chunks, 0};
+    const bool fused_ok = !is_fp32 && gtrgla::fused_supported(s);
+    if (fused_ok && policy != GTR_GLA_POLICY_GENERIC) {
+        c.kernel = kFused;
+        const int span = (policy == GTR_GLA_POLICY_FUSED_ONE) ? 1 : span_override_from_env();
+        c.plan = gtrgla::fused_plan(s, span);
+        c.ws_bytes = gtrgla::fused_workspace_bytes(s, c.plan);
+    } else {
+        c.ws_bytes = gtrgla::generic_workspace_bytes(s);
+    }
+    return c;
+}
+
+// Library-owned workspaces for the non-_ws entry points, one per (device, stream).
+struct CachedWs {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, uintptr_t>, CachedWs> g_ws;
+
+int cached_workspace(size_t need, hipStream_t st, void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GTR_GLA_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    CachedWs& c = g_ws[std::make_pair(dev, (uintptr_t)st)];
+    if (c.bytes < need) {
+        if (c.ptr) {
+            // the previous workspace may still be in use by work on this stream
+            if (hipStreamSynchronize(st) != hipSuccess) return GTR_GLA_ERR_HIP;
+            (void)hipFree(c.ptr);
+            c.ptr = nullptr;
+            c.bytes = 0;
+        }
+        size_t bytes = need < (1u << 20) ? (1u << 20) : need;
+        if (hipMalloc(&c.ptr, bytes) != hipSuccess) {
+            c.ptr = nullptr;
+            return GTR_GLA_ERR_HIP;
+        }
+        if (hipMemsetAsync(c.ptr, 0, bytes, st) != hipSuccess) return GTR_GLA_ERR_HIP;
+        c.bytes = bytes;
+    }
+    *out = c.ptr;
+    return GTR_GLA_OK;
+}
+
+int run(const void* q, const void* k, const void* v, const void* lg, int B, int H, int gh, int gw,
+        int dk, int dv, int dir, int chunk, void* out, float* fs, bool is_fp32, void* ws,
+        size_t ws_bytes, bool own_ws, hipStream_t st)
+{
+    Shape s;
+    int r = validate_sizes(B, H, gh, gw, dk, dv, dir, chunk, &s);
+    if (r != GTR_GLA_OK) return r;
+    r = validate_pointers(q, k, v, lg, out, fs, s, is_fp32 ? 4 : 2);
+    if (r != GTR_GLA_OK) return r;
+    const Choice c = choose(s, is_fp32, current_policy());
+    if (own_ws) {
+        r = cached_workspace(c.ws_bytes, st, &ws);
+        if (r != GTR_GLA_OK) return r;
+    } else if (!ws || ws_bytes < c.ws_bytes) {
+        return GTR_GLA_ERR_WORKSPACE;
+    }
+    hipError_t e;
+    if (c.kernel == kFused)
+        e = gtrgla::launch_fused(q, k, v, lg, s, c.plan, out, fs, ws, st);
+    else
+        e = gtrgla::launch_generic(q, k, v, lg, is_fp32, s, out, fs, ws, st);
+    return e == hipSuccess ? GTR_GLA_OK : GTR_GLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gtr_gla_fwd(const void* q, const void* k, const void* v, const void* log_gamma, int B, int H,
+                int grid_h, int grid_w, int d_k, int d_v, int dir, int chunk, void* out,
+                float* final_state, hipStream_t stream)
+{
+    return run(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, dir, chunk, out, final_state,
+               false, nullptr, 0, true, stream);
+}
+
+int gtr_gla_fwd_f32(const float* q, const float* k, const float* v, const float* log_gamma, int B,
+                    int H, int grid_h, int grid_w, int d_k, int d_v, int dir, int chunk,
+                    float* out, float* final_state, hipStream_t stream)
+{
+    return run(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, dir, chunk, out, final_state,
+               true, nullptr, 0, true, stream);
+}
+
+size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunk,
+                               int is_fp32)
+{
+    Shape s;
+    if (validate_sizes(B, H, grid_h, grid_w, d_k, d_v, 0, chunk, &s) != GTR_GLA_OK) return 0;
+    return choose(s, is_fp32 != 0, current_policy()).ws_bytes;
+}
+
+int gtr_gla_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!workspace) return GTR_GLA_ERR_NULL;
+    if (workspace_bytes == 0) return GTR_GLA_ERR_WORKSPACE;
+    return hipMemsetAsync(workspace, 0, workspace_bytes, stream) == hipSuccess ? GTR_GLA_OK
+                                                                               : GTR_GLA_ERR_HIP;
+}
+
+int gtr_gla_fwd_ws(const void* q, const void* k, const void* v, const void* log_gamma, int B,
+                   int H, int grid_h, int grid_w, int d_k, int d_v, int dir, int chunk, void* out,
+                   float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return run(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, dir, chunk, out, final_state,
+               false, workspace, workspace_bytes, false, stream);
+}
+
+int gtr_gla_fwd_f32_ws(const float* q, const float* k, const float* v, const float* log_gamma,
+                       int B, int H, int grid_h, int grid_w, int d_k, int d_v, int dir, int chunk,
+                       float* out, float* final_state, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream)
+{
+    return run(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, dir, chunk, out, final_state,
+               true, workspace, workspace_bytes, false, stream);
+}
+
+int gtr_gla_set_policy(int policy)
+{
+    if (policy < GTR_GLA_POLICY_AUTO || policy > GTR_GLA_POLICY_FUSED_ONE) return GTR_GLA_ERR_POLICY;
+    g_policy.store(policy, std::memory_order_relaxed);
+    return GTR_GLA_OK;
+}
+
+int gtr_gla_get_policy(void) { return current_policy(); }
+
+int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunk, int is_fp32,
+                 int* kernel_out, int* span_out, int* grid_out)
+{
+    Shape s;
+    const int r = validate_sizes(B, H, grid_h, grid_w, d_k, d_v, 0, chunk, &s);
+    if (r != GTR_GLA_OK) return r;
+    const Choice c = choose(s, is_fp32 != 0, current_policy());
+    if (kernel_out) *kernel_out = (int)c.kernel;
+    if (span_out) *span_out = c.kernel == kFused ? c.plan.span : 1;
+    if (grid_out) *grid_out = c.kernel == kFused ? c.plan.grid : B * H * s.n_chunks;
+    return GTR_GLA_OK;
+}
+
+const char* gtr_gla_status_str(int status)
+{
+    switch (status) {
+    case GTR_GLA_OK: return "ok";
+    case GTR_GLA_ERR_NULL: return "a required pointer is NULL";
+    case GTR_GLA_ERR_SHAPE: return "invalid size (must be >= 1 and within index range)";
+    case GTR_GLA_ERR_DIR: return "dir must be 0 (L->R), 1 (R->L), 2 (T->B) or 3 (B->T)";
+    case GTR_GLA_ERR_CHUNK: return "chunk must be 16, 32, 64 or 128";
+    case GTR_GLA_ERR_UNSUPPORTED: return "unsupported head size (d_k <= 128, d_v <= 512)";
+    case GTR_GLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GTR_GLA_ERR_HIP: return "HIP runtime error";
+    case GTR_GLA_ERR_ALIAS: return "an output overlaps an input or the other output";
+    case GTR_GLA_ERR_POLICY: return "unknown policy";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+/*
+ * gtr_gla.h -- C ABI of libgtrgla: the inference forward pass of the key-only
+ * gated linear attention (GLA) token mixer of "GTR: Gated Token Recurrence for
+ * Efficient Dense Prediction", on AMD Instinct MI355X (gfx950).
+ *
+ * Operation (GTR summary page "GTR:门控Token循环实现高效稠密预测", section
+ * 前置知识 › 门控线性注意力(GLA) and section 核心方法): for every batch entry b
+ * and head h, along one scan order over the stride-16 patch grid,
+ *
+ *     S_t = Diag(gamma_t) S_{t-1} + k_t^T v_t,    o_t = d_k^{-1/2} q_t S_t,
+ *
+ * with S_0 = 0, gamma_t = exp(log_gamma_t) a per-key-dimension gate and no
+ * decay on the value side. It is evaluated chunkwise (section 前置知识 ›
+ * Chunkwise(分块)并行 of the same page; section 3.3 of the 0539edu.com page):
+ * per-chunk summaries U_c and decays d_c, the boundary scan
+ * S_[c+1] = Diag(d_c) S_[c] + U_c, and per-chunk outputs.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors (all contiguous, row-major, device memory owned by the caller):
+ *   q, k, log_gamma : [B, L, H, d_k]      v, out : [B, L, H, d_v]
+ *   final_state     : [B, H, d_k, d_v] fp32, the state after the last scan
+ *                     step, without the d_k^{-1/2} scale. May be NULL.
+ *   L = grid_h * grid_w; spatial token p = row * grid_w + col.
+ *   log_gamma is the natural log of the gate, finite and <= 0.
+ * Scan order (dir): the pages name left->right, right->left, top->bottom and
+ *   bottom->top (summary page, section 核心方法). Read here as
+ *   0 raster order, 1 the whole raster reversed, 2 column-major order,
+ *   3 column-major order reversed. o for token p is written at p.
+ * chunk: tokens per chunk, one of 16, 32, 64, 128 (64 is the pages' choice,
+ *   summary page section 方法步骤详情).
+ * Outputs are fully overwritten, never accumulated into. Outputs must not
+ *   overlap inputs or each other. Inputs are read only.
+ * Errors: every entry point returns a gtr_gla_status. A call that fails
+ *   validation launches nothing and writes nothing. GTR_GLA_ERR_HIP reports a
+ *   HIP error seen while launching; faults inside a kernel surface at the
+ *   caller's next synchronisation, as for any HIP call. Nothing throws.
+ * Synchronisation: every call is asynchronous on `stream`. It performs no
+ *   host synchronisation and no device-to-host copy.
+ */
+#ifndef GTR_GLA_H
+#define GTR_GLA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GTR_GLA_L2R = 0,   /* left -> right: raster order            */
+    GTR_GLA_R2L = 1,   /* right -> left: raster order reversed   */
+    GTR_GLA_T2B = 2,   /* top -> bottom: column-major order      */
+    GTR_GLA_B2T = 3    /* bottom -> top: column-major reversed   */
+} gtr_gla_dir;
+
+typedef enum {
+    GTR_GLA_OK = 0,
+    GTR_GLA_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    GTR_GLA_ERR_SHAPE = 2,       /* a size is < 1, or a tensor would exceed 2^31 rows */
+    GTR_GLA_ERR_DIR = 3,         /* dir not in 0..3                                  */
+    GTR_GLA_ERR_CHUNK = 4,       /* chunk not in {16, 32, 64, 128}                    */
+    GTR_GLA_ERR_UNSUPPORTED = 5, /* no kernel for these head sizes (d_k > 128 or d_v > 512) */
+    GTR_GLA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required          */
+    GTR_GLA_ERR_HIP = 7,         /* the HIP runtime reported an error               */
+    GTR_GLA_ERR_ALIAS = 8,       /* an output overlaps an input or the other output  */
+    GTR_GLA_ERR_POLICY = 9       /* unknown policy value                             */
+} gtr_gla_status;
+
+/* Launch policies (the pages' length-aware scheduling: short sequences take
+ * one kernel, long ones an occupancy-aware kernel that overlaps the boundary
+ * scan with output computation; 0539edu.com page, section 3.3).            */
+typedef enum {
+    GTR_GLA_POLICY_AUTO = 0,     /* choose by shape (the default)                    */
+    GTR_GLA_POLICY_GENERIC = 1,  /* three generic fp32 kernels: summaries, scan,
+                                    outputs. Any supported shape, fp16 or fp32.     */
+    GTR_GLA_POLICY_FUSED = 2,    /* one fp16 MFMA kernel, one workgroup per span of
+                                    chunks, decoupled look-back across spans.       */
+    GTR_GLA_POLICY_FUSED_ONE = 3 /* the fused kernel with one chunk per span        */
+} gtr_gla_policy;
+
+/*
+ * gtr_gla_fwd -- fp16 (IEEE binary16) q, k, v, log_gamma and out; fp32
+ * accumulation, fp32 state and fp32 final_state.
+ * Uses a workspace that the library allocates on the first call for each
+ * (device, stream) pair and grows when a larger shape arrives; call it once
+ * outside stream capture for a shape before capturing it. Calls on different
+ * streams use different workspaces and may overlap.
+ */
+int gtr_gla_fwd(const void* q, const void* k, const void* v, const void* log_gamma,
+                int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                int dir, int chunk, void* out, float* final_state, hipStream_t stream);
+
+/* gtr_gla_fwd_f32 -- the same with every tensor fp32 (generic kernels only). */
+int gtr_gla_fwd_f32(const float* q, const float* k, const float* v, const float* log_gamma,
+                    int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                    int dir, int chunk, float* out, float* final_state, hipStream_t stream);
+
+/*
+ * Caller-managed workspace (the deployment interface of the pages supports a
+ * persistent caller-managed workspace, preallocated outputs and graph capture:
+ * 0539edu.com page, appendix E.3.1).
+ * gtr_gla_workspace_bytes returns the size needed by the _ws entry points for
+ * this shape and precision under the current policy, or 0 for invalid sizes.
+ * A workspace must be cleared once by gtr_gla_workspace_init before its first
+ * use; the kernels leave it ready for the next call. One workspace must not
+ * be used by two calls that may run at the same time.
+ * The _ws entry points allocate nothing and may be captured in a HIP graph.
+ */
+size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                               int chunk, int is_fp32);
+int gtr_gla_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+int gtr_gla_fwd_ws(const void* q, const void* k, const void* v, const void* log_gamma,
+                   int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                   int dir, int chunk, void* out, float* final_state,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+int gtr_gla_fwd_f32_ws(const float* q, const float* k, const float* v, const float* log_gamma,
+                       int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                       int dir, int chunk, float* out, float* final_state,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Policy control, for A/B measurement and tests. The setting is process-wide
+ * and read at each call; it is not synchronised with calls running on other
+ * host threads. A policy that cannot serve a call (fused with fp32 inputs or
+ * with head sizes other than 64) falls back to the generic kernels, as the
+ * pages' specialised operator falls back to a generic implementation
+ * (summary page, section 局限与改进).
+ */
+int gtr_gla_set_policy(int policy);
+int gtr_gla_get_policy(void);
+
+/*
+ * gtr_gla_plan -- describes the launch a call with these arguments would make
+ * under the current policy, without launching anything. Any output pointer
+ * may be NULL. kernel_out: 1 generic, 2 fused. span_out: chunks per workgroup
+ * (fused) or 1. grid_out: workgroups of the main kernel.
+ */
+int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunk,
+                 int is_fp32, int* kernel_out, int* span_out, int* grid_out);
+
+/* Static description of a status code. Never NULL. */
+const char* gtr_gla_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GTR_GLA_H */

@@ -1,0 +1,129 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, and
+rejects invalid arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunkwise_gated_recurrence_amd as gla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gtr_gla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gla.LIB_PATH):
+        from chunkwise_gated_recurrence_amd import build
+        build.build()
+    return gla.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(gtr_gla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    assert "gtr_gla_fwd" in names and "gtr_gla_fwd_ws" in names
+    assert set(names) == set(gla.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _fwd(lib, ptrs, B=1, H=2, gh=4, gw=4, dk=64, dv=64, d=0, C=64, f32=False, ws=None, nws=0):
+    q, k, v, g, o, fs = ptrs
+    if ws is None and nws == 0:
+        fn = lib.gtr_gla_fwd_f32 if f32 else lib.gtr_gla_fwd
+        return fn(q, k, v, g, B, H, gh, gw, dk, dv, d, C, o, fs, None)
+    fn = lib.gtr_gla_fwd_f32_ws if f32 else lib.gtr_gla_fwd_ws
+    return fn(q, k, v, g, B, H, gh, gw, dk, dv, d, C, o, fs, ws, nws, None)
+
+
+# Fake, well separated, never dereferenced device addresses: every call below
+# fails validation before any HIP call.
+BASE = 1 << 40
+SEP = 1 << 32
+PTRS = [BASE + i * SEP for i in range(6)]
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_null_pointers(lib, f32):
+    for i in range(5):
+        ptrs = list(PTRS)
+        ptrs[i] = None
+        assert _fwd(lib, ptrs, f32=f32) == gla.ERR_NULL
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_bad_sizes(lib, f32):
+    for kw in (dict(B=0), dict(H=-1), dict(gh=0), dict(gw=0), dict(dk=0), dict(dv=0)):
+        assert _fwd(lib, PTRS, f32=f32, **kw) == gla.ERR_SHAPE, kw
+    assert _fwd(lib, PTRS, f32=f32, gh=1 << 16, gw=1 << 16) == gla.ERR_SHAPE
+    assert _fwd(lib, PTRS, f32=f32, d=4) == gla.ERR_DIR
+    assert _fwd(lib, PTRS, f32=f32, d=-1) == gla.ERR_DIR
+    for C in (0, 1, 48, 256):
+        assert _fwd(lib, PTRS, f32=f32, C=C) == gla.ERR_CHUNK
+    assert _fwd(lib, PTRS, f32=f32, dk=129) == gla.ERR_UNSUPPORTED
+    assert _fwd(lib, PTRS, f32=f32, dv=513) == gla.ERR_UNSUPPORTED
+
+
+def test_aliasing_outputs(lib):
+    p = list(PTRS)
+    p[4] = p[2] + 64          # out inside v
+    assert _fwd(lib, p) == gla.ERR_ALIAS
+    p = list(PTRS)
+    p[5] = p[0]               # final_state on q
+    assert _fwd(lib, p) == gla.ERR_ALIAS
+    p = list(PTRS)
+    p[5] = p[4]               # final_state on out
+    assert _fwd(lib, p) == gla.ERR_ALIAS
+
+
+def test_workspace_checks(lib):
+    # fp32 always takes the generic kernels: U/S (d_k*d_v) and d (d_k) per chunk
+    n = lib.gtr_gla_workspace_bytes(2, 3, 10, 13, 32, 16, 64, 1)
+    chunks = 2 * 3 * ((10 * 13 + 63) // 64)
+    assert n == chunks * (32 * 16 + 32) * 4
+    assert lib.gtr_gla_workspace_bytes(0, 3, 10, 13, 32, 16, 64, 1) == 0
+    assert lib.gtr_gla_workspace_bytes(2, 3, 10, 13, 32, 16, 48, 1) == 0
+    assert _fwd(lib, PTRS, B=2, H=3, gh=10, gw=13, dk=32, dv=16, f32=True, ws=None, nws=1) == \
+        gla.ERR_WORKSPACE
+    assert _fwd(lib, PTRS, B=2, H=3, gh=10, gw=13, dk=32, dv=16, f32=True,
+                ws=BASE + 7 * SEP, nws=n - 1) == gla.ERR_WORKSPACE
+    assert lib.gtr_gla_workspace_init(None, 16, None) == gla.ERR_NULL
+    assert lib.gtr_gla_workspace_init(BASE, 0, None) == gla.ERR_WORKSPACE
+
+
+def test_policy_and_plan(lib):
+    assert lib.gtr_gla_set_policy(7) == gla.ERR_POLICY
+    assert lib.gtr_gla_set_policy(-1) == gla.ERR_POLICY
+    old = lib.gtr_gla_get_policy()
+    assert lib.gtr_gla_set_policy(gla.POLICY_GENERIC) == gla.OK
+    assert lib.gtr_gla_get_policy() == gla.POLICY_GENERIC
+    k, s, g = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert lib.gtr_gla_plan(1, 6, 40, 40, 64, 64, 64, 0, ctypes.byref(k), ctypes.byref(s),
+                            ctypes.byref(g)) == gla.OK
+    assert (k.value, s.value, g.value) == (1, 1, 6 * 25)
+    # fp32 never takes the fused kernel
+    assert lib.gtr_gla_set_policy(gla.POLICY_FUSED) == gla.OK
+    assert lib.gtr_gla_plan(1, 6, 40, 40, 64, 64, 64, 1, ctypes.byref(k), None, None) == gla.OK
+    assert k.value == 1
+    assert lib.gtr_gla_plan(1, 6, 40, 40, 64, 64, 48, 1, None, None, None) == gla.ERR_CHUNK
+    assert lib.gtr_gla_set_policy(old) == gla.OK
+
+
+def test_status_strings(lib):
+    seen = set()
+    for s in range(10):
+        txt = lib.gtr_gla_status_str(s).decode()
+        assert txt and txt != "unknown status"
+        seen.add(txt)
+    assert len(seen) == 10
+    assert lib.gtr_gla_status_str(99).decode() == "unknown status"

@@ -1,0 +1,178 @@
+"""GPU parity: the HIP path against the fp64 oracle, element by element.
+
+Bar (max|gpu - oracle| / max|oracle| over a whole tensor, separately for the
+outputs and the final state): 5e-3 for fp16 inputs, 1e-5 for fp32 inputs.
+Workloads are the seeded synthetic grids of gla_synth (full sizes), in the
+launch configuration the benchmark times, plus ragged and degenerate shapes,
+every scan order, every launch policy and span, and the decay extremes.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import gla_synth
+import oracle
+
+torch = pytest.importorskip("torch")
+import chunkwise_gated_recurrence_amd as gla  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp16": 5e-3, "fp32": 1e-5}
+DIRS = ["l2r", "r2l", "t2b", "b2t"]
+_oracle_cache = {}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    assert torch.cuda.is_available(), "the gpu tests need an MI355X"
+    gla.load_library()
+    yield
+    gla.gtr_gla_set_policy(gla.POLICY_AUTO)
+    os.environ.pop("GTR_GLA_SPAN", None)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def run_gpu(w, arrays, d, chunk=None):
+    q, k, v, lg = [dev(a) for a in arrays]
+    out, fs = gla.forward(q, k, v, lg, w.grid_h, w.grid_w, d, chunk=chunk or w.chunk)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), fs.cpu().numpy()
+
+
+def ref(w, arrays, d, key=None):
+    if key is not None and (key, d) in _oracle_cache:
+        return _oracle_cache[(key, d)]
+    r = oracle.recurrent(*arrays, w.grid_h, w.grid_w, d)
+    if key is not None:
+        _oracle_cache[(key, d)] = r
+    return r
+
+
+def check(w, arrays, d, tag, key=None, chunk=None, tol=None):
+    say(f"[case] {tag} {w.name} B={w.B} H={w.H} grid={w.grid_h}x{w.grid_w} dk={w.d_k} dv={w.d_v} "
+        f"{w.dtype} dir={d} chunk={chunk or w.chunk} policy={gla.gtr_gla_get_policy()} "
+        f"span_env={os.environ.get('GTR_GLA_SPAN')}")
+    o, s = run_gpu(w, arrays, d, chunk)
+    o_ref, s_ref = ref(w, arrays, d, key)
+    eo, es = oracle.rel_err(o, o_ref), oracle.rel_err(s, s_ref)
+    tol = tol or TOL[w.dtype]
+    say(f"       err_o={eo:.3e} err_S={es:.3e} (tol {tol:g})")
+    assert np.isfinite(o.astype(np.float64)).all() and np.isfinite(s).all()
+    assert eo <= tol, f"outputs: {eo}"
+    assert es <= tol, f"final state: {es}"
+    return o, s
+
+
+# --------------------------------------------------------------------------- workloads
+@pytest.mark.parametrize("d", DIRS)
+@pytest.mark.parametrize("name", list(gla_synth.WORKLOADS))
+def test_workload_parity(name, d):
+    gla.gtr_gla_set_policy(gla.POLICY_AUTO)
+    w = gla_synth.WORKLOADS[name]
+    arrays = gla_synth.generate(w)
+    check(w, arrays, d, "auto", key=name)
+
+
+@pytest.mark.parametrize("d", DIRS)
+@pytest.mark.parametrize("name", ["img640", "img1024"])
+def test_generic_policy_parity(name, d):
+    gla.gtr_gla_set_policy(gla.POLICY_GENERIC)
+    try:
+        w = gla_synth.WORKLOADS[name]
+        check(w, gla_synth.generate(w), d, "generic", key=name)
+    finally:
+        gla.gtr_gla_set_policy(gla.POLICY_AUTO)
+
+
+@pytest.mark.parametrize("span", [1, 2, 4, 8])
+@pytest.mark.parametrize("name", ["img1024", "ragged30"])
+def test_fused_spans(name, span):
+    w = gla_synth.WORKLOADS["img1024"]
+    if name == "ragged30":
+        w = w.with_(name="ragged30", B=2, H=3, grid_h=30, grid_w=30, seed=17)
+    arrays = gla_synth.generate(w)
+    gla.gtr_gla_set_policy(gla.POLICY_FUSED)
+    os.environ["GTR_GLA_SPAN"] = str(span)
+    try:
+        kern, sp, _ = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, 64, 64, 64, 0)
+        assert (kern, sp) == (2, span)
+        for d in DIRS:
+            check(w, arrays, d, f"fused-span{span}", key=w.name)
+    finally:
+        os.environ.pop("GTR_GLA_SPAN", None)
+        gla.gtr_gla_set_policy(gla.POLICY_AUTO)
+
+
+# --------------------------------------------------------------------------- odd shapes
+BASE16 = gla_synth.WORKLOADS["img640"]
+BASE32 = gla_synth.WORKLOADS["tiny"]
+SHAPES = [
+    ("tail30x30", BASE16.with_(grid_h=30, grid_w=30, H=2, seed=21)),
+    ("nonsquare24x40", BASE16.with_(grid_h=24, grid_w=40, H=3, seed=22)),
+    ("batch3", BASE16.with_(B=3, H=2, grid_h=20, grid_w=17, seed=23)),
+    ("row1x100", BASE16.with_(grid_h=1, grid_w=100, H=2, seed=24)),
+    ("col100x1", BASE16.with_(grid_h=100, grid_w=1, H=2, seed=25)),
+    ("single1x1", BASE16.with_(grid_h=1, grid_w=1, H=2, seed=26)),
+    ("dk32dv64", BASE16.with_(d_k=32, d_v=64, grid_h=24, grid_w=24, seed=27)),
+    ("dk32dv32", BASE16.with_(d_k=32, d_v=32, grid_h=16, grid_w=16, seed=28)),
+    ("dk128dv96", BASE16.with_(d_k=128, d_v=96, grid_h=12, grid_w=20, H=2, seed=29)),
+    ("fp32_d64", BASE32.with_(d_k=64, d_v=64, grid_h=30, grid_w=30, H=2, seed=30)),
+    ("fp32_ragged", BASE32.with_(d_k=32, d_v=48, grid_h=13, grid_w=11, B=2, H=3, seed=31)),
+]
+
+
+@pytest.mark.parametrize("d", DIRS)
+@pytest.mark.parametrize("name,w", SHAPES, ids=[s[0] for s in SHAPES])
+def test_shapes(name, w, d):
+    check(w, gla_synth.generate(w), d, name, key=name)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64, 128])
+def test_chunk_sizes(chunk):
+    w = BASE16.with_(name="chunks", grid_h=20, grid_w=30, H=2, seed=41)
+    arrays = gla_synth.generate(w)
+    for d in DIRS:
+        check(w, arrays, d, f"chunk{chunk}", key="chunks", chunk=chunk)
+
+
+def _with_gates(w, lg_value, seed):
+    q, k, v, _ = gla_synth.generate(w.with_(seed=seed))
+    lg = np.full(q.shape, lg_value, dtype=q.dtype)
+    return q, k, v, lg
+
+
+@pytest.mark.parametrize("policy", [gla.POLICY_AUTO, gla.POLICY_GENERIC])
+@pytest.mark.parametrize("lg_value", [0.0, -1.0, -1e4])
+def test_decay_extremes(lg_value, policy):
+    """gamma = 1 (plain causal linear attention), strong decay, and gamma -> 0."""
+    w = BASE16.with_(name=f"decay{lg_value}", grid_h=32, grid_w=40, H=2)
+    arrays = _with_gates(w, lg_value, 51)
+    gla.gtr_gla_set_policy(policy)
+    try:
+        for d in DIRS:
+            check(w, arrays, d, f"lg={lg_value}", key=w.name)
+    finally:
+        gla.gtr_gla_set_policy(gla.POLICY_AUTO)
+
+
+def test_mixed_decay_chunks():
+    """Some chunks inside the factorised-score range and some far outside it."""
+    w = BASE16.with_(name="mixed", grid_h=32, grid_w=64, H=2)
+    q, k, v, lg = gla_synth.generate(w.with_(seed=61))
+    lg = lg.astype(np.float32)
+    lg[:, 640:1280] = -0.6          # ~ 55 log2 units per chunk: exact-score path
+    lg[:, 1500] = -30.0             # one very small gate
+    arrays = (q, k, v, lg.astype(np.float16))
+    for d in DIRS:
+        check(w, arrays, d, "mixed", key="mixed")
