@@ -17,8 +17,11 @@ hipError_t launch_generic(const void* q, const void* k, const void* v, const voi
 // Fused fp16 MFMA path (gla_fused.hip).
 struct FusedPlan {
     int span;        // chunks per workgroup
-    int n_spans;     // spans per (batch, head) sequence
-    int grid;        // workgroups launched
+    bool keep;       // outputs kept on chip through the boundary scan
+    int n_spans;     // spans (workgroups) per (batch, head) sequence
+    int seq_batch;   // sequences per launch (every workgroup of a launch is resident)
+    int grid;        // workgroups per launch
+    int slice;       // state elements each workgroup scans
 };
 bool fused_supported(const Shape& s);
 FusedPlan fused_plan(const Shape& s, int span_override);

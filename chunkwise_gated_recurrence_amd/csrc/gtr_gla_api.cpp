@@ -108,7 +108,7 @@ Choice choose(const Shape& s, bool is_fp32, int policy)
 {
     Choice c;
     c.kernel = kGeneric;
-    c.plan = FusedPlan{1, s.n_chunks, 0};
+    c.plan = FusedPlan{1, false, s.n_chunks, 0, 0, 0};
     const bool fused_ok = !is_fp32 && gtrgla::fused_supported(s);
     if (fused_ok && policy != GTR_GLA_POLICY_GENERIC) {
         c.kernel = kFused;
