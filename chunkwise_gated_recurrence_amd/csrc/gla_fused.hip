@@ -65,7 +65,7 @@ constexpr int kThreads = 256;     // 4 waves
 constexpr int kMaxKeep = 2;       // longest span kept on chip
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kGuard = 16.0f;   // max log2 range of a chunk for factorised scores
-constexpr int kTile = kC * kD;    // halves per LDS tile
+constexpr int kTile = kC * 72;    // halves per LDS tile (rows padded to 72)
 constexpr int kAggWords = kD * kD + kD;   // U (lane order) then D
 constexpr unsigned int kMaxPolls = 1u << 22;
 constexpr int kMaxSpans = 64;        // spans per sequence
@@ -76,25 +76,21 @@ constexpr int kDevScope = 16;        // cache policy: device-scope (sc1) access
 // ---------------------------------------------------------------------------
 // small device helpers
 
-// 64 x 64 fp16 tiles in LDS, 128 B rows in 16 B granules permuted by row, so
-// that reads of 16 consecutive rows and writes of rows 8 apart spread over
-// the banks.
-__device__ __forceinline__ int swz(int row, int col)
-{
-    const int g = (col >> 3) ^ ((row ^ (row >> 3)) & 7);
-    return row * kD + (g << 3) + (col & 7);
-}
+// 64 x 64 fp16 tiles in LDS with rows padded to 72 halves (144 B): the 16 rows
+// an MFMA operand read touches fall on distinct banks, and every access is a
+// per-lane base plus a compile-time offset.
+constexpr int kRow = 72;
 __device__ __forceinline__ h8 ld8(const _Float16* t, int row, int col)
 {
-    return *reinterpret_cast<const h8*>(t + swz(row, col));
+    return *reinterpret_cast<const h8*>(t + row * kRow + col);
 }
 __device__ __forceinline__ void st8(_Float16* t, int row, int col, h8 x)
 {
-    *reinterpret_cast<h8*>(t + swz(row, col)) = x;
+    *reinterpret_cast<h8*>(t + row * kRow + col) = x;
 }
 __device__ __forceinline__ void st4(_Float16* t, int row, int col, h4 x)
 {
-    *reinterpret_cast<h4*>(t + swz(row, col)) = x;
+    *reinterpret_cast<h4*>(t + row * kRow + col) = x;
 }
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c)
@@ -197,18 +193,19 @@ struct FusedArgs {
 };
 
 struct Smem {
-    // Kh and Sc are adjacent: the exact-score path uses them as one fp32 table
+    // Kh and Sc are adjacent: the exact-score path uses them as one fp32 table.
+    // Kh .. ST0 (five tiles) also serve as the exchange scratch.
     _Float16 Kh[kTile];       // k 2^{r-b}, rows s
     _Float16 Sc[kTile];       // per-wave rows: scores [t][s], then output staging [t][j]
-    _Float16 KtT[kTile];      // (k 2^{b_last-b})^T  [i][s]
+    _Float16 KtT[kTile];      // (k 2^{b_last-b})^T  [i][s]   (exact path: raw k)
     _Float16 VT[kTile];       // v^T                 [j][s]
-    _Float16 ST[2][kTile];    // fp16 state, transposed [j][i]
+    _Float16 ST0[kTile];      // fp16 state, transposed [j][i]
     float tot[4][kD];         // per-wave sums of log2 gates
     float bfirst[kD];         // log2 gate of the chunk's first row
     float pre[4][kD];         // prefix offset of each wave's rows
     float ref[kD];            // reference point r
-    float cq[kD];             // 2^r
-    float ck[kD];             // 2^{b_last - r}
+    _Float16 cq16[kD];        // 2^r
+    _Float16 ck16[kD];        // 2^{b_last - r}
     float dcv[kD];            // 2^{b_last} = d_c
     float blast[kD];          // b_last (log2 of d_c)
     float P[kMaxKeep + 1][kD];  // log2 decay from the span start to each chunk start
@@ -216,7 +213,10 @@ struct Smem {
     unsigned int tag;
     int fail;
     int stale;
+    _Float16 ST1[kTile];      // second state buffer, last: one-chunk spans never use it
 };
+
+__device__ __forceinline__ _Float16* st_tile(Smem& sm, int i) { return i ? sm.ST1 : sm.ST0; }
 
 struct ChunkRegs {
     u4 q[2], k[2], v[2], g[2];
@@ -254,16 +254,16 @@ __device__ __forceinline__ void load_chunk(const FusedArgs& a, int b, int h, int
 }
 
 // Exact fp32 scores of the wave's rows t = 16w + r for a chunk whose gate
-// range is too wide for the factorised form. The fp32 prefix of every row
-// sits in the Kh+Sc table, raw k in ST[kbuf]; each lane sums its own 16 dims
-// and four lanes (one per dim group) combine their partial sums.
+// range is too wide for the factorised form. The fp32 prefix of every row goes
+// to the Kh+Sc table and raw k to KtT (the state update has consumed it); each
+// lane sums its own 16 dims and four lanes (one per dim group) combine.
 __device__ void exact_scores(Smem& sm, const ChunkRegs& R, const float (&x)[2][8], int w,
-                             int lane, int kbuf, f4 (&sc)[4])
+                             int lane, f4 (&sc)[4])
 {
     const int r = lane & 15, g = lane >> 4;
     const int t = 16 * w + r;
     float* Bt = reinterpret_cast<float*>(sm.Kh);       // [64][64] fp32, overlays Kh and Sc
-    _Float16* Kr = sm.ST[kbuf];                        // [64][64] raw k, row-major
+    _Float16* Kr = sm.KtT;                             // [64][64] raw k, row-major
     lds_barrier();
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -311,15 +311,22 @@ __device__ void exact_scores(Smem& sm, const ChunkRegs& R, const float (&x)[2][8
     lds_barrier();
 }
 
-// ---------------------------------------------------------------------------
-// One chunk. FULL: outputs too (O += scores V [+ Qt ST]); otherwise only the
-// state update. S (C layout: rows 16w+4g+e, cols 16jt+r) enters as the state
-// at the chunk start and leaves as the state after it. ST[st] holds fp16(S)
-// transposed when has_state. Writes ST[st ^ 1] when write_next.
+// What the output half of a chunk needs from its front half.
+struct ChunkTmp {
+    h8 qh[2];        // q 2^{b-r} (factorised scores)
+    float x[2][8];   // log2 prefix b (exact scores)
+    bool exact;
+};
+
+// Front half of one chunk: log2-gate prefix, per-dim constants, operand tiles,
+// and the state update S <- Diag(d_c) S + (k 2^{b_last-b})^T v. S (C layout:
+// rows 16w+4g+e, cols 16jt+r) enters as the state at the chunk start and
+// leaves as the state after it; written transposed to ST[st ^ 1] when
+// write_next. FULL also prepares the output half (Qt = q 2^b, Kh, qh).
 template <bool FULL>
-__device__ __forceinline__ void chunk_step(Smem& sm, const ChunkRegs& R, int w, int lane, int c,
-                                           f4 (&S)[4], int st, bool has_state, bool write_next,
-                                           f4 (&O)[4], h8 (&Qt)[2])
+__device__ __forceinline__ void chunk_front(Smem& sm, const ChunkRegs& R, int w, int lane, int c,
+                                            f4 (&S)[4], int st, bool write_next, h8 (&Qt)[2],
+                                            ChunkTmp& T)
 {
     const int r = lane & 15, g = lane >> 4;
     const int tid = 64 * w + lane;
@@ -365,8 +372,8 @@ __device__ __forceinline__ void chunk_step(Smem& sm, const ChunkRegs& R, int w, 
         const float bf = sm.bfirst[d];
         const float rf = 0.5f * (bf + bl);
         sm.ref[d] = rf;
-        sm.cq[d] = ex2(rf);
-        sm.ck[d] = ex2(bl - rf);
+        sm.cq16[d] = (_Float16)ex2(rf);
+        sm.ck16[d] = (_Float16)ex2(bl - rf);
         sm.dcv[d] = ex2(bl);
         sm.blast[d] = bl;
         sm.Pend[d] += bl;
@@ -377,7 +384,6 @@ __device__ __forceinline__ void chunk_step(Smem& sm, const ChunkRegs& R, int w, 
     lds_barrier();  // (A2)
 
     const bool exact = FULL && sm.fail;
-    h8 qh[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const int d0 = 32 * hh + 8 * g;
@@ -385,30 +391,34 @@ __device__ __forceinline__ void chunk_step(Smem& sm, const ChunkRegs& R, int w, 
         ld_f8(&sm.pre[w][d0], pre);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[hh][e] += pre[e];
-        float kf[8], kt[8];
-        unpack8(R.k[hh], kf);
+        h8 kt8;
         if (FULL && !exact) {
-            float rf[8], cq[8], ck[8], qf[8], q1[8], q2[8], k1[8];
+            // E = 2^{b-r} and 1/E in fp32, the products in packed fp16
+            float rf[8], ef[8], ei[8];
             ld_f8(&sm.ref[d0], rf);
-            ld_f8(&sm.cq[d0], cq);
-            ld_f8(&sm.ck[d0], ck);
-            unpack8(R.q[hh], qf);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float E = ex2(x[hh][e] - rf[e]);
-                q1[e] = qf[e] * E;
-                q2[e] = q1[e] * cq[e];
-                k1[e] = kf[e] * rcp(E);
-                kt[e] = k1[e] * ck[e];
+                const float dlt = x[hh][e] - rf[e];
+                ef[e] = ex2(dlt);
+                ei[e] = ex2(-dlt);
             }
-            qh[hh] = pack8(q1);
-            Qt[hh] = pack8(q2);
-            st8(sm.Kh, 16 * w + r, d0, pack8(k1));
+            const h8 cq = *reinterpret_cast<const h8*>(&sm.cq16[d0]);
+            const h8 ck = *reinterpret_cast<const h8*>(&sm.ck16[d0]);
+            const h8 q8 = __builtin_bit_cast(h8, R.q[hh]);
+            const h8 k8 = __builtin_bit_cast(h8, R.k[hh]);
+            const h8 qh = q8 * pack8(ef);
+            const h8 kh = k8 * pack8(ei);
+            T.qh[hh] = qh;
+            Qt[hh] = qh * cq;
+            kt8 = kh * ck;
+            st8(sm.Kh, 16 * w + r, d0, kh);
         } else {
-            float bl[8];
+            float bl[8], kf[8], kt[8];
             ld_f8(&sm.blast[d0], bl);
+            unpack8(R.k[hh], kf);
 #pragma unroll
             for (int e = 0; e < 8; ++e) kt[e] = kf[e] * ex2(bl[e] - x[hh][e]);
+            kt8 = pack8(kt);
             if (FULL) {
                 float qf[8], q2[8];
                 unpack8(R.q[hh], qf);
@@ -418,7 +428,6 @@ __device__ __forceinline__ void chunk_step(Smem& sm, const ChunkRegs& R, int w, 
             }
         }
         // transposes through the MFMA: D[m][n] = X[16w + m][32hh + 16half + n]
-        const h8 kt8 = pack8(kt);
         const h8 v8 = __builtin_bit_cast(h8, R.v[hh]);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -432,49 +441,6 @@ __device__ __forceinline__ void chunk_step(Smem& sm, const ChunkRegs& R, int w, 
         }
     }
     lds_barrier();  // (B)
-
-    if (FULL) {
-        const int t = 16 * w + r;
-        f4 sc[4];
-        if (!exact) {
-            // Sc^T[s][t] = sum_i Kh[s][i] Qh[t][i] for s-blocks up to the diagonal
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                sc[sb] = f4{0.f, 0.f, 0.f, 0.f};
-                if (sb <= w) {
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        sc[sb] = mfma(ld8(sm.Kh, 16 * sb + r, 32 * ks + 8 * g), qh[ks], sc[sb]);
-                }
-            }
-        } else {
-            exact_scores(sm, R, x, w, lane, st ^ 1, sc);
-        }
-        // mask, and write the wave's score rows Sc[t][s] (zeros above the diagonal)
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            h4 hv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                hv[e] = (_Float16)((16 * sb + 4 * g + e <= t) ? sc[sb][e] : 0.f);
-            st4(sm.Sc, t, 16 * sb + 4 * g, hv);
-        }
-        // O^T[j][t] += sum_s VT[j][s] Sc[t][s] (+ sum_i ST[j][i] Qt[t][i])
-        const int kmax = (w >= 2) ? 2 : 1;
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                if (ks < kmax)
-                    O[jt] = mfma(ld8(sm.VT, 16 * jt + r, 32 * ks + 8 * g),
-                                 ld8(sm.Sc, t, 32 * ks + 8 * g), O[jt]);
-            if (has_state) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    O[jt] = mfma(ld8(sm.ST[st], 16 * jt + r, 32 * ks + 8 * g), Qt[ks], O[jt]);
-            }
-        }
-    }
 
     // -- state: S[i][j] <- d_c[i] S[i][j] + sum_s KtT[i][s] VT[j][s]
     const f4 dc = *reinterpret_cast<const f4*>(&sm.dcv[16 * w + 4 * g]);
@@ -490,7 +456,62 @@ __device__ __forceinline__ void chunk_step(Smem& sm, const ChunkRegs& R, int w, 
     if (write_next) {
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
-            st4(sm.ST[st ^ 1], 16 * jt + r, 16 * w + 4 * g, pack4(S[jt], 1.f));
+            st4(st_tile(sm, st ^ 1), 16 * jt + r, 16 * w + 4 * g, pack4(S[jt], 1.f));
+    }
+    if (FULL) {
+        T.exact = exact;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) T.x[hh][e] = x[hh][e];
+    }
+}
+
+// Output half of one chunk: O^T[j][t] += sum_s VT[j][s] Sc[t][s], plus
+// sum_i ST[st][j][i] Qt[t][i] when has_state.
+__device__ __forceinline__ void chunk_back(Smem& sm, const ChunkRegs& R, int w, int lane, int st,
+                                           bool has_state, f4 (&O)[4], const h8 (&Qt)[2],
+                                           const ChunkTmp& T)
+{
+    const int r = lane & 15, g = lane >> 4;
+    const int t = 16 * w + r;
+    f4 sc[4];
+    if (!T.exact) {
+        // Sc^T[s][t] = sum_i Kh[s][i] Qh[t][i] for s-blocks up to the diagonal
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            sc[sb] = f4{0.f, 0.f, 0.f, 0.f};
+            if (sb <= w) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    sc[sb] = mfma(ld8(sm.Kh, 16 * sb + r, 32 * ks + 8 * g), T.qh[ks], sc[sb]);
+            }
+        }
+    } else {
+        exact_scores(sm, R, T.x, w, lane, sc);
+    }
+    // mask, and write the wave's score rows Sc[t][s] (zeros above the diagonal)
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+        h4 hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            hv[e] = (_Float16)((16 * sb + 4 * g + e <= t) ? sc[sb][e] : 0.f);
+        st4(sm.Sc, t, 16 * sb + 4 * g, hv);
+    }
+    const int kmax = (w >= 2) ? 2 : 1;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            if (ks < kmax)
+                O[jt] = mfma(ld8(sm.VT, 16 * jt + r, 32 * ks + 8 * g), ld8(sm.Sc, t, 32 * ks + 8 * g),
+                             O[jt]);
+        if (has_state) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                O[jt] = mfma(ld8(st_tile(sm, st), 16 * jt + r, 32 * ks + 8 * g), Qt[ks], O[jt]);
+        }
     }
 }
 
@@ -512,6 +533,22 @@ __device__ __forceinline__ void store_out(Smem& sm, const FusedArgs& a, int b, i
                                         reinterpret_cast<u4*>(a.out + off + 8 * g + 32 * hh));
         }
     }
+}
+
+// Publish a span summary: U = local final state (C layout in S), D = decay
+// of the span, as tagged words (U at i * 64 + j, D at 4096 + i).
+__device__ __forceinline__ void publish_summary(const FusedArgs& a, const Smem& sm, const f4 (&S)[4],
+                                                long long slot, int w, int lane)
+{
+    const int r = lane & 15, g = lane >> 4;
+    const unsigned int tag = sm.tag;
+    u64* my_agg = a.agg + slot * kAggWords;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            ll_store(my_agg + (16 * w + 4 * g + e) * kD + 16 * jt + r, S[jt][e], tag);
+    if (w == 0) ll_store(my_agg + kD * kD + lane, ex2(sm.Pend[lane]), tag);
 }
 
 // ---------------------------------------------------------------------------
@@ -546,6 +583,9 @@ gla_fused_kernel(FusedArgs a)
     }
 
     // ---- 1. local pass --------------------------------------------------------
+    // The span summary is published right after the last chunk's state update,
+    // before that chunk's outputs, so the exchange overlaps them.
+    const long long seq_slot = (long long)local_seq * a.n_spans;
     f4 S[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) S[n] = f4{0.f, 0.f, 0.f, 0.f};
@@ -558,34 +598,29 @@ gla_fused_kernel(FusedArgs a)
             for (int n = 0; n < 4; ++n) O[c][n] = f4{0.f, 0.f, 0.f, 0.f};
             if (c < n_c) {
                 if (c + 1 < n_c) load_chunk<true>(a, b, h, (c_first + c + 1) * kC, w, lane, nxt);
-                chunk_step<true>(sm, cur, w, lane, c, S, c & 1, c > 0, c + 1 < n_c, O[c], Qt[c]);
+                ChunkTmp T;
+                chunk_front<true>(sm, cur, w, lane, c, S, c & 1, c + 1 < n_c, Qt[c], T);
+                if (c + 1 == n_c) publish_summary(a, sm, S, seq_slot + j, w, lane);
+                chunk_back(sm, cur, w, lane, c & 1, c > 0, O[c], Qt[c], T);
                 if (c + 1 < n_c) cur = nxt;
             }
         }
     } else {
         h8 qdummy[2];
-        f4 odummy[4];
+        ChunkTmp T;
         for (int c = 0; c < n_c; ++c) {
             if (c + 1 < n_c) load_chunk<false>(a, b, h, (c_first + c + 1) * kC, w, lane, nxt);
-            chunk_step<false>(sm, cur, w, lane, c, S, 0, false, false, odummy, qdummy);
+            chunk_front<false>(sm, cur, w, lane, c, S, 0, false, qdummy, T);
             if (c + 1 < n_c) cur = nxt;
         }
+        publish_summary(a, sm, S, seq_slot + j, w, lane);
     }
 
     // ---- 2. boundary scan across the sequence's spans -------------------------
     // Exchange words are indexed i * 64 + j (state row i, column j); the span
     // decays follow at 4096 + i.
     const unsigned int tag = sm.tag;
-    const long long seq_slot = (long long)local_seq * a.n_spans;
-    {
-        u64* my_agg = a.agg + (seq_slot + j) * kAggWords;
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                ll_store(my_agg + (16 * w + 4 * g + e) * kD + 16 * jt + r, S[jt][e], tag);
-        if (tid < kD) ll_store(my_agg + kD * kD + tid, ex2(sm.Pend[tid]), tag);
-    }
+    lds_barrier();   // every wave is done with the chunk tiles
     // The chunk tiles are free now: 48 KB of LDS scratch for the exchange.
     unsigned char* scr = reinterpret_cast<unsigned char*>(sm.Kh);
     {
@@ -726,7 +761,7 @@ gla_fused_kernel(FusedArgs a)
         if (j > 0) {
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
-                st4(sm.ST[0], 16 * jt + r, 16 * w + 4 * g, pack4(Sin[jt], 1.f));
+                st4(sm.ST0, 16 * jt + r, 16 * w + 4 * g, pack4(Sin[jt], 1.f));
         }
         lds_barrier();
 #pragma unroll
@@ -745,7 +780,7 @@ gla_fused_kernel(FusedArgs a)
                     }
 #pragma unroll
                     for (int jt = 0; jt < 4; ++jt)
-                        O[c][jt] = mfma(ld8(sm.ST[0], 16 * jt + r, 32 * hh + 8 * g), qs, O[c][jt]);
+                        O[c][jt] = mfma(ld8(sm.ST0, 16 * jt + r, 32 * hh + 8 * g), qs, O[c][jt]);
                 }
             }
             store_out(sm, a, b, h, (c_first + c) * kC, w, lane, O[c]);
@@ -757,7 +792,7 @@ gla_fused_kernel(FusedArgs a)
         if (j > 0) {
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
-                st4(sm.ST[0], 16 * jt + r, 16 * w + 4 * g, pack4(S[jt], 1.f));
+                st4(sm.ST0, 16 * jt + r, 16 * w + 4 * g, pack4(S[jt], 1.f));
         }
         load_chunk<true>(a, b, h, c_first * kC, w, lane, cur);
         int st = 0;
@@ -767,8 +802,9 @@ gla_fused_kernel(FusedArgs a)
             h8 qt[2];
 #pragma unroll
             for (int n = 0; n < 4; ++n) Oc[n] = f4{0.f, 0.f, 0.f, 0.f};
-            chunk_step<true>(sm, cur, w, lane, kMaxKeep, S, st, (j > 0) || (c > 0), c + 1 < n_c,
-                             Oc, qt);
+            ChunkTmp T;
+            chunk_front<true>(sm, cur, w, lane, kMaxKeep, S, st, c + 1 < n_c, qt, T);
+            chunk_back(sm, cur, w, lane, st, (j > 0) || (c > 0), Oc, qt, T);
             store_out(sm, a, b, h, (c_first + c) * kC, w, lane, Oc);
             st ^= 1;
             if (c + 1 < n_c) cur = nxt;
@@ -803,6 +839,12 @@ static const void* pick_kernel(int span, bool keep)
     return (const void*)gla_fused_kernel<2, true>;
 }
 
+// Dynamic LDS of a variant: one-chunk spans never touch the second state buffer.
+static size_t smem_bytes(int span, bool keep)
+{
+    return (keep && span == 1) ? offsetof(Smem, ST1) : sizeof(Smem);
+}
+
 // Workgroups of one variant that fit on a CU at once.
 static int resident_per_cu(int span, bool keep)
 {
@@ -811,10 +853,10 @@ static int resident_per_cu(int span, bool keep)
     if (c == 0) {
         const void* fn = pick_kernel(span, keep);
         int n = 0;
-        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)sizeof(Smem)) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, sizeof(Smem)) !=
+        const size_t sh = smem_bytes(span, keep);
+        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh) !=
                 hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, sh) != hipSuccess ||
             n < 1)
             n = 1;
         c = n;
@@ -906,7 +948,7 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
         const int nseq = (n_seq - s0 < p.seq_batch) ? (n_seq - s0) : p.seq_batch;
         void* args[] = {&a};
         const hipError_t e = hipLaunchKernel(fn, dim3(nseq * p.n_spans), dim3(kThreads), args,
-                                             sizeof(Smem), st);
+                                             smem_bytes(p.span, p.keep), st);
         if (e != hipSuccess) return e;
     }
     return hipGetLastError();
