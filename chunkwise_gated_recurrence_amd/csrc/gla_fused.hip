@@ -26,12 +26,21 @@
 //      store them. Without KEEP: stream the span again (mostly from cache)
 //      starting from S_in and store the outputs as they are produced.
 //
-// Exchanged values travel as 8-byte words {float value, 32-bit tag} written
-// and read with device-scope (sc1) accesses. A reader polls the words
-// themselves until every tag equals this launch's tag, so a hand-over costs
-// one memory round trip: no flags, no fences, no atomics. The tag is a
-// per-sequence epoch kept in the workspace, advanced once per launch, so a
-// workspace is cleared only once.
+// Exchanged values travel as 4-byte words: an fp32 value rounded to 16
+// mantissa bits whose low 8 bits carry a tag, written and read with
+// device-scope (sc1) accesses. A reader polls the words themselves until every
+// tag equals the expected one, so a hand-over costs one memory round trip: no
+// flags, no fences, no atomics. Each exchange slot (sequence in the launch,
+// span) has its own epoch in the workspace; the words of a slot are rewritten
+// in full by every launch that uses it and its epoch is advanced once all of
+// that launch's readers know it, so the words in memory always carry the
+// previous tag and a workspace is cleared only once. The rounding perturbs an
+// exchanged value by at most 2^-16 of itself.
+//
+// Roles inside a workgroup: waves 0-1 wait on global loads (polls), waves 2-3
+// issue the exchange stores. One counter tracks a wave's loads and stores
+// together, so a wave that waits for a load also waits for every store it has
+// in flight; keeping the roles apart keeps store latency off the polls.
 //
 // Per chunk (wave w owns rows 16w..16w+15 of the chunk and state rows
 // 16w..16w+15; lane l holds row r = l & 15 and dims 8(l >> 4) + 32h + e):
@@ -66,11 +75,10 @@ constexpr int kMaxKeep = 2;       // longest span kept on chip
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kGuard = 16.0f;   // max log2 range of a chunk for factorised scores
 constexpr int kTile = kC * 72;    // halves per LDS tile (rows padded to 72)
-constexpr int kAggWords = kD * kD + kD;   // U (lane order) then D
+constexpr int kAggWords = kD * kD + kD;   // U and D words of one span summary
 constexpr unsigned int kMaxPolls = 1u << 22;
 constexpr int kMaxSpans = 64;        // spans per sequence
-constexpr int kScanU = 40 * 1024;    // exchange scratch: span words of a slice
-constexpr int kScanD = 512;          // exchange scratch: decays of a slice (floats)
+constexpr int kScanD = 32 * 1024;    // exchange scratch: byte offset of the decays
 constexpr int kDevScope = 16;        // cache policy: device-scope (sc1) access
 
 // ---------------------------------------------------------------------------
@@ -117,17 +125,28 @@ __device__ __forceinline__ float row_shr(float x)
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// Tagged exchange words.
-__device__ __forceinline__ void ll_store(u64* p, float v, unsigned int tag)
+// Tagged exchange words: value rounded to nearest at 16 mantissa bits, tag in
+// the low 8 bits.
+__device__ __forceinline__ unsigned int ll_word(float v, unsigned int tag)
 {
-    __hip_atomic_store(p, ((u64)tag << 32) | (u64)__float_as_uint(v), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    return ((__float_as_uint(v) + 0x80u) & 0xFFFFFF00u) | tag;
 }
-__device__ __forceinline__ bool ll_load(const u64* p, unsigned int tag, float& v)
+__device__ __forceinline__ float ll_value(unsigned int x) { return __uint_as_float(x & 0xFFFFFF00u); }
+__device__ __forceinline__ bool ll_ok(unsigned int x, unsigned int tag) { return (x & 0xFFu) == tag; }
+
+// Buffer resource over n_bytes at base: accesses past the end read zeros and
+// are dropped on write.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int n_bytes)
 {
-    const u64 x = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    v = __uint_as_float((unsigned int)x);
-    return (unsigned int)(x >> 32) == tag;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n_bytes, 0x00020000);
+}
+__device__ __forceinline__ void st_dev1(__amdgpu_buffer_rsrc_t rs, int voff, unsigned int x)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(x, rs, voff, 0, kDevScope);
+}
+__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t rs, int voff, u4 x)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(x, rs, voff, 0, kDevScope);
 }
 
 __device__ __forceinline__ void unpack8(u4 u, float* f)
@@ -179,16 +198,16 @@ struct FusedArgs {
     const __half* lg;
     __half* out;
     float* final_state;
-    unsigned int* epoch;        // [seq in launch] launches completed
+    unsigned int* epoch;        // [seq in launch][n_spans] low 8 bits: tag of the slot's words
     unsigned int* err;          // set when a wait gives up
-    u64* agg;                   // [seq in launch][n_spans][kAggWords]  tagged
-    u64* sin;                   // [seq in launch][n_spans][kD * kD]   tagged
+    unsigned int* agg;          // [seq in launch][agg_seq_words(n_spans)]  tagged, owner-major
+    unsigned int* sin;          // [seq in launch][n_spans][kD * kD]   tagged
     int L, H, grid_h, grid_w, dir;
     int n_chunks;               // per sequence
     int span;                   // chunks per workgroup
     int n_spans;                // workgroups per sequence
     int seq0;                   // first sequence of this launch
-    int slice;                  // state elements per workgroup in the scan
+    int slice_log2;             // log2 of the state elements each owner scans
     float scale;
 };
 
@@ -210,7 +229,7 @@ struct Smem {
     float blast[kD];          // b_last (log2 of d_c)
     float P[kMaxKeep + 1][kD];  // log2 decay from the span start to each chunk start
     float Pend[kD];           // log2 decay of the span so far
-    unsigned int tag;
+    unsigned int tags[kMaxSpans];   // expected tag of every span slot of the sequence
     int fail;
     int stale;
     _Float16 ST1[kTile];      // second state buffer, last: one-chunk spans never use it
@@ -230,10 +249,22 @@ __device__ __forceinline__ long long row_offset(const FusedArgs& a, int b, int h
     return (((long long)b * a.L + p) * a.H + h) * kD;
 }
 
-__device__ __forceinline__ u4 load16(const __half* base, long long off)
+// Buffer resource over batch b of a [B, L, H, 64] fp16 tensor. Buffer loads
+// past num_records return zeros, so rows beyond the sequence end read as zero
+// without a branch (a branch around a load makes the compiler wait for it).
+constexpr int kNT = 2;   // cache policy: streaming (nontemporal) access
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t batch_rsrc(const __half* base, const FusedArgs& a,
+                                                             int b)
 {
-    if (off < 0) return u4{0u, 0u, 0u, 0u};
-    return __builtin_nontemporal_load(reinterpret_cast<const u4*>(base + off));
+    const long long per_batch = (long long)a.L * a.H * kD;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + b * per_batch), (short)0,
+                                             (int)(per_batch * 2), 0x00020000);
+}
+
+__device__ __forceinline__ u4 load16(__amdgpu_buffer_rsrc_t rs, int voff)
+{
+    return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, kNT));
 }
 
 // Lane l of wave w loads row 16w + (l & 15), dims 8(l >> 4) + 32h .. +7.
@@ -241,15 +272,19 @@ template <bool WITH_Q>
 __device__ __forceinline__ void load_chunk(const FusedArgs& a, int b, int h, int t0, int w,
                                            int lane, ChunkRegs& R)
 {
-    const long long off = row_offset(a, b, h, t0 + 16 * w + (lane & 15));
-    const int col = 8 * (lane >> 4);
+    const int t = t0 + 16 * w + (lane & 15);
+    const int bytes = a.L * a.H * kD * 2;
+    const int voff = t < a.L
+        ? (scan_to_spatial(t, a.L, a.grid_h, a.grid_w, a.dir) * a.H + h) * (kD * 2) + 16 * (lane >> 4)
+        : bytes;
+    const __amdgpu_buffer_rsrc_t rk = batch_rsrc(a.k, a, b), rv = batch_rsrc(a.v, a, b),
+                                 rg = batch_rsrc(a.lg, a, b);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-        const long long o = off < 0 ? -1 : off + col + 32 * hh;
-        if (WITH_Q) R.q[hh] = load16(a.q, o);
-        R.k[hh] = load16(a.k, o);
-        R.v[hh] = load16(a.v, o);
-        R.g[hh] = load16(a.lg, o);
+        if (WITH_Q) R.q[hh] = load16(batch_rsrc(a.q, a, b), voff + 64 * hh);
+        R.k[hh] = load16(rk, voff + 64 * hh);
+        R.v[hh] = load16(rv, voff + 64 * hh);
+        R.g[hh] = load16(rg, voff + 64 * hh);
     }
 }
 
@@ -535,20 +570,91 @@ __device__ __forceinline__ void store_out(Smem& sm, const FusedArgs& a, int b, i
     }
 }
 
+// Summary words of one sequence, owner-major: for each owner o (slice of
+// 2^lo state elements) a contiguous region [ns][slice] of U words, then
+// [ns][slice / 64] D words (the decays of the slice's state rows), padded to
+// 16 bytes. An owner then reads its whole input as one contiguous block.
+__device__ __forceinline__ int owner_region_words(int ns, int lo)
+{
+    return (ns << lo) + (((ns << (lo - 6)) + 3) & ~3);
+}
+__host__ __device__ inline long long agg_seq_words(int ns) { return (long long)ns * kAggWords + 256; }
+
 // Publish a span summary: U = local final state (C layout in S), D = decay
-// of the span, as tagged words (U at i * 64 + j, D at 4096 + i).
-__device__ __forceinline__ void publish_summary(const FusedArgs& a, const Smem& sm, const f4 (&S)[4],
-                                                long long slot, int w, int lane)
+// of the span, as tagged words of slot `slot` (U at i * 64 + j, D at 4096 + i).
+// Also turns the epochs loaded at the start (thread t < n_spans holds the one
+// of span t in ep) into the tag table. Waves 0-1 hand their U rows to the
+// storer waves through ST0 (free here: no kept chunk reads it).
+constexpr int kU01 = 68;   // fp32 row stride of the handed-over rows (no bank conflicts)
+
+__device__ __forceinline__ void publish_summary(const FusedArgs& a, Smem& sm, const f4 (&S)[4],
+                                                long long slot, int j, unsigned int ep, int w,
+                                                int lane)
 {
     const int r = lane & 15, g = lane >> 4;
-    const unsigned int tag = sm.tag;
-    u64* my_agg = a.agg + slot * kAggWords;
+    const int tid = 64 * w + lane;
+    // Every chunk load has landed (or reads past the end): retire them all
+    // here, so that no later wait on a reused register waits for these stores.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    float* u01 = reinterpret_cast<float*>(sm.ST0);
+    if (w < 2) {
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
+        for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            ll_store(my_agg + (16 * w + 4 * g + e) * kD + 16 * jt + r, S[jt][e], tag);
-    if (w == 0) ll_store(my_agg + kD * kD + lane, ex2(sm.Pend[lane]), tag);
+            for (int e = 0; e < 4; ++e) u01[(16 * w + 4 * g + e) * kU01 + 16 * jt + r] = S[jt][e];
+    }
+    if (tid < kMaxSpans) sm.tags[tid] = (ep + 1u) & 0xFFu;
+    lds_barrier();
+    if (w >= 2) {
+        const unsigned int tag = sm.tags[j];
+        const int ns = a.n_spans, lo = a.slice_log2;
+        const int ow = owner_region_words(ns, lo);
+        const long long seq_base = (slot - j) / ns * agg_seq_words(ns);
+        const __amdgpu_buffer_rsrc_t rs = rsrc(a.agg + seq_base, (int)(agg_seq_words(ns) * 4));
+        // word of state element e = i * 64 + col in the owner-major layout
+        auto uoff = [&](int e) { return (e >> lo) * ow + (j << lo) + (e & ((1 << lo) - 1)); };
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                st_dev1(rs, 4 * uoff((16 * w + 4 * g + e) * kD + 16 * jt + r), ll_word(S[jt][e], tag));
+        // rows 0-31 from LDS, 16 B per lane: row q >> 4, columns 4 (q & 15) .. +3
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int q = tid - 128 + 128 * k;
+            const int row = q >> 4, c4 = 4 * (q & 15);
+            const f4 x = *reinterpret_cast<const f4*>(u01 + row * kU01 + c4);
+            u4 t;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[e] = ll_word(x[e], tag);
+            st_dev4(rs, 4 * uoff(row * kD + c4), t);
+        }
+        if (w == 2) {
+            // decay of state row `lane`: owner (64 lane) >> lo, row within its slice
+            const int o = (kD * lane) >> lo, ri = lane - (o << (lo - 6));
+            st_dev1(rs, 4 * (o * ow + (ns << lo) + (j << (lo - 6)) + ri),
+                    ll_word(ex2(sm.Pend[lane]), tag));
+        }
+    }
+}
+
+// Local pass of a kept span of NC chunks (cur, then nxt): intra-chunk outputs
+// into O, decay-scaled queries into Qt, final local state in S; the summary is
+// published right after the last state update.
+template <int NC, int SPAN>
+__device__ __forceinline__ void keep_pass(const FusedArgs& a, Smem& sm, const ChunkRegs& cur,
+                                          const ChunkRegs& nxt, int w, int lane, f4 (&S)[4],
+                                          f4 (&O)[SPAN][4], h8 (&Qt)[SPAN][2], long long slot,
+                                          int j, unsigned int ep)
+{
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const ChunkRegs& R = c == 0 ? cur : nxt;
+        ChunkTmp T;
+        chunk_front<true>(sm, R, w, lane, c, S, c & 1, c + 1 < NC, Qt[c], T);
+        if (c + 1 == NC) publish_summary(a, sm, S, slot, j, ep, w, lane);
+        chunk_back(sm, R, w, lane, c & 1, c > 0, O[c], Qt[c], T);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -556,6 +662,7 @@ template <int SPAN, bool KEEP>
 __global__ void __launch_bounds__(kThreads, (KEEP && SPAN == 1) ? 3 : 2)
 gla_fused_kernel(FusedArgs a)
 {
+    static_assert(!KEEP || SPAN <= kMaxKeep, "a kept span holds at most kMaxKeep chunks");
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
 
@@ -571,21 +678,28 @@ gla_fused_kernel(FusedArgs a)
     const int span = KEEP ? SPAN : a.span;
     const int c_first = j * span;
     const int n_c = min(span, a.n_chunks - c_first);
+    __builtin_assume(n_c >= 1);   // every span starts inside the sequence
 
+    // Epochs of the sequence's span slots (thread t < n_spans reads slot t;
+    // the rest read zeros past the end), then the chunk loads: a kept span
+    // issues the loads of all its chunks up front. The epochs are first used
+    // at the publish, so nothing waits for them before.
+    const long long seq_slot = (long long)local_seq * a.n_spans;
+    const unsigned int ep = __builtin_amdgcn_raw_buffer_load_b32(
+        rsrc(a.epoch + seq_slot, 4 * a.n_spans), 4 * tid, 0, kDevScope);
     ChunkRegs cur, nxt;
     load_chunk<KEEP>(a, b, h, c_first * kC, w, lane, cur);
+    // Loads are never under a branch (the compiler would wait for them at the
+    // join); a chunk past the span's end starts at L and reads zeros.
+    if (KEEP && SPAN > 1) load_chunk<true>(a, b, h, n_c > 1 ? (c_first + 1) * kC : a.L, w, lane, nxt);
     if (tid < kD) {
         sm.P[0][tid] = 0.f;
         sm.Pend[tid] = 0.f;
-    }
-    if (tid == 0) {
-        sm.tag = __hip_atomic_load(a.epoch + local_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     }
 
     // ---- 1. local pass --------------------------------------------------------
     // The span summary is published right after the last chunk's state update,
     // before that chunk's outputs, so the exchange overlaps them.
-    const long long seq_slot = (long long)local_seq * a.n_spans;
     f4 S[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) S[n] = f4{0.f, 0.f, 0.f, 0.f};
@@ -593,140 +707,209 @@ gla_fused_kernel(FusedArgs a)
     h8 Qt[KEEP ? SPAN : 1][2];
     if (KEEP) {
 #pragma unroll
-        for (int c = 0; c < SPAN; ++c) {
+        for (int c = 0; c < (KEEP ? SPAN : 1); ++c)
 #pragma unroll
             for (int n = 0; n < 4; ++n) O[c][n] = f4{0.f, 0.f, 0.f, 0.f};
-            if (c < n_c) {
-                if (c + 1 < n_c) load_chunk<true>(a, b, h, (c_first + c + 1) * kC, w, lane, nxt);
-                ChunkTmp T;
-                chunk_front<true>(sm, cur, w, lane, c, S, c & 1, c + 1 < n_c, Qt[c], T);
-                if (c + 1 == n_c) publish_summary(a, sm, S, seq_slot + j, w, lane);
-                chunk_back(sm, cur, w, lane, c & 1, c > 0, O[c], Qt[c], T);
-                if (c + 1 < n_c) cur = nxt;
-            }
-        }
+        // Straight-line code with no branch on the chunk count, so that no
+        // path past the publish stores has a chunk load in flight (a wait for
+        // one would also wait for the stores). A span that ends early runs an
+        // empty chunk: zero rows leave the state and the decay unchanged and
+        // their outputs are never stored.
+        keep_pass<(KEEP ? SPAN : 1)>(a, sm, cur, nxt, w, lane, S, O, Qt, seq_slot + j, j, ep);
     } else {
         h8 qdummy[2];
         ChunkTmp T;
         for (int c = 0; c < n_c; ++c) {
-            if (c + 1 < n_c) load_chunk<false>(a, b, h, (c_first + c + 1) * kC, w, lane, nxt);
+            load_chunk<false>(a, b, h, c + 1 < n_c ? (c_first + c + 1) * kC : a.L, w, lane, nxt);
             chunk_front<false>(sm, cur, w, lane, c, S, 0, false, qdummy, T);
-            if (c + 1 < n_c) cur = nxt;
+            cur = nxt;
         }
-        publish_summary(a, sm, S, seq_slot + j, w, lane);
+        publish_summary(a, sm, S, seq_slot + j, j, ep, w, lane);
     }
 
     // ---- 2. boundary scan across the sequence's spans -------------------------
-    // Exchange words are indexed i * 64 + j (state row i, column j); the span
-    // decays follow at 4096 + i.
-    const unsigned int tag = sm.tag;
+    // The first `owners` workgroups (a power of two <= n_spans) each own a
+    // slice of 2^slice_log2 state elements: they read that slice of every
+    // span's U and D, fold S_in[m+1] = D_m S_in[m] + U_m through the spans, and
+    // write every span's incoming state (and the final state) for the slice.
+    // Then every workgroup reads its own S_in.
     lds_barrier();   // every wave is done with the chunk tiles
-    // The chunk tiles are free now: 48 KB of LDS scratch for the exchange.
+    // The chunk tiles are free now: 45 KB of LDS scratch for the exchange.
     unsigned char* scr = reinterpret_cast<unsigned char*>(sm.Kh);
-    {
-        // My slice: elements [e_first, e_first + ecount) of the state, through
-        // every span of the sequence. All words arrive by DMA into LDS, tags
-        // are checked there.
-        const int ns = a.n_spans;
-        const int e_first = j * a.slice;
-        const int ecount = max(0, min(a.slice, kD * kD - e_first));
-        if (ecount > 0) {
-            const u64* agg0 = a.agg + seq_slot * kAggWords;
-            u64* sin0 = a.sin + seq_slot * (kD * kD);
-            const int i0 = e_first >> 6;
-            const int nrows = ((e_first + ecount - 1) >> 6) - i0 + 1;
-            u64* ubuf = reinterpret_cast<u64*>(scr);                 // [ns][ecount]
-            float* dbuf = reinterpret_cast<float*>(scr + kScanU);    // [ns][nrows]
-            float* compA = dbuf + kScanD;
-            float* compB = compA + kThreads;
-            const int half = ecount >> 1;              // 16 B lane loads per span
-            const int nl = ns * half;
-            for (unsigned int polls = 0;; ++polls) {
-                for (int k0 = 64 * w; k0 < nl; k0 += kThreads) {
-                    const int q = k0 + lane;
-                    if (q < nl) {
-                        const int m = q / half, pr = q - (q / half) * half;
-                        __builtin_amdgcn_global_load_lds(
-                            agg0 + (long long)m * kAggWords + e_first + 2 * pr, ubuf + 2 * k0, 16, 0,
-                            kDevScope);
-                    }
-                }
-                bool ok = true;
-                for (int q = tid; q < ns * nrows; q += kThreads) {
-                    const int m = q / nrows, rr = q - (q / nrows) * nrows;
-                    float v;
-                    ok &= ll_load(agg0 + (long long)m * kAggWords + kD * kD + i0 + rr, tag, v);
-                    dbuf[q] = v;
+    const int ns = a.n_spans;
+    const int lo = a.slice_log2;
+    const int slice = 1 << lo;
+    if (j < (kD * kD >> lo)) {
+        const int e_first = j << lo;
+        const int lrows = lo - 6;                      // log2 of state rows in the slice
+        const int ow = owner_region_words(ns, lo);
+        const unsigned int* src = a.agg + local_seq * agg_seq_words(ns) + (long long)j * ow;
+        unsigned int* ubuf = reinterpret_cast<unsigned int*>(scr);   // [ns][slice] U, [ns][nrows] D
+        const float* dbuf = reinterpret_cast<const float*>(ubuf + (ns << lo));
+        unsigned int* fin = ubuf + ow;                                // final state of the slice
+        const int lq = lo - 2;                         // log2 of 16 B pieces per span
+        const int nl = ow >> 2;
+        for (unsigned int polls = 0;; ++polls) {
+            bool ok = true;
+            if (w < 2) {   // loader waves
+                for (int k0 = 64 * w; k0 < nl; k0 += 128) {
+                    if (k0 + lane < nl)
+                        __builtin_amdgcn_global_load_lds(src + 4 * (k0 + lane), ubuf + 4 * k0, 16, 0,
+                                                         kDevScope);
                 }
                 __builtin_amdgcn_s_waitcnt(0x0F70);
-                if (tid == 0) sm.stale = 0;
-                lds_barrier();
-                for (int q = tid; q < ns * ecount; q += kThreads)
-                    ok &= (unsigned int)(ubuf[q] >> 32) == tag;
-                if (!__all(ok) && lane == 0) sm.stale = 1;
-                lds_barrier();
-                const bool stale = sm.stale;
-                if (!stale) break;
-                if (polls > kMaxPolls) {
-                    if (tid == 0) atomicOr(a.err, 1u);
-                    break;
-                }
-                lds_barrier();   // every thread has read the flag before it is reset
-                __builtin_amdgcn_s_sleep(2);
             }
-            // P threads per element fold contiguous span ranges; LDS combines them
-            int P = 1;
-            while (P < 16 && ecount * P * 2 <= kThreads) P *= 2;
-            const int epad = kThreads / P;
-            const int p = tid / epad, el0 = tid - (tid / epad) * epad;
+            if (tid == 0) sm.stale = 0;
+            lds_barrier();
+            {
+                // U pieces (four words of one span each), every LDS read issued
+                // before the first compare; then the D words, one per thread
+                const int nu = ns << lq;                // <= 2048 pieces
+                u4 xs[8];
+                unsigned int tg[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int q = min(tid + kThreads * i, nu - 1);
+                    xs[i] = *reinterpret_cast<const u4*>(ubuf + 4 * q);
+                    tg[i] = sm.tags[q >> lq];
+                }
+                const int nd = ns << lrows;              // <= 128 words
+                const int wd = min(tid, nd - 1);
+                const unsigned int xd = ubuf[(ns << lo) + wd];
+                const unsigned int td = sm.tags[wd >> lrows];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    ok &= ll_ok(xs[i][0], tg[i]) & ll_ok(xs[i][1], tg[i]) & ll_ok(xs[i][2], tg[i]) &
+                          ll_ok(xs[i][3], tg[i]);
+                ok &= ll_ok(xd, td);
+            }
+            if (!__all(ok) && lane == 0) sm.stale = 1;
+            lds_barrier();
+            const bool stale = sm.stale;
+            if (!stale) break;
+            if (polls > kMaxPolls) {
+                if (tid == 0) atomicOr(a.err, 1u);
+                break;
+            }
+            lds_barrier();   // every thread has read the flag before it is reset
+            __builtin_amdgcn_s_sleep(2);
+        }
+        // Fold, four elements (one 16 B word group, same state row, so one
+        // decay) per thread: P = 256 / Qn contiguous span ranges per group,
+        // Qn = min(slice / 4, 256) groups at a time; LDS combines the ranges.
+        // The incoming states overwrite the U words in place (tagged); the
+        // final state goes to fin.
+        {
+            const int lQ = lo - 2;
+            const int lQn = lQ < 8 ? lQ : 8;
+            const int Qn = 1 << lQn;
+            const int P = kThreads >> lQn;
             const int per = (ns + P - 1) / P;
+            const int qi0 = tid & (Qn - 1), p = tid >> lQn;
             const int m_lo = min(p * per, ns), m_hi = min(m_lo + per, ns);
-            for (int eg = 0; eg < ecount; eg += epad) {
-                const int el = eg + el0;
-                const bool mine = el < ecount;
-                const int elc = mine ? el : 0;
-                const int e = e_first + elc;
-                const int ir = (e >> 6) - i0;
-                float A = 1.f, Bv = 0.f;
-                for (int m = m_lo; m < m_hi; ++m) {
-                    const float d = dbuf[m * nrows + ir];
-                    A *= d;
-                    Bv = d * Bv + __uint_as_float((unsigned int)ubuf[m * ecount + elc]);
+            float* compA = reinterpret_cast<float*>(scr + kScanD + 2048);   // [256]
+            f4* compB = reinterpret_cast<f4*>(scr + kScanD + 3072);        // [256]
+            for (int g0 = 0; g0 < (1 << lQ); g0 += Qn) {
+                const int el = 4 * (g0 + qi0);
+                const float* drow = dbuf + (el >> 6);
+                const unsigned int* ucol = ubuf + el;
+                // spans in blocks of 4, every LDS read of a block issued first
+                float A = 1.f;
+                f4 Bv = {0.f, 0.f, 0.f, 0.f};
+                for (int m0 = m_lo; m0 < m_hi; m0 += 4) {
+                    u4 xb[4];
+                    float db[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int m = min(m0 + k, m_hi - 1);
+                        xb[k] = *reinterpret_cast<const u4*>(ucol + (m << lo));
+                        db[k] = drow[m << lrows];
+                    }
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float d = m0 + k < m_hi ? db[k] : 1.f;
+                        const float z = m0 + k < m_hi ? 1.f : 0.f;
+                        A *= d;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Bv[e] = d * Bv[e] + z * ll_value(xb[k][e]);
+                    }
                 }
                 compA[tid] = A;
                 compB[tid] = Bv;
                 lds_barrier();
-                float run = 0.f;
-                for (int pp = 0; pp < p; ++pp)
-                    run = compA[pp * epad + el0] * run + compB[pp * epad + el0];
-                if (mine) {
-                    for (int m = m_lo; m < m_hi; ++m) {
-                        ll_store(sin0 + (long long)m * (kD * kD) + e, run, tag);
-                        run = dbuf[m * nrows + ir] * run +
-                              __uint_as_float((unsigned int)ubuf[m * ecount + elc]);
-                    }
-                    if (p == P - 1 && a.final_state)
-                        a.final_state[(long long)seq * kD * kD + e] = run;
+                f4 run = {0.f, 0.f, 0.f, 0.f};
+                for (int pp = 0; pp < p; ++pp) {
+                    const float ca = compA[pp * Qn + qi0];
+                    const f4 cb = compB[pp * Qn + qi0];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) run[e] = ca * run[e] + cb[e];
                 }
-                lds_barrier();   // comp reusable
+                for (int m0 = m_lo; m0 < m_hi; m0 += 4) {
+                    u4 xb[4];
+                    float db[4];
+                    unsigned int tb[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int m = min(m0 + k, m_hi - 1);
+                        xb[k] = *reinterpret_cast<const u4*>(ucol + (m << lo));
+                        db[k] = drow[m << lrows];
+                        tb[k] = sm.tags[m];
+                    }
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        if (m0 + k < m_hi) {
+                            u4 y;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                y[e] = ll_word(run[e], tb[k]);
+                                run[e] = db[k] * run[e] + ll_value(xb[k][e]);
+                            }
+                            *reinterpret_cast<u4*>(ubuf + el + ((m0 + k) << lo)) = y;
+                        }
+                    }
+                }
+                if (p == P - 1) *reinterpret_cast<f4*>(fin + el) = run;
+                lds_barrier();   // comp reusable; rows complete
             }
         }
-        lds_barrier();   // scratch free again
+        // storer waves: rows 0..ns-1 to the incoming-state slots, fin to
+        // final_state (a null final_state gives an empty resource: dropped)
+        if (w >= 2) {
+            const __amdgpu_buffer_rsrc_t rs = rsrc(a.sin + seq_slot * (kD * kD), ns * (kD * kD * 4));
+            const __amdgpu_buffer_rsrc_t rf =
+                rsrc(a.final_state + (a.final_state ? (long long)seq * kD * kD : 0),
+                     a.final_state ? kD * kD * 4 : 0);
+            const int n16 = (ns + 1) << lq;            // <= 2048
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int q = tid - 128 + 128 * k;
+                const int m = q >> lq, off = e_first + 4 * (q & ((1 << lq) - 1));
+                const u4 x = *reinterpret_cast<const u4*>(
+                    m < ns ? ubuf + 4 * (q & 2047) : fin + 4 * (q & ((1 << lq) - 1)));
+                const int oob = 0x7FFFFFF0;
+                st_dev4(rs, (q < n16 && m < ns) ? 4 * (m * (kD * kD) + off) : oob, x);
+                __builtin_amdgcn_raw_buffer_store_b128(x, rf, (q < n16 && m == ns) ? 4 * off : oob, 0, 0);
+            }
+        }
     }
+    lds_barrier();   // scratch free again
 
-    // my incoming state S_in (C layout), by DMA into the scratch
+    // my incoming state S_in (C layout), by DMA into the scratch; span 0 reads
+    // zeros like the others so that its epoch, too, advances only once every
+    // owner has read it
     f4 Sin[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n) Sin[n] = f4{0.f, 0.f, 0.f, 0.f};
-    if (j > 0) {
-        const u64* src = a.sin + (seq_slot + j) * (kD * kD);
-        u64* sbuf = reinterpret_cast<u64*>(scr);
+    {
+        const unsigned int tag = sm.tags[j];
+        const unsigned int* src = a.sin + (seq_slot + j) * (kD * kD);
+        unsigned int* sbuf = reinterpret_cast<unsigned int*>(scr);
         for (unsigned int polls = 0;; ++polls) {
+            if (w < 2) {   // loader waves
 #pragma unroll
-            for (int k0 = 0; k0 < kD * kD / 2; k0 += kThreads)
-                __builtin_amdgcn_global_load_lds(src + 2 * (k0 + 64 * w + lane), sbuf + 2 * (k0 + 64 * w),
-                                                 16, 0, kDevScope);
-            __builtin_amdgcn_s_waitcnt(0x0F70);
+                for (int k0 = 0; k0 < kD * kD / 4; k0 += 128)
+                    __builtin_amdgcn_global_load_lds(src + 4 * (k0 + 64 * w + lane),
+                                                     sbuf + 4 * (k0 + 64 * w), 16, 0, kDevScope);
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+            }
             if (tid == 0) sm.stale = 0;
             lds_barrier();
             bool ok = true;
@@ -734,9 +917,9 @@ gla_fused_kernel(FusedArgs a)
             for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const u64 x = sbuf[(16 * w + 4 * g + e) * kD + 16 * jt + r];
-                    ok &= (unsigned int)(x >> 32) == tag;
-                    Sin[jt][e] = __uint_as_float((unsigned int)x);
+                    const unsigned int x = sbuf[(16 * w + 4 * g + e) * kD + 16 * jt + r];
+                    ok &= ll_ok(x, tag);
+                    Sin[jt][e] = ll_value(x);
                 }
             if (!__all(ok) && lane == 0) sm.stale = 1;
             lds_barrier();
@@ -749,12 +932,10 @@ gla_fused_kernel(FusedArgs a)
             lds_barrier();   // every thread has read the flag before it is reset
             __builtin_amdgcn_s_sleep(2);
         }
+        // Every owner has read this slot's epoch (it wrote S_in after reading
+        // the epochs), and so has this workgroup: advance it.
+        if (tid == 0) __hip_atomic_store(a.epoch + seq_slot + j, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // Every slice owner has read every span's summary before the last span's
-    // S_in is complete, so every workgroup of the sequence has read this
-    // launch's tag by then: advance it for the next launch.
-    if (j == a.n_spans - 1 && tid == 0)
-        __hip_atomic_store(a.epoch + local_seq, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // ---- 3. outputs -----------------------------------------------------------
     if (KEEP) {
@@ -797,7 +978,7 @@ gla_fused_kernel(FusedArgs a)
         load_chunk<true>(a, b, h, c_first * kC, w, lane, cur);
         int st = 0;
         for (int c = 0; c < n_c; ++c) {
-            if (c + 1 < n_c) load_chunk<true>(a, b, h, (c_first + c + 1) * kC, w, lane, nxt);
+            load_chunk<true>(a, b, h, c + 1 < n_c ? (c_first + c + 1) * kC : a.L, w, lane, nxt);
             f4 Oc[4];
             h8 qt[2];
 #pragma unroll
@@ -807,15 +988,40 @@ gla_fused_kernel(FusedArgs a)
             chunk_back(sm, cur, w, lane, st, (j > 0) || (c > 0), Oc, qt, T);
             store_out(sm, a, b, h, (c_first + c) * kC, w, lane, Oc);
             st ^= 1;
-            if (c + 1 < n_c) cur = nxt;
+            cur = nxt;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
+// Zero fill, used instead of hipMemsetAsync so that it can sit in a captured graph.
+__global__ void fill_zero_kernel(unsigned char* p, size_t n)
+{
+    const size_t n16 = n / 16;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+         i += (size_t)gridDim.x * blockDim.x)
+        reinterpret_cast<u4*>(p)[i] = u4{0u, 0u, 0u, 0u};
+    if (blockIdx.x == 0 && threadIdx.x < n - 16 * n16) p[16 * n16 + threadIdx.x] = 0;
+}
+
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t st)
+{
+    if (bytes == 0) return hipSuccess;
+    if (((uintptr_t)p & 15) != 0) return hipErrorInvalidValue;
+    const size_t n16 = bytes / 16;
+    int blocks = (int)((n16 + 255) / 256);
+    if (blocks < 1) blocks = 1;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, st, (unsigned char*)p, bytes);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 bool fused_supported(const Shape& s)
 {
-    return s.d_k == kD && s.d_v == kD && s.chunk == kC;
+    // buffer offsets within one batch are 32-bit
+    return s.d_k == kD && s.d_v == kD && s.chunk == kC &&
+           (long long)s.L * s.H * kD * 2 + 256 <= 0x7FFFFFFFLL;
 }
 
 static int device_cus()
@@ -879,7 +1085,10 @@ FusedPlan fused_plan(const Shape& s, int span_override)
         if (per < 1) per = 1;
         p.seq_batch = (int)(per < n_seq ? per : n_seq);
         p.grid = p.seq_batch * p.n_spans;
-        p.slice = 16 * ((256 + p.n_spans - 1) / p.n_spans);
+        // owners: the largest power of two <= n_spans; each scans 4096 / owners elements
+        int lg = 0;
+        while ((2 << lg) <= p.n_spans) ++lg;
+        p.slice_log2 = 12 - lg;
     };
     auto one_seq_fits = [&]() {
         return (long long)p.n_spans <= (long long)resident_per_cu(p.span, p.keep) * device_cus();
@@ -905,12 +1114,14 @@ FusedPlan fused_plan(const Shape& s, int span_override)
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Workspace: error word, then per exchange slot (sequence in launch, span): an
+// epoch, the published summary and the incoming state.
 size_t fused_workspace_bytes(const Shape& s, const FusedPlan& p)
 {
     (void)s;
-    const size_t nb = (size_t)p.seq_batch;
-    return 256 + align256(nb * sizeof(unsigned int)) +
-           nb * p.n_spans * (size_t)(kAggWords + kD * kD) * sizeof(u64);
+    const size_t slots = (size_t)p.seq_batch * p.n_spans;
+    return 256 + align256(slots * sizeof(unsigned int)) +
+           ((size_t)p.seq_batch * agg_seq_words(p.n_spans) + slots * kD * kD) * sizeof(unsigned int);
 }
 
 hipError_t launch_fused(const void* q, const void* k, const void* v, const void* lg,
@@ -925,11 +1136,11 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
     a.out = (__half*)out;
     a.final_state = final_state;
     unsigned char* base = (unsigned char*)ws;
-    const size_t nb = (size_t)p.seq_batch;
+    const size_t slots = (size_t)p.seq_batch * p.n_spans;
     a.err = (unsigned int*)base;
     a.epoch = (unsigned int*)(base + 256);
-    a.agg = (u64*)(base + 256 + align256(nb * sizeof(unsigned int)));
-    a.sin = a.agg + nb * p.n_spans * kAggWords;
+    a.agg = (unsigned int*)(base + 256 + align256(slots * sizeof(unsigned int)));
+    a.sin = a.agg + (size_t)p.seq_batch * agg_seq_words(p.n_spans);
     a.L = s.L;
     a.H = s.H;
     a.grid_h = s.grid_h;
@@ -938,7 +1149,7 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
     a.n_chunks = s.n_chunks;
     a.span = p.span;
     a.n_spans = p.n_spans;
-    a.slice = p.slice;
+    a.slice_log2 = p.slice_log2;
     a.scale = s.scale;
     const void* fn = pick_kernel(p.span, p.keep);
     resident_per_cu(p.span, p.keep);   // also raises the kernel's dynamic LDS limit

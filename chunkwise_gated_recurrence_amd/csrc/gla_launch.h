@@ -21,7 +21,7 @@ struct FusedPlan {
     int n_spans;     // spans (workgroups) per (batch, head) sequence
     int seq_batch;   // sequences per launch (every workgroup of a launch is resident)
     int grid;        // workgroups per launch
-    int slice;       // state elements each workgroup scans
+    int slice_log2;  // log2 of the state elements each owning workgroup scans
 };
 bool fused_supported(const Shape& s);
 FusedPlan fused_plan(const Shape& s, int span_override);
@@ -29,5 +29,8 @@ size_t fused_workspace_bytes(const Shape& s, const FusedPlan& p);
 hipError_t launch_fused(const void* q, const void* k, const void* v, const void* lg,
                         const Shape& s, const FusedPlan& p, void* out, float* final_state,
                         void* ws, hipStream_t st);
+
+// Zero fill by a kernel (graph-capturable); p must be 16-byte aligned.
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
 
 }  // namespace gtrgla

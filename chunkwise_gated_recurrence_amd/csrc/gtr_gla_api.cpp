@@ -121,20 +121,59 @@ Choice choose(const Shape& s, bool is_fp32, int policy)
     return c;
 }
 
-// Library-owned workspaces for the non-_ws entry points, one per (device, stream).
+// What each workspace last held, by address. The fused kernel's tagged
+// exchange words are valid only in a region that was zeroed once and since
+// then used by fused launches of one layout (spans per sequence, sequences per
+// launch): the layout decides which epoch guards which word. Any other use
+// (the generic kernels, or a fused plan of another layout) invalidates it, and
+// the next fused call zeroes the region first.
+struct WsLayout {
+    int kind;        // 0 clean (zeroed), kGeneric, kFused
+    int n_spans;
+    int seq_batch;
+    bool operator==(const WsLayout& o) const
+    {
+        return kind == o.kind && n_spans == o.n_spans && seq_batch == o.seq_batch;
+    }
+    bool operator<(const WsLayout& o) const
+    {
+        if (kind != o.kind) return kind < o.kind;
+        if (n_spans != o.n_spans) return n_spans < o.n_spans;
+        return seq_batch < o.seq_batch;
+    }
+};
+const WsLayout kWsClean = {0, 0, 0};
+std::mutex g_state_mu;
+std::map<uintptr_t, WsLayout> g_ws_state;
+
+void mark_workspace(const void* ws, const WsLayout& l)
+{
+    std::lock_guard<std::mutex> lk(g_state_mu);
+    g_ws_state[(uintptr_t)ws] = l;
+}
+
+bool workspace_ready_for(const void* ws, const WsLayout& l)
+{
+    std::lock_guard<std::mutex> lk(g_state_mu);
+    auto it = g_ws_state.find((uintptr_t)ws);
+    return it != g_ws_state.end() && (it->second == kWsClean || it->second == l);
+}
+
+// Library-owned workspaces for the non-_ws entry points, one per (device,
+// stream, layout): calls that alternate between shapes keep their own.
 struct CachedWs {
     void* ptr = nullptr;
     size_t bytes = 0;
 };
 std::mutex g_ws_mu;
-std::map<std::pair<int, uintptr_t>, CachedWs> g_ws;
+std::map<std::pair<std::pair<int, uintptr_t>, WsLayout>, CachedWs> g_ws;
 
-int cached_workspace(size_t need, hipStream_t st, void** out)
+int cached_workspace(size_t need, hipStream_t st, const WsLayout& layout, void** out)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return GTR_GLA_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_ws_mu);
-    CachedWs& c = g_ws[std::make_pair(dev, (uintptr_t)st)];
+    CachedWs& c = g_ws[std::make_pair(std::make_pair(dev, (uintptr_t)st), layout)];
     if (c.bytes < need) {
         if (c.ptr) {
             // the previous workspace may still be in use by work on this stream
@@ -148,8 +187,9 @@ int cached_workspace(size_t need, hipStream_t st, void** out)
             c.ptr = nullptr;
             return GTR_GLA_ERR_HIP;
         }
-        if (hipMemsetAsync(c.ptr, 0, bytes, st) != hipSuccess) return GTR_GLA_ERR_HIP;
+        if (gtrgla::fill_zero(c.ptr, bytes, st) != hipSuccess) return GTR_GLA_ERR_HIP;
         c.bytes = bytes;
+        mark_workspace(c.ptr, kWsClean);
     }
     *out = c.ptr;
     return GTR_GLA_OK;
@@ -165,17 +205,22 @@ int run(const void* q, const void* k, const void* v, const void* lg, int B, int 
     r = validate_pointers(q, k, v, lg, out, fs, s, is_fp32 ? 4 : 2);
     if (r != GTR_GLA_OK) return r;
     const Choice c = choose(s, is_fp32, current_policy());
+    const WsLayout layout = c.kernel == kFused ? WsLayout{kFused, c.plan.n_spans, c.plan.seq_batch}
+                                               : WsLayout{kGeneric, 0, 0};
     if (own_ws) {
-        r = cached_workspace(c.ws_bytes, st, &ws);
+        r = cached_workspace(c.ws_bytes, st, layout, &ws);
         if (r != GTR_GLA_OK) return r;
     } else if (!ws || ws_bytes < c.ws_bytes) {
         return GTR_GLA_ERR_WORKSPACE;
     }
-    hipError_t e;
-    if (c.kernel == kFused)
-        e = gtrgla::launch_fused(q, k, v, lg, s, c.plan, out, fs, ws, st);
-    else
+    hipError_t e = hipSuccess;
+    if (c.kernel == kFused) {
+        if (!workspace_ready_for(ws, layout)) e = gtrgla::fill_zero(ws, c.ws_bytes, st);
+        if (e == hipSuccess) e = gtrgla::launch_fused(q, k, v, lg, s, c.plan, out, fs, ws, st);
+    } else {
         e = gtrgla::launch_generic(q, k, v, lg, is_fp32, s, out, fs, ws, st);
+    }
+    mark_workspace(ws, layout);
     return e == hipSuccess ? GTR_GLA_OK : GTR_GLA_ERR_HIP;
 }
 
@@ -211,8 +256,9 @@ int gtr_gla_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t 
 {
     if (!workspace) return GTR_GLA_ERR_NULL;
     if (workspace_bytes == 0) return GTR_GLA_ERR_WORKSPACE;
-    return hipMemsetAsync(workspace, 0, workspace_bytes, stream) == hipSuccess ? GTR_GLA_OK
-                                                                               : GTR_GLA_ERR_HIP;
+    if (gtrgla::fill_zero(workspace, workspace_bytes, stream) != hipSuccess) return GTR_GLA_ERR_HIP;
+    mark_workspace(workspace, kWsClean);
+    return GTR_GLA_OK;
 }
 
 int gtr_gla_fwd_ws(const void* q, const void* k, const void* v, const void* log_gamma, int B,
