@@ -7,14 +7,17 @@ A step is one pass of the hot path over one batch: the four scan-order calls
 blocks make, each on its own input tensors. Inputs are synthetic
 (gla_synth, seeded) and already resident in HBM when timing starts. They are
 rotated over at least 512 MiB of distinct buffers so that the 256 MB Infinity
-Cache cannot serve them from a previous call.
+Cache cannot serve them from a previous call. Steps are captured into HIP
+graphs and replayed (--no-graph: direct calls).
 
 Prints ONE JSON line. `value` is tokens/s over the timed steps: calls x B x L
-tokens divided by the wall time between two events on the stream the kernels
-run on. `roofline` covers the dominant kernel: algorithmic bytes per launch
-(inputs read once, outputs written once) divided by the mean launch duration
-from per-call HIP events, against the 8 TB/s HBM peak. `cpu_baseline` times
-the fp64 oracle on this host for a bounded sample of the same workload.
+tokens divided by the time between two HIP events on the stream the graphs
+(and so the kernels) run on. `roofline` covers the fused kernel (one launch
+per call): algorithmic bytes per launch (inputs read once, outputs and final
+state written once) divided by the mean launch duration, i.e. the same event
+interval divided by the number of launches, against the 8 TB/s HBM peak.
+`cpu_baseline` times the fp64 oracle on this host for a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -33,7 +36,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 512 << 20     # 2x the Infinity Cache
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 DIRS = (0, 1, 2, 3)
 
 
@@ -60,20 +63,30 @@ def kernel_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None if
-    they were taken on a different kernel source."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic_<workload>.txt, lines "key: value"), or None when it was
+    taken on a different kernel source."""
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{workload}.txt")
     try:
-        with open(TRAFFIC_FILE) as fh:
-            t = json.load(fh)
-    except (OSError, ValueError):
+        with open(path) as fh:
+            kv = dict(l.split(":", 1) for l in fh if ":" in l and not l.startswith("#"))
+    except OSError:
         return None
-    e = t.get(workload)
-    if not e or e.get("kernel_hash") != kernel_hash():
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_hash") != kernel_hash():
         return None
-    return e.get("bytes_per_launch")
+    try:
+        return float(kv["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
-def run_workload(w, steps: int, warmup: int, rotate: bool):
+def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = True):
+    """Time `steps` steps of the workload. A step is four calls (the four scan
+    orders), each on its own input set; the sets rotate over >= 512 MiB. The
+    steps are captured into HIP graphs (one graph per four sets) and replayed,
+    so the timed region holds the kernels back to back, as the pages measure
+    their operator (under CUDA Graph); --no-graph times direct calls."""
     import numpy as np
     import torch
 
@@ -82,7 +95,10 @@ def run_workload(w, steps: int, warmup: int, rotate: bool):
 
     arrays = gla_synth.generate(w)
     per_call = alg_bytes(w)
-    nsets = max(len(DIRS), math.ceil(ROTATE_BYTES / per_call)) if rotate else len(DIRS)
+    nsets = len(DIRS)
+    if rotate:
+        nsets = max(nsets, math.ceil(ROTATE_BYTES / per_call))
+        nsets = (nsets + len(DIRS) - 1) // len(DIRS) * len(DIRS)
     dev = torch.device("cuda:0")
     base = [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in arrays]
     sets = []
@@ -91,52 +107,62 @@ def run_workload(w, steps: int, warmup: int, rotate: bool):
         out = torch.empty((w.B, w.L, w.H, w.d_v), dtype=base[0].dtype, device=dev)
         fs = torch.empty((w.B, w.H, w.d_k, w.d_v), dtype=torch.float32, device=dev)
         sets.append((ins, out, fs))
-    fn = gla.gtr_gla_fwd if w.dtype == "fp16" else gla.gtr_gla_fwd_f32
-    stream = torch.cuda.current_stream()
+    is_fp32 = w.dtype == "fp32"
+    ws_bytes = gla.gtr_gla_workspace_bytes(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, w.chunk,
+                                           int(is_fp32))
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    gla.gtr_gla_workspace_init(ws, ws.numel())
+    fn = gla.gtr_gla_fwd_f32_ws if is_fp32 else gla.gtr_gla_fwd_ws
 
     def call(i, d):
         (q, k, v, lg), out, fs = sets[i % nsets]
-        fn(q, k, v, lg, w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, d, w.chunk, out, fs, stream)
+        fn(q, k, v, lg, w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, d, w.chunk, out, fs, ws,
+           ws.numel())
 
-    n = 0
-    for _ in range(warmup):
-        for d in DIRS:
-            call(n, d)
-            n += 1
+    n_groups = nsets // len(DIRS)
+    for d in DIRS:   # eager calls first: plan caches, kernel attributes
+        call(d, d)
     torch.cuda.synchronize()
+    if use_graph:
+        graphs = []
+        for g in range(n_groups):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for d in DIRS:
+                    call(len(DIRS) * g + d, d)
+            graphs.append(graph)
+        torch.cuda.synchronize()
 
-    ncalls = steps * len(DIRS)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(ncalls)]
+        def step(n):
+            graphs[n % n_groups].replay()
+    else:
+        def step(n):
+            for d in DIRS:
+                call(len(DIRS) * (n % n_groups) + d, d)
+
+    for n in range(warmup):
+        step(n)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record(stream)
-    c = 0
-    for _ in range(steps):
-        for d in DIRS:
-            ev[c][0].record(stream)
-            call(n, d)
-            ev[c][1].record(stream)
-            n += 1
-            c += 1
+    for n in range(steps):
+        step(warmup + n)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    call_ms = sorted(a.elapsed_time(b) for a, b in ev)
-    mean_call_us = 1e3 * sum(call_ms) / len(call_ms)
+    ncalls = steps * len(DIRS)
     kern, span, grid = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, w.chunk,
-                                        int(w.dtype == "fp32"))
+                                        int(is_fp32))
     return {
         "total_ms": total_ms,
         "ms_per_step": total_ms / steps,
         "tokens_per_s": ncalls * w.B * w.L / (total_ms * 1e-3),
-        "call_us_mean": mean_call_us,
-        "call_us_median": 1e3 * call_ms[len(call_ms) // 2],
-        "call_us_p10": 1e3 * call_ms[len(call_ms) // 10],
-        "call_us_p90": 1e3 * call_ms[(9 * len(call_ms)) // 10],
+        "call_us_mean": 1e3 * total_ms / ncalls,
         "alg_bytes_per_call": per_call,
         "rotating_sets": nsets,
+        "graph": use_graph,
         "kernel": {1: "generic", 2: "fused"}.get(kern, str(kern)),
         "span": span,
         "grid": grid,
@@ -173,20 +199,23 @@ def cpu_baseline(w, budget_s: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="img640")
-    ap.add_argument("--secondary", default="img1024,long2048",
+    ap.add_argument("--secondary", default="img1024,long2048,batched640",
                     help="comma-separated extra workloads reported beside the main one")
     ap.add_argument("--warm", action="store_true", help="reuse one input set (cache-warm)")
+    ap.add_argument("--no-graph", action="store_true", help="time direct calls, not graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of COPY_BYTES (for counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the B*H sequences "
-              "shard across GPUs with no communication, so run one process per GPU.",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this build runs on "
+              "one GPU; the B*H sequences shard across GPUs with no communication, so N GPUs run "
+              "N independent copies of this measurement.", file=sys.stderr)
         return 2
 
     import torch
@@ -197,30 +226,34 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.copy_calibration:
+        return copy_calibration()
     if not os.path.exists(gla.LIB_PATH):
         from chunkwise_gated_recurrence_amd import build as _b
         _b.build()
     gla.load_library()
 
     w = gla_synth.WORKLOADS[args.workload]
-    r = run_workload(w, args.steps, args.warmup, rotate=not args.warm)
+    graph = not args.no_graph
+    r = run_workload(w, args.steps, args.warmup, rotate=not args.warm, use_graph=graph)
     achieved = r["alg_bytes_per_call"] / (r["call_us_mean"] * 1e-6) / 1e9
     traffic = measured_traffic(w.name)
     secondary = []
     for name in [s for s in args.secondary.split(",") if s and s != w.name]:
         ws = gla_synth.WORKLOADS[name]
-        rs = run_workload(ws, max(10, args.steps // 2), args.warmup, rotate=not args.warm)
+        rs = run_workload(ws, max(20, args.steps // 4), args.warmup, rotate=not args.warm,
+                          use_graph=graph)
         gbs = rs["alg_bytes_per_call"] / (rs["call_us_mean"] * 1e-6) / 1e9
         secondary.append({
             "workload": name, "tokens_per_s": rs["tokens_per_s"], "ms_per_step": rs["ms_per_step"],
-            "call_us_mean": rs["call_us_mean"], "call_us_median": rs["call_us_median"],
-            "achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "call_us_mean": rs["call_us_mean"], "achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "mfma_frac": mfma_flops(ws) / (rs["call_us_mean"] * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
             "kernel": rs["kernel"], "span": rs["span"], "grid": rs["grid"],
+            "traffic": measured_traffic(name),
         })
 
     line = {
-        "metric": "key-only GLA fwd tokens/s",
+        "metric": "key-only GLA fwd tokens/s at 1.6K & 16.4K tokens; % of HBM/MFMA roofline",
         "value": r["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -231,12 +264,13 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16" if w.dtype == "fp16" else "f32",
-        "data": "synthetic (seeded gla_synth inputs, rotated over >=512 MiB of HBM buffers)"
-                if not args.warm else "synthetic (seeded gla_synth inputs, one warm set)",
+        "data": ("synthetic (seeded gla_synth inputs, rotated over >=512 MiB of HBM buffers)"
+                 if not args.warm else "synthetic (seeded gla_synth inputs, one warm set)"),
         "config": {
             "workload": w.name, "B": w.B, "grid": f"{w.grid_h}x{w.grid_w}", "L": w.L, "H": w.H,
             "d_k": w.d_k, "d_v": w.d_v, "chunk": w.chunk, "calls_per_step": len(DIRS),
             "input_dtype": w.dtype, "kernel": r["kernel"], "span": r["span"], "grid_wg": r["grid"],
+            "timing": "HIP graph replay" if graph else "direct calls",
             "parallelism": "single GPU",
         },
         "roofline": {
@@ -249,7 +283,6 @@ def main() -> int:
             "kernel": "gla_fused_kernel" if r["kernel"] == "fused" else "generic (3 kernels)",
             "alg_bytes_per_launch": r["alg_bytes_per_call"],
             "launch_us_mean": r["call_us_mean"],
-            "launch_us_median": r["call_us_median"],
             "mfma_frac": mfma_flops(w) / (r["call_us_mean"] * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
         },
         "secondary": secondary,
@@ -258,6 +291,24 @@ def main() -> int:
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+    return 0
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration() -> int:
+    """A plain device-to-device copy of COPY_BYTES (read once, written once),
+    run a few times: the FETCH_SIZE / WRITE_SIZE counters of this run, divided
+    by COPY_BYTES, give the factor that turns counter readings into bytes."""
+    import torch
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "repeats": 3}), flush=True)
     return 0
 
 
