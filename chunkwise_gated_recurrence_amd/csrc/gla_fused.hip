@@ -71,7 +71,7 @@ typedef unsigned long long u64;
 constexpr int kC = 64;            // chunk length
 constexpr int kD = 64;            // d_k = d_v
 constexpr int kThreads = 256;     // 4 waves
-constexpr int kMaxKeep = 2;       // longest span kept on chip
+constexpr int kMaxKeep = 8;       // longest span kept on chip
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kGuard = 16.0f;   // max log2 range of a chunk for factorised scores
 constexpr int kTile = kC * 72;    // halves per LDS tile (rows padded to 72)
@@ -202,6 +202,7 @@ struct FusedArgs {
     unsigned int* err;          // set when a wait gives up
     unsigned int* agg;          // [seq in launch][agg_seq_words(n_spans)]  tagged, owner-major
     unsigned int* sin;          // [seq in launch][n_spans][kD * kD]   tagged
+    u4* park;                   // [workgroup][span - 1][256 threads][4]: parked outputs (long kept spans)
     int L, H, grid_h, grid_w, dir;
     int n_chunks;               // per sequence
     int span;                   // chunks per workgroup
@@ -225,6 +226,7 @@ struct Smem {
     float ref[kD];            // reference point r
     _Float16 cq16[kD];        // 2^r
     _Float16 ck16[kD];        // 2^{b_last - r}
+    _Float16 cp16[kD];        // 2^{P_c}: decay from the span start to the chunk start
     float dcv[kD];            // 2^{b_last} = d_c
     float blast[kD];          // b_last (log2 of d_c)
     float P[kMaxKeep + 1][kD];  // log2 decay from the span start to each chunk start
@@ -232,10 +234,8 @@ struct Smem {
     unsigned int tags[kMaxSpans];   // expected tag of every span slot of the sequence
     int fail;
     int stale;
-    _Float16 ST1[kTile];      // second state buffer, last: one-chunk spans never use it
 };
 
-__device__ __forceinline__ _Float16* st_tile(Smem& sm, int i) { return i ? sm.ST1 : sm.ST0; }
 
 struct ChunkRegs {
     u4 q[2], k[2], v[2], g[2];
@@ -252,7 +252,7 @@ __device__ __forceinline__ long long row_offset(const FusedArgs& a, int b, int h
 // Buffer resource over batch b of a [B, L, H, 64] fp16 tensor. Buffer loads
 // past num_records return zeros, so rows beyond the sequence end read as zero
 // without a branch (a branch around a load makes the compiler wait for it).
-constexpr int kNT = 2;   // cache policy: streaming (nontemporal) access
+constexpr int kNT = 0;   // cache policy of the chunk loads: default (a streaming hint measured slower)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t batch_rsrc(const __half* base, const FusedArgs& a,
                                                              int b)
@@ -289,24 +289,29 @@ __device__ __forceinline__ void load_chunk(const FusedArgs& a, int b, int h, int
 }
 
 // Exact fp32 scores of the wave's rows t = 16w + r for a chunk whose gate
-// range is too wide for the factorised form. The fp32 prefix of every row goes
-// to the Kh+Sc table and raw k to KtT (the state update has consumed it); each
-// lane sums its own 16 dims and four lanes (one per dim group) combine.
-__device__ void exact_scores(Smem& sm, const ChunkRegs& R, const float (&x)[2][8], int w,
-                             int lane, f4 (&sc)[4])
+// range is too wide for the factorised form. chunk_front has put the fp32
+// prefix of every row in the Kh+Sc table; raw k goes to KtT (the state update
+// has consumed it); each lane sums its own 16 dims and four lanes (one per dim
+// group) combine.
+__device__ void exact_scores(Smem& sm, const FusedArgs& a, int b, int h, int t0, int w, int lane,
+                             f4 (&sc)[4])
 {
     const int r = lane & 15, g = lane >> 4;
     const int t = 16 * w + r;
     float* Bt = reinterpret_cast<float*>(sm.Kh);       // [64][64] fp32, overlays Kh and Sc
     _Float16* Kr = sm.KtT;                             // [64][64] raw k, row-major
+    // raw q and k of the chunk again (rare path; the chunk registers hold the
+    // next chunk by now)
+    ChunkRegs R;
+    load_chunk<true>(a, b, h, t0, w, lane, R);
     lds_barrier();
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Bt[t * kD + 32 * hh + 8 * g + e] = x[hh][e];
+    for (int hh = 0; hh < 2; ++hh)
         *reinterpret_cast<u4*>(Kr + t * kD + 32 * hh + 8 * g) = R.k[hh];
-    }
     lds_barrier();
+    float x[2][8];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) ld_f8(Bt + t * kD + 32 * hh + 8 * g, x[hh]);
     float qf[2][8];
     unpack8(R.q[0], qf[0]);
     unpack8(R.q[1], qf[1]);
@@ -349,8 +354,7 @@ __device__ void exact_scores(Smem& sm, const ChunkRegs& R, const float (&x)[2][8
 // What the output half of a chunk needs from its front half.
 struct ChunkTmp {
     h8 qh[2];        // q 2^{b-r} (factorised scores)
-    float x[2][8];   // log2 prefix b (exact scores)
-    bool exact;
+    bool exact;      // exact scores: the log2 prefix of every row is in the Kh+Sc table
 };
 
 // Front half of one chunk: log2-gate prefix, per-dim constants, operand tiles,
@@ -360,8 +364,7 @@ struct ChunkTmp {
 // write_next. FULL also prepares the output half (Qt = q 2^b, Kh, qh).
 template <bool FULL>
 __device__ __forceinline__ void chunk_front(Smem& sm, const ChunkRegs& R, int w, int lane, int c,
-                                            f4 (&S)[4], int st, bool write_next, h8 (&Qt)[2],
-                                            ChunkTmp& T)
+                                            f4 (&S)[4], bool stage_state, h8 (&Qt)[2], ChunkTmp& T)
 {
     const int r = lane & 15, g = lane >> 4;
     const int tid = 64 * w + lane;
@@ -394,6 +397,13 @@ __device__ __forceinline__ void chunk_front(Smem& sm, const ChunkRegs& R, int w,
             for (int e = 0; e < 8; ++e) sm.bfirst[32 * hh + 8 * g + e] = x[hh][e];
     }
     lds_barrier();  // (A)
+    // the state entering this chunk, for its outputs (ST0 is free: the
+    // previous chunk's output half has passed barrier A)
+    if (stage_state) {
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+            st4(sm.ST0, 16 * jt + r, 16 * w + 4 * g, pack4(S[jt], 1.f));
+    }
 
     // -- per-dim offsets and constants, one thread per key dim
     if (tid < kD) {
@@ -412,6 +422,7 @@ __device__ __forceinline__ void chunk_front(Smem& sm, const ChunkRegs& R, int w,
         sm.dcv[d] = ex2(bl);
         sm.blast[d] = bl;
         sm.Pend[d] += bl;
+        sm.cp16[d] = (_Float16)ex2(sm.P[c][d]);
         if (c < kMaxKeep) sm.P[c + 1][d] = sm.P[c][d] + bl;
         const bool wide = __any((bf - bl) > kGuard);
         if (d == 0) sm.fail = wide ? 1 : 0;
@@ -448,6 +459,11 @@ __device__ __forceinline__ void chunk_front(Smem& sm, const ChunkRegs& R, int w,
             kt8 = kh * ck;
             st8(sm.Kh, 16 * w + r, d0, kh);
         } else {
+            if (exact) {   // the prefix table of the exact scores (Kh is unused then)
+                float* Bt = reinterpret_cast<float*>(sm.Kh);
+                *reinterpret_cast<f4*>(Bt + (16 * w + r) * kD + d0) = f4{x[hh][0], x[hh][1], x[hh][2], x[hh][3]};
+                *reinterpret_cast<f4*>(Bt + (16 * w + r) * kD + d0 + 4) = f4{x[hh][4], x[hh][5], x[hh][6], x[hh][7]};
+            }
             float bl[8], kf[8], kt[8];
             ld_f8(&sm.blast[d0], bl);
             unpack8(R.k[hh], kf);
@@ -488,24 +504,13 @@ __device__ __forceinline__ void chunk_front(Smem& sm, const ChunkRegs& R, int w,
             S[jt] = mfma(ld8(sm.KtT, 16 * w + r, 32 * ks + 8 * g),
                          ld8(sm.VT, 16 * jt + r, 32 * ks + 8 * g), S[jt]);
     }
-    if (write_next) {
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-            st4(st_tile(sm, st ^ 1), 16 * jt + r, 16 * w + 4 * g, pack4(S[jt], 1.f));
-    }
-    if (FULL) {
-        T.exact = exact;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) T.x[hh][e] = x[hh][e];
-    }
+    if (FULL) T.exact = exact;
 }
 
 // Output half of one chunk: O^T[j][t] += sum_s VT[j][s] Sc[t][s], plus
 // sum_i ST[st][j][i] Qt[t][i] when has_state.
-__device__ __forceinline__ void chunk_back(Smem& sm, const ChunkRegs& R, int w, int lane, int st,
-                                           bool has_state, f4 (&O)[4], const h8 (&Qt)[2],
+__device__ __forceinline__ void chunk_back(Smem& sm, const FusedArgs& a, int b, int h, int t0, int w,
+                                           int lane, bool has_state, f4 (&O)[4], const h8 (&Qt)[2],
                                            const ChunkTmp& T)
 {
     const int r = lane & 15, g = lane >> 4;
@@ -523,7 +528,7 @@ __device__ __forceinline__ void chunk_back(Smem& sm, const ChunkRegs& R, int w, 
             }
         }
     } else {
-        exact_scores(sm, R, T.x, w, lane, sc);
+        exact_scores(sm, a, b, h, t0, w, lane, sc);
     }
     // mask, and write the wave's score rows Sc[t][s] (zeros above the diagonal)
 #pragma unroll
@@ -545,7 +550,7 @@ __device__ __forceinline__ void chunk_back(Smem& sm, const ChunkRegs& R, int w, 
         if (has_state) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                O[jt] = mfma(ld8(st_tile(sm, st), 16 * jt + r, 32 * ks + 8 * g), Qt[ks], O[jt]);
+                O[jt] = mfma(ld8(sm.ST0, 16 * jt + r, 32 * ks + 8 * g), Qt[ks], O[jt]);
         }
     }
 }
@@ -584,9 +589,12 @@ __host__ __device__ inline long long agg_seq_words(int ns) { return (long long)n
 // of the span, as tagged words of slot `slot` (U at i * 64 + j, D at 4096 + i).
 // Also turns the epochs loaded at the start (thread t < n_spans holds the one
 // of span t in ep) into the tag table. Waves 0-1 hand their U rows to the
-// storer waves through ST0 (free here: no kept chunk reads it).
+// storer waves through an LDS tile that the chunk's output half does not read:
+// ST0 when that half takes no incoming state (AFTER_STATE false), else KtT,
+// after a barrier (every wave's state update has read its KtT rows by then).
 constexpr int kU01 = 68;   // fp32 row stride of the handed-over rows (no bank conflicts)
 
+template <bool AFTER_STATE>
 __device__ __forceinline__ void publish_summary(const FusedArgs& a, Smem& sm, const f4 (&S)[4],
                                                 long long slot, int j, unsigned int ep, int w,
                                                 int lane)
@@ -596,7 +604,8 @@ __device__ __forceinline__ void publish_summary(const FusedArgs& a, Smem& sm, co
     // Every chunk load has landed (or reads past the end): retire them all
     // here, so that no later wait on a reused register waits for these stores.
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    float* u01 = reinterpret_cast<float*>(sm.ST0);
+    if (AFTER_STATE) lds_barrier();
+    float* u01 = reinterpret_cast<float*>(AFTER_STATE ? sm.KtT : sm.ST0);
     if (w < 2) {
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
@@ -638,28 +647,111 @@ __device__ __forceinline__ void publish_summary(const FusedArgs& a, Smem& sm, co
     }
 }
 
-// Local pass of a kept span of NC chunks (cur, then nxt): intra-chunk outputs
-// into O, decay-scaled queries into Qt, final local state in S; the summary is
-// published right after the last state update.
-template <int NC, int SPAN>
-__device__ __forceinline__ void keep_pass(const FusedArgs& a, Smem& sm, const ChunkRegs& cur,
-                                          const ChunkRegs& nxt, int w, int lane, f4 (&S)[4],
-                                          f4 (&O)[SPAN][4], h8 (&Qt)[SPAN][2], long long slot,
-                                          int j, unsigned int ep)
-{
+// Intra-chunk outputs kept through the exchange: fp32 for spans of up to two
+// chunks, packed fp16 beyond (the register budget of long spans); the rounding
+// is below the output's own fp16 rounding.
+template <int SPAN>
+struct KeptOut {
+    static constexpr bool kHalf = SPAN > 2;
+    f4 f[kHalf ? 1 : 4];
+    h4 hv[kHalf ? 4 : 1];
+    __device__ __forceinline__ void put(const f4 (&O)[4])
+    {
 #pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            if (kHalf) hv[jt] = pack4(O[jt], 1.f);
+            else f[jt] = O[jt];
+        }
+    }
+    __device__ __forceinline__ void get(f4 (&O)[4]) const
+    {
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            if (kHalf) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) O[jt][e] = (float)hv[jt][e];
+            } else {
+                O[jt] = f[jt];
+            }
+        }
+    }
+};
+
+// Local pass of a one-chunk span: intra-chunk outputs into K and the
+// correction operand Qs = q 2^b for the incoming state; final local state in S;
+// the summary is published right after the state update.
+template <int SPAN>
+__device__ __forceinline__ void keep_pass1(const FusedArgs& a, Smem& sm, const ChunkRegs& R, int b,
+                                           int h, int c_first, int w, int lane, f4 (&S)[4],
+                                           KeptOut<SPAN> (&K)[SPAN], h8 (&Qs)[SPAN][2],
+                                           long long slot, int j, unsigned int ep)
+{
+    const int g = lane >> 4;
+    ChunkTmp T;
+    h8 Qt[2];
+    chunk_front<true>(sm, R, w, lane, 0, S, false, Qt, T);
+    publish_summary<false>(a, sm, S, slot, j, ep, w, lane);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+        Qs[0][hh] = Qt[hh] * *reinterpret_cast<const h8*>(&sm.cp16[32 * hh + 8 * g]);
+    f4 O[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) O[n] = f4{0.f, 0.f, 0.f, 0.f};
+    chunk_back(sm, a, b, h, c_first * kC, w, lane, false, O, Qt, T);
+    K[0].put(O);
+}
+
+// Local pass of a span of NC >= 2 chunks, as a loop (one copy of the chunk
+// code, for the instruction cache). One register set: chunk c + 1 is loaded
+// as soon as chunk c's front half has consumed its registers. The intra-chunk
+// outputs (fp16) and Qs = q 2^{b + P_c} (P_c: log2 decay from the span start
+// to chunk c) of every chunk are parked in this workgroup's slots of the
+// workspace, 64 bytes per thread per chunk; the summary is published right
+// after the last state update.
+__device__ __forceinline__ u4* park_slot(const FusedArgs& a, int c)
+{
+    return a.park + ((size_t)blockIdx.x * kMaxKeep + c) * (kThreads * 4) + 4 * threadIdx.x;
+}
+
+template <int NC>
+__device__ __forceinline__ void keep_pass_loop(const FusedArgs& a, Smem& sm, ChunkRegs& R, int b,
+                                               int h, int c_first, int w, int lane, f4 (&S)[4],
+                                               long long slot, int j, unsigned int ep)
+{
     for (int c = 0; c < NC; ++c) {
-        const ChunkRegs& R = c == 0 ? cur : nxt;
+        // per-lane addresses are recomputed inside the loop instead of being
+        // hoisted and held in registers across it
+        asm volatile("" : "+v"(lane));
+        const int g = lane >> 4;
         ChunkTmp T;
-        chunk_front<true>(sm, R, w, lane, c, S, c & 1, c + 1 < NC, Qt[c], T);
-        if (c + 1 == NC) publish_summary(a, sm, S, slot, j, ep, w, lane);
-        chunk_back(sm, R, w, lane, c & 1, c > 0, O[c], Qt[c], T);
+        h8 Qt[2];
+        chunk_front<true>(sm, R, w, lane, c, S, c > 0, Qt, T);
+        // never under a branch; past the span's end reads zeros
+        load_chunk<true>(a, b, h, c + 1 < NC ? (c_first + c + 1) * kC : a.L, w, lane, R);
+        if (c + 1 == NC) publish_summary<true>(a, sm, S, slot, j, ep, w, lane);
+        h8 qs[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            qs[hh] = Qt[hh] * *reinterpret_cast<const h8*>(&sm.cp16[32 * hh + 8 * g]);
+        f4 O[4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) O[n] = f4{0.f, 0.f, 0.f, 0.f};
+        chunk_back(sm, a, b, h, (c_first + c) * kC, w, lane, c > 0, O, Qt, T);
+        u4* pk = park_slot(a, c);
+        pk[0] = __builtin_bit_cast(u4, h8{(_Float16)O[0][0], (_Float16)O[0][1], (_Float16)O[0][2],
+                                          (_Float16)O[0][3], (_Float16)O[1][0], (_Float16)O[1][1],
+                                          (_Float16)O[1][2], (_Float16)O[1][3]});
+        pk[1] = __builtin_bit_cast(u4, h8{(_Float16)O[2][0], (_Float16)O[2][1], (_Float16)O[2][2],
+                                          (_Float16)O[2][3], (_Float16)O[3][0], (_Float16)O[3][1],
+                                          (_Float16)O[3][2], (_Float16)O[3][3]});
+        pk[2] = __builtin_bit_cast(u4, qs[0]);
+        pk[3] = __builtin_bit_cast(u4, qs[1]);
     }
 }
 
 // ---------------------------------------------------------------------------
 template <int SPAN, bool KEEP>
-__global__ void __launch_bounds__(kThreads, (KEEP && SPAN == 1) ? 3 : 2)
+__global__ void __launch_bounds__(kThreads, 3)
 gla_fused_kernel(FusedArgs a)
 {
     static_assert(!KEEP || SPAN <= kMaxKeep, "a kept span holds at most kMaxKeep chunks");
@@ -681,17 +773,13 @@ gla_fused_kernel(FusedArgs a)
     __builtin_assume(n_c >= 1);   // every span starts inside the sequence
 
     // Epochs of the sequence's span slots (thread t < n_spans reads slot t;
-    // the rest read zeros past the end), then the chunk loads: a kept span
-    // issues the loads of all its chunks up front. The epochs are first used
-    // at the publish, so nothing waits for them before.
+    // the rest read zeros past the end), then the first chunk. The epochs are
+    // first used at the publish, so nothing waits for them before.
     const long long seq_slot = (long long)local_seq * a.n_spans;
     const unsigned int ep = __builtin_amdgcn_raw_buffer_load_b32(
         rsrc(a.epoch + seq_slot, 4 * a.n_spans), 4 * tid, 0, kDevScope);
-    ChunkRegs cur, nxt;
+    ChunkRegs cur;
     load_chunk<KEEP>(a, b, h, c_first * kC, w, lane, cur);
-    // Loads are never under a branch (the compiler would wait for them at the
-    // join); a chunk past the span's end starts at L and reads zeros.
-    if (KEEP && SPAN > 1) load_chunk<true>(a, b, h, n_c > 1 ? (c_first + 1) * kC : a.L, w, lane, nxt);
     if (tid < kD) {
         sm.P[0][tid] = 0.f;
         sm.Pend[tid] = 0.f;
@@ -703,28 +791,30 @@ gla_fused_kernel(FusedArgs a)
     f4 S[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) S[n] = f4{0.f, 0.f, 0.f, 0.f};
-    f4 O[KEEP ? SPAN : 1][4];
-    h8 Qt[KEEP ? SPAN : 1][2];
+    // kept intra-chunk output and correction operand of a one-chunk span
+    KeptOut<1> K[1];
+    h8 Qs[1][2];
     if (KEEP) {
-#pragma unroll
-        for (int c = 0; c < (KEEP ? SPAN : 1); ++c)
-#pragma unroll
-            for (int n = 0; n < 4; ++n) O[c][n] = f4{0.f, 0.f, 0.f, 0.f};
-        // Straight-line code with no branch on the chunk count, so that no
-        // path past the publish stores has a chunk load in flight (a wait for
-        // one would also wait for the stores). A span that ends early runs an
-        // empty chunk: zero rows leave the state and the decay unchanged and
-        // their outputs are never stored.
-        keep_pass<(KEEP ? SPAN : 1)>(a, sm, cur, nxt, w, lane, S, O, Qt, seq_slot + j, j, ep);
+        // No branch on the chunk count: a span that ends early runs empty
+        // chunks (zero rows leave the state and the decay unchanged and their
+        // outputs are never stored), so every workgroup does the same work and
+        // no path past the publish stores has a chunk load in flight (a wait
+        // for one would also wait for the stores).
+        if constexpr (SPAN == 1)
+            keep_pass1<1>(a, sm, cur, b, h, c_first, w, lane, S, K, Qs, seq_slot + j, j, ep);
+        else
+            keep_pass_loop<(KEEP ? SPAN : 1)>(a, sm, cur, b, h, c_first, w, lane, S, seq_slot + j,
+                                              j, ep);
     } else {
         h8 qdummy[2];
         ChunkTmp T;
         for (int c = 0; c < n_c; ++c) {
-            load_chunk<false>(a, b, h, c + 1 < n_c ? (c_first + c + 1) * kC : a.L, w, lane, nxt);
-            chunk_front<false>(sm, cur, w, lane, c, S, 0, false, qdummy, T);
-            cur = nxt;
+            int ln = lane;
+            asm volatile("" : "+v"(ln));   // addresses recomputed per chunk, not held live
+            chunk_front<false>(sm, cur, w, ln, c, S, false, qdummy, T);
+            load_chunk<false>(a, b, h, c + 1 < n_c ? (c_first + c + 1) * kC : a.L, w, lane, cur);
         }
-        publish_summary(a, sm, S, seq_slot + j, j, ep, w, lane);
+        publish_summary<false>(a, sm, S, seq_slot + j, j, ep, w, lane);
     }
 
     // ---- 2. boundary scan across the sequence's spans -------------------------
@@ -945,26 +1035,48 @@ gla_fused_kernel(FusedArgs a)
                 st4(sm.ST0, 16 * jt + r, 16 * w + 4 * g, pack4(Sin[jt], 1.f));
         }
         lds_barrier();
-#pragma unroll
-        for (int c = 0; c < SPAN; ++c) {
-            if (c >= n_c) continue;
+        if constexpr (SPAN == 1) {
+            f4 O[4];
+            K[0].get(O);
             if (j > 0) {
-                // q 2^b scaled by the decay from the span start to this chunk
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    h8 qs = Qt[c][hh];
-                    if (c > 0) {
-                        float p[8];
-                        ld_f8(&sm.P[c][32 * hh + 8 * g], p);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) qs[e] = (_Float16)((float)qs[e] * ex2(p[e]));
-                    }
+                for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                     for (int jt = 0; jt < 4; ++jt)
-                        O[c][jt] = mfma(ld8(sm.ST0, 16 * jt + r, 32 * hh + 8 * g), qs, O[c][jt]);
-                }
+                        O[jt] = mfma(ld8(sm.ST0, 16 * jt + r, 32 * hh + 8 * g), Qs[0][hh], O[jt]);
             }
-            store_out(sm, a, b, h, (c_first + c) * kC, w, lane, O[c]);
+            store_out(sm, a, b, h, c_first * kC, w, lane, O);
+        } else {
+            // parked chunks: the next chunk's slot loads while this one finishes
+            u4 pk[4], pn[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) pk[k] = park_slot(a, 0)[k];
+            for (int c = 0; c < n_c; ++c) {
+                f4 O[4];
+                h8 qs[2];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) pn[k] = park_slot(a, c + 1 < SPAN ? c + 1 : c)[k];
+                const h8 o01 = __builtin_bit_cast(h8, pk[0]), o23 = __builtin_bit_cast(h8, pk[1]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    O[0][e] = (float)o01[e];
+                    O[1][e] = (float)o01[4 + e];
+                    O[2][e] = (float)o23[e];
+                    O[3][e] = (float)o23[4 + e];
+                }
+                qs[0] = __builtin_bit_cast(h8, pk[2]);
+                qs[1] = __builtin_bit_cast(h8, pk[3]);
+                if (j > 0) {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                        for (int jt = 0; jt < 4; ++jt)
+                            O[jt] = mfma(ld8(sm.ST0, 16 * jt + r, 32 * hh + 8 * g), qs[hh], O[jt]);
+                }
+                store_out(sm, a, b, h, (c_first + c) * kC, w, lane, O);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) pk[k] = pn[k];
+            }
         }
     } else {
         // stream the span again from its incoming state
@@ -976,19 +1088,18 @@ gla_fused_kernel(FusedArgs a)
                 st4(sm.ST0, 16 * jt + r, 16 * w + 4 * g, pack4(S[jt], 1.f));
         }
         load_chunk<true>(a, b, h, c_first * kC, w, lane, cur);
-        int st = 0;
         for (int c = 0; c < n_c; ++c) {
-            load_chunk<true>(a, b, h, c + 1 < n_c ? (c_first + c + 1) * kC : a.L, w, lane, nxt);
+            int ln = lane;
+            asm volatile("" : "+v"(ln));   // addresses recomputed per chunk, not held live
             f4 Oc[4];
             h8 qt[2];
 #pragma unroll
             for (int n = 0; n < 4; ++n) Oc[n] = f4{0.f, 0.f, 0.f, 0.f};
             ChunkTmp T;
-            chunk_front<true>(sm, cur, w, lane, kMaxKeep, S, st, c + 1 < n_c, qt, T);
-            chunk_back(sm, cur, w, lane, st, (j > 0) || (c > 0), Oc, qt, T);
-            store_out(sm, a, b, h, (c_first + c) * kC, w, lane, Oc);
-            st ^= 1;
-            cur = nxt;
+            chunk_front<true>(sm, cur, w, ln, kMaxKeep, S, c > 0, qt, T);
+            load_chunk<true>(a, b, h, c + 1 < n_c ? (c_first + c + 1) * kC : a.L, w, ln, cur);
+            chunk_back(sm, a, b, h, (c_first + c) * kC, w, ln, (j > 0) || (c > 0), Oc, qt, T);
+            store_out(sm, a, b, h, (c_first + c) * kC, w, ln, Oc);
         }
     }
 }
@@ -1038,17 +1149,25 @@ static int device_cus()
     return cached;
 }
 
+// Kept spans are instantiated for these lengths.
+static bool keep_span_ok(int span) { return span == 1 || span == 2 || span == 4 || span == 8; }
+
 static const void* pick_kernel(int span, bool keep)
 {
     if (!keep) return (const void*)gla_fused_kernel<1, false>;
-    if (span == 1) return (const void*)gla_fused_kernel<1, true>;
-    return (const void*)gla_fused_kernel<2, true>;
+    switch (span) {
+    case 1: return (const void*)gla_fused_kernel<1, true>;
+    case 2: return (const void*)gla_fused_kernel<2, true>;
+    case 4: return (const void*)gla_fused_kernel<4, true>;
+    default: return (const void*)gla_fused_kernel<8, true>;
+    }
 }
 
-// Dynamic LDS of a variant: one-chunk spans never touch the second state buffer.
 static size_t smem_bytes(int span, bool keep)
 {
-    return (keep && span == 1) ? offsetof(Smem, ST1) : sizeof(Smem);
+    (void)span;
+    (void)keep;
+    return sizeof(Smem);
 }
 
 // Workgroups of one variant that fit on a CU at once.
@@ -1094,12 +1213,12 @@ FusedPlan fused_plan(const Shape& s, int span_override)
         return (long long)p.n_spans <= (long long)resident_per_cu(p.span, p.keep) * device_cus();
     };
     if (span_override > 0) {
-        fill(span_override, span_override <= kMaxKeep);
+        fill(span_override, keep_span_ok(span_override));
         while (!one_seq_fits() || p.n_spans > kMaxSpans) fill(p.span * 2, false);
         return p;
     }
     // the shortest kept span whose whole grid is resident; else streamed spans
-    for (int sp = 1; sp <= kMaxKeep; ++sp) {
+    for (int sp = 1; sp <= kMaxKeep; sp *= 2) {
         fill(sp, true);
         if (p.seq_batch == n_seq && p.n_spans <= kMaxSpans) return p;
     }
@@ -1115,13 +1234,22 @@ FusedPlan fused_plan(const Shape& s, int span_override)
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace: error word, then per exchange slot (sequence in launch, span): an
-// epoch, the published summary and the incoming state.
+// epoch, the published summary and the incoming state; then, for kept spans of
+// two or more chunks (keep_pass_loop), the parking slots (kMaxKeep chunks per
+// workgroup).
+static size_t park_bytes(const FusedPlan& p)
+{
+    return (p.keep && p.span >= 2) ? (size_t)p.grid * kMaxKeep * kThreads * sizeof(u4) * 4 : 0;
+}
+
 size_t fused_workspace_bytes(const Shape& s, const FusedPlan& p)
 {
     (void)s;
     const size_t slots = (size_t)p.seq_batch * p.n_spans;
     return 256 + align256(slots * sizeof(unsigned int)) +
-           ((size_t)p.seq_batch * agg_seq_words(p.n_spans) + slots * kD * kD) * sizeof(unsigned int);
+           align256(((size_t)p.seq_batch * agg_seq_words(p.n_spans) + slots * kD * kD) *
+                    sizeof(unsigned int)) +
+           park_bytes(p);
 }
 
 hipError_t launch_fused(const void* q, const void* k, const void* v, const void* lg,
@@ -1141,6 +1269,7 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
     a.epoch = (unsigned int*)(base + 256);
     a.agg = (unsigned int*)(base + 256 + align256(slots * sizeof(unsigned int)));
     a.sin = a.agg + (size_t)p.seq_batch * agg_seq_words(p.n_spans);
+    a.park = park_bytes(p) ? (u4*)(base + fused_workspace_bytes(s, p) - park_bytes(p)) : nullptr;
     a.L = s.L;
     a.H = s.H;
     a.grid_h = s.grid_h;
@@ -1151,6 +1280,7 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
     a.n_spans = p.n_spans;
     a.slice_log2 = p.slice_log2;
     a.scale = s.scale;
+    if (p.keep && p.span >= 2 && a.park == nullptr) return hipErrorInvalidValue;
     const void* fn = pick_kernel(p.span, p.keep);
     resident_per_cu(p.span, p.keep);   // also raises the kernel's dynamic LDS limit
     const int n_seq = s.B * s.H;
