@@ -163,7 +163,7 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
         "alg_bytes_per_call": per_call,
         "rotating_sets": nsets,
         "graph": use_graph,
-        "kernel": {1: "generic", 2: "fused"}.get(kern, str(kern)),
+        "kernel": {1: "generic", 2: "fused", 3: "fused-rk"}.get(kern, str(kern)),
         "span": span,
         "grid": grid,
     }
@@ -280,7 +280,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": "gla_fused_kernel" if r["kernel"] == "fused" else "generic (3 kernels)",
+            "kernel": {"fused": "gla_fused_kernel", "fused-rk": "gla_fused_rk_kernel"}.get(
+                r["kernel"], "generic (3 kernels)"),
             "alg_bytes_per_launch": r["alg_bytes_per_call"],
             "launch_us_mean": r["call_us_mean"],
             "mfma_frac": mfma_flops(w) / (r["call_us_mean"] * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,

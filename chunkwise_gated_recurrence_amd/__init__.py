@@ -188,7 +188,8 @@ def gtr_gla_get_policy() -> int:
 
 
 def gtr_gla_plan(B, H, grid_h, grid_w, d_k, d_v, chunk, is_fp32) -> Tuple[int, int, int]:
-    """(kernel, span, grid) of the launch a call would make: kernel 1 generic, 2 fused."""
+    """(kernel, span, grid) of the launch a call would make: kernel 1 generic, 2 fused,
+    3 fused with the outputs kept in registers (long sequences)."""
     kern, span, grid = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     r = load_library().gtr_gla_plan(B, H, grid_h, grid_w, d_k, d_v, chunk, int(is_fp32),
                                     ctypes.byref(kern), ctypes.byref(span), ctypes.byref(grid))

@@ -181,13 +181,16 @@ __device__ __forceinline__ void ld_f8(const float* p, float* f)
 }
 
 // 0/1 selector (B operand of a 32x16 block): B[k][n] = (k == n + 16 half).
+// Lane (n, kb) holds B[8kb .. 8kb+7][n]: at most one 1.0 (fp16 0x3C00), at
+// element e = n + 16 half - 8 kb when that is in 0..7.
 __device__ __forceinline__ h8 selector(int lane, int half)
 {
-    h8 s;
+    const int e = (lane & 15) + 16 * half - 8 * (lane >> 4);
+    const unsigned int one = 0x3C00u << (16 * (e & 1));
+    u4 u;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-        s[e] = (_Float16)((8 * (lane >> 4) + e == (lane & 15) + 16 * half) ? 1.0f : 0.0f);
-    return s;
+    for (int d = 0; d < 4; ++d) u[d] = (e >> 1) == d ? one : 0u;
+    return __builtin_bit_cast(h8, u);
 }
 
 // ---------------------------------------------------------------------------
@@ -360,11 +363,18 @@ struct ChunkTmp {
 // Front half of one chunk: log2-gate prefix, per-dim constants, operand tiles,
 // and the state update S <- Diag(d_c) S + (k 2^{b_last-b})^T v. S (C layout:
 // rows 16w+4g+e, cols 16jt+r) enters as the state at the chunk start and
-// leaves as the state after it; written transposed to ST[st ^ 1] when
-// write_next. FULL also prepares the output half (Qt = q 2^b, Kh, qh).
-template <bool FULL>
+// leaves as the state after it; the entering state is staged transposed in
+// ST0 when stage_state. FULL also prepares the output half (Qt = q 2^b, Kh,
+// qh). after_a runs right after the first barrier, when every wave has taken
+// its operands out of R's source.
+struct NoHook {
+    __device__ void operator()() const {}
+};
+
+template <bool FULL, class AfterA = NoHook>
 __device__ __forceinline__ void chunk_front(Smem& sm, const ChunkRegs& R, int w, int lane, int c,
-                                            f4 (&S)[4], bool stage_state, h8 (&Qt)[2], ChunkTmp& T)
+                                            f4 (&S)[4], bool stage_state, h8 (&Qt)[2], ChunkTmp& T,
+                                            AfterA after_a = AfterA{})
 {
     const int r = lane & 15, g = lane >> 4;
     const int tid = 64 * w + lane;
@@ -397,6 +407,7 @@ __device__ __forceinline__ void chunk_front(Smem& sm, const ChunkRegs& R, int w,
             for (int e = 0; e < 8; ++e) sm.bfirst[32 * hh + 8 * g + e] = x[hh][e];
     }
     lds_barrier();  // (A)
+    after_a();      // every wave has read its chunk operands by now
     // the state entering this chunk, for its outputs (ST0 is free: the
     // previous chunk's output half has passed barrier A)
     if (stage_state) {
@@ -508,7 +519,7 @@ __device__ __forceinline__ void chunk_front(Smem& sm, const ChunkRegs& R, int w,
 }
 
 // Output half of one chunk: O^T[j][t] += sum_s VT[j][s] Sc[t][s], plus
-// sum_i ST[st][j][i] Qt[t][i] when has_state.
+// sum_i ST0[j][i] Qt[t][i] when has_state.
 __device__ __forceinline__ void chunk_back(Smem& sm, const FusedArgs& a, int b, int h, int t0, int w,
                                            int lane, bool has_state, f4 (&O)[4], const h8 (&Qt)[2],
                                            const ChunkTmp& T)
@@ -530,13 +541,20 @@ __device__ __forceinline__ void chunk_back(Smem& sm, const FusedArgs& a, int b, 
     } else {
         exact_scores(sm, a, b, h, t0, w, lane, sc);
     }
-    // mask, and write the wave's score rows Sc[t][s] (zeros above the diagonal)
+    // mask, and write the wave's score rows Sc[t][s] (zeros above the
+    // diagonal): blocks left of the wave's diagonal block are whole, blocks
+    // right of it are zero (w is uniform, so these are scalar branches)
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
         h4 hv;
+        if (sb < w) {
+            hv = pack4(sc[sb], 1.f);
+        } else if (sb == w) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            hv[e] = (_Float16)((16 * sb + 4 * g + e <= t) ? sc[sb][e] : 0.f);
+            for (int e = 0; e < 4; ++e) hv[e] = (_Float16)((4 * g + e <= r) ? sc[sb][e] : 0.f);
+        } else {
+            hv = h4{0, 0, 0, 0};
+        }
         st4(sm.Sc, t, 16 * sb + 4 * g, hv);
     }
     const int kmax = (w >= 2) ? 2 : 1;
@@ -620,13 +638,18 @@ __device__ __forceinline__ void publish_summary(const FusedArgs& a, Smem& sm, co
         const int ow = owner_region_words(ns, lo);
         const long long seq_base = (slot - j) / ns * agg_seq_words(ns);
         const __amdgpu_buffer_rsrc_t rs = rsrc(a.agg + seq_base, (int)(agg_seq_words(ns) * 4));
-        // word of state element e = i * 64 + col in the owner-major layout
-        auto uoff = [&](int e) { return (e >> lo) * ow + (j << lo) + (e & ((1 << lo) - 1)); };
+        // word of state element (row i, column col) in the owner-major layout:
+        // owner i >> lr (2^lr rows each), then span j's slice, row and column
+        const int lr = lo - 6;
+        auto row_word = [&](int i) {
+            return (i >> lr) * ow + (j << lo) + ((i & ((1 << lr) - 1)) << 6);
+        };
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
+        for (int e = 0; e < 4; ++e) {
+            const int base = 4 * (row_word(16 * w + 4 * g + e) + r);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                st_dev1(rs, 4 * uoff((16 * w + 4 * g + e) * kD + 16 * jt + r), ll_word(S[jt][e], tag));
+            for (int jt = 0; jt < 4; ++jt) st_dev1(rs, base + 64 * jt, ll_word(S[jt][e], tag));
+        }
         // rows 0-31 from LDS, 16 B per lane: row q >> 4, columns 4 (q & 15) .. +3
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -636,7 +659,7 @@ __device__ __forceinline__ void publish_summary(const FusedArgs& a, Smem& sm, co
             u4 t;
 #pragma unroll
             for (int e = 0; e < 4; ++e) t[e] = ll_word(x[e], tag);
-            st_dev4(rs, 4 * uoff(row * kD + c4), t);
+            st_dev4(rs, 4 * (row_word(row) + c4), t);
         }
         if (w == 2) {
             // decay of state row `lane`: owner (64 lane) >> lo, row within its slice
@@ -749,80 +772,16 @@ __device__ __forceinline__ void keep_pass_loop(const FusedArgs& a, Smem& sm, Chu
     }
 }
 
-// ---------------------------------------------------------------------------
-template <int SPAN, bool KEEP>
-__global__ void __launch_bounds__(kThreads, 3)
-gla_fused_kernel(FusedArgs a)
+// Boundary exchange of one span (workgroup j of sequence local_seq): owners
+// fold their slice of every span's summary and write each span's incoming
+// state; every workgroup then reads its own incoming state into Sin (C layout:
+// rows 16w + 4g + e, columns 16jt + r) and advances its slot's epoch. Every
+// wave must have finished with the chunk tiles' contents: they become scratch.
+__device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local_seq, int seq, int j,
+                                         long long seq_slot, int w, int lane, f4 (&Sin)[4])
 {
-    static_assert(!KEEP || SPAN <= kMaxKeep, "a kept span holds at most kMaxKeep chunks");
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
-
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const int lane = tid & 63;
+    const int tid = 64 * w + lane;
     const int r = lane & 15, g = lane >> 4;
-
-    const int local_seq = blockIdx.x / a.n_spans;
-    const int j = blockIdx.x - local_seq * a.n_spans;
-    const int seq = a.seq0 + local_seq;
-    const int b = seq / a.H, h = seq - (seq / a.H) * a.H;
-    const int span = KEEP ? SPAN : a.span;
-    const int c_first = j * span;
-    const int n_c = min(span, a.n_chunks - c_first);
-    __builtin_assume(n_c >= 1);   // every span starts inside the sequence
-
-    // Epochs of the sequence's span slots (thread t < n_spans reads slot t;
-    // the rest read zeros past the end), then the first chunk. The epochs are
-    // first used at the publish, so nothing waits for them before.
-    const long long seq_slot = (long long)local_seq * a.n_spans;
-    const unsigned int ep = __builtin_amdgcn_raw_buffer_load_b32(
-        rsrc(a.epoch + seq_slot, 4 * a.n_spans), 4 * tid, 0, kDevScope);
-    ChunkRegs cur;
-    load_chunk<KEEP>(a, b, h, c_first * kC, w, lane, cur);
-    if (tid < kD) {
-        sm.P[0][tid] = 0.f;
-        sm.Pend[tid] = 0.f;
-    }
-
-    // ---- 1. local pass --------------------------------------------------------
-    // The span summary is published right after the last chunk's state update,
-    // before that chunk's outputs, so the exchange overlaps them.
-    f4 S[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n) S[n] = f4{0.f, 0.f, 0.f, 0.f};
-    // kept intra-chunk output and correction operand of a one-chunk span
-    KeptOut<1> K[1];
-    h8 Qs[1][2];
-    if (KEEP) {
-        // No branch on the chunk count: a span that ends early runs empty
-        // chunks (zero rows leave the state and the decay unchanged and their
-        // outputs are never stored), so every workgroup does the same work and
-        // no path past the publish stores has a chunk load in flight (a wait
-        // for one would also wait for the stores).
-        if constexpr (SPAN == 1)
-            keep_pass1<1>(a, sm, cur, b, h, c_first, w, lane, S, K, Qs, seq_slot + j, j, ep);
-        else
-            keep_pass_loop<(KEEP ? SPAN : 1)>(a, sm, cur, b, h, c_first, w, lane, S, seq_slot + j,
-                                              j, ep);
-    } else {
-        h8 qdummy[2];
-        ChunkTmp T;
-        for (int c = 0; c < n_c; ++c) {
-            int ln = lane;
-            asm volatile("" : "+v"(ln));   // addresses recomputed per chunk, not held live
-            chunk_front<false>(sm, cur, w, ln, c, S, false, qdummy, T);
-            load_chunk<false>(a, b, h, c + 1 < n_c ? (c_first + c + 1) * kC : a.L, w, lane, cur);
-        }
-        publish_summary<false>(a, sm, S, seq_slot + j, j, ep, w, lane);
-    }
-
-    // ---- 2. boundary scan across the sequence's spans -------------------------
-    // The first `owners` workgroups (a power of two <= n_spans) each own a
-    // slice of 2^slice_log2 state elements: they read that slice of every
-    // span's U and D, fold S_in[m+1] = D_m S_in[m] + U_m through the spans, and
-    // write every span's incoming state (and the final state) for the slice.
-    // Then every workgroup reads its own S_in.
     lds_barrier();   // every wave is done with the chunk tiles
     // The chunk tiles are free now: 45 KB of LDS scratch for the exchange.
     unsigned char* scr = reinterpret_cast<unsigned char*>(sm.Kh);
@@ -987,7 +946,6 @@ gla_fused_kernel(FusedArgs a)
     // my incoming state S_in (C layout), by DMA into the scratch; span 0 reads
     // zeros like the others so that its epoch, too, advances only once every
     // owner has read it
-    f4 Sin[4];
     {
         const unsigned int tag = sm.tags[j];
         const unsigned int* src = a.sin + (seq_slot + j) * (kD * kD);
@@ -1026,6 +984,84 @@ gla_fused_kernel(FusedArgs a)
         // the epochs), and so has this workgroup: advance it.
         if (tid == 0) __hip_atomic_store(a.epoch + seq_slot + j, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+
+// ---------------------------------------------------------------------------
+template <int SPAN, bool KEEP>
+__global__ void __launch_bounds__(kThreads, 3)
+gla_fused_kernel(FusedArgs a)
+{
+    static_assert(!KEEP || SPAN <= kMaxKeep, "a kept span holds at most kMaxKeep chunks");
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+
+    const int local_seq = blockIdx.x / a.n_spans;
+    const int j = blockIdx.x - local_seq * a.n_spans;
+    const int seq = a.seq0 + local_seq;
+    const int b = seq / a.H, h = seq - (seq / a.H) * a.H;
+    const int span = KEEP ? SPAN : a.span;
+    const int c_first = j * span;
+    const int n_c = min(span, a.n_chunks - c_first);
+    __builtin_assume(n_c >= 1);   // every span starts inside the sequence
+
+    // Epochs of the sequence's span slots (thread t < n_spans reads slot t;
+    // the rest read zeros past the end), then the first chunk. The epochs are
+    // first used at the publish, so nothing waits for them before.
+    const long long seq_slot = (long long)local_seq * a.n_spans;
+    const unsigned int ep = __builtin_amdgcn_raw_buffer_load_b32(
+        rsrc(a.epoch + seq_slot, 4 * a.n_spans), 4 * tid, 0, kDevScope);
+    ChunkRegs cur;
+    load_chunk<KEEP>(a, b, h, c_first * kC, w, lane, cur);
+    if (tid < kD) {
+        sm.P[0][tid] = 0.f;
+        sm.Pend[tid] = 0.f;
+    }
+
+    // ---- 1. local pass --------------------------------------------------------
+    // The span summary is published right after the last chunk's state update,
+    // before that chunk's outputs, so the exchange overlaps them.
+    f4 S[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) S[n] = f4{0.f, 0.f, 0.f, 0.f};
+    // kept intra-chunk output and correction operand of a one-chunk span
+    KeptOut<1> K[1];
+    h8 Qs[1][2];
+    if (KEEP) {
+        // No branch on the chunk count: a span that ends early runs empty
+        // chunks (zero rows leave the state and the decay unchanged and their
+        // outputs are never stored), so every workgroup does the same work and
+        // no path past the publish stores has a chunk load in flight (a wait
+        // for one would also wait for the stores).
+        if constexpr (SPAN == 1)
+            keep_pass1<1>(a, sm, cur, b, h, c_first, w, lane, S, K, Qs, seq_slot + j, j, ep);
+        else
+            keep_pass_loop<(KEEP ? SPAN : 1)>(a, sm, cur, b, h, c_first, w, lane, S, seq_slot + j,
+                                              j, ep);
+    } else {
+        h8 qdummy[2];
+        ChunkTmp T;
+        for (int c = 0; c < n_c; ++c) {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));   // addresses recomputed per chunk, not held live
+            chunk_front<false>(sm, cur, w, ln, c, S, false, qdummy, T);
+            load_chunk<false>(a, b, h, c + 1 < n_c ? (c_first + c + 1) * kC : a.L, w, lane, cur);
+        }
+        publish_summary<false>(a, sm, S, seq_slot + j, j, ep, w, lane);
+    }
+
+    // ---- 2. boundary scan across the sequence's spans -------------------------
+    // The first `owners` workgroups (a power of two <= n_spans) each own a
+    // slice of 2^slice_log2 state elements: they read that slice of every
+    // span's U and D, fold S_in[m+1] = D_m S_in[m] + U_m through the spans, and
+    // write every span's incoming state (and the final state) for the slice.
+    // Then every workgroup reads its own S_in.
+    f4 Sin[4];
+    exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin);
 
     // ---- 3. outputs -----------------------------------------------------------
     if (KEEP) {
@@ -1105,6 +1141,187 @@ gla_fused_kernel(FusedArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Register-kept spans: every chunk's intra-chunk outputs (fp16) and correction
+// operand Qs stay in registers through the exchange (two workgroups per CU),
+// and the next chunk's g, k and v are staged in LDS by DMA while the current
+// chunk computes, so that a chunk's loads are in flight for a whole chunk.
+struct SmemRK {
+    Smem s;
+    // g, k, v of one chunk, 64 rows of eight 16-byte blocks; block m of row t
+    // sits in slot m ^ (t & 7) (consecutive rows spread over the banks)
+    _Float16 raw[3][kC * kD];
+};
+
+// Each wave stages its own 16 rows: lane l fetches row 16w + 8i + (l >> 3)
+// (i = 0, 1), block (l & 7) ^ (row & 7), into slot l & 7. Rows past the
+// sequence end read zeros.
+__device__ __forceinline__ void dma_gkv(const FusedArgs& a, SmemRK& sk, int b, int h, int t0, int w,
+                                        int lane)
+{
+    const int bytes = a.L * a.H * kD * 2;
+    const __amdgpu_buffer_rsrc_t rg = batch_rsrc(a.lg, a, b), rk = batch_rsrc(a.k, a, b),
+                                 rv = batch_rsrc(a.v, a, b);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = 16 * w + 8 * i + (lane >> 3);
+        const int t = t0 + row;
+        const int blk = (lane & 7) ^ (row & 7);
+        const int voff = t < a.L
+            ? (scan_to_spatial(t, a.L, a.grid_h, a.grid_w, a.dir) * a.H + h) * (kD * 2) + 16 * blk
+            : bytes;
+        const int base = (16 * w + 8 * i) * kD;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rg, (__attribute__((address_space(3))) void*)(sk.raw[0] + base), 16, voff, 0, 0, kNT);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (__attribute__((address_space(3))) void*)(sk.raw[1] + base), 16, voff, 0, 0, kNT);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)(sk.raw[2] + base), 16, voff, 0, 0, kNT);
+    }
+}
+
+__device__ __forceinline__ u4 raw_ld(const _Float16* tile, int row, int blk)
+{
+    return *reinterpret_cast<const u4*>(tile + row * kD + 8 * (blk ^ (row & 7)));
+}
+
+// q of a chunk into registers, in the operand layout of load_chunk.
+__device__ __forceinline__ void load_q(const FusedArgs& a, int b, int h, int t0, int w, int lane,
+                                       u4 (&q)[2])
+{
+    const int t = t0 + 16 * w + (lane & 15);
+    const int bytes = a.L * a.H * kD * 2;
+    const int voff = t < a.L
+        ? (scan_to_spatial(t, a.L, a.grid_h, a.grid_w, a.dir) * a.H + h) * (kD * 2) + 16 * (lane >> 4)
+        : bytes;
+    const __amdgpu_buffer_rsrc_t rq = batch_rsrc(a.q, a, b);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) q[hh] = load16(rq, voff + 64 * hh);
+}
+
+template <int SPAN>
+__global__ void __launch_bounds__(kThreads, 2)
+gla_fused_rk_kernel(FusedArgs a)
+{
+    static_assert(SPAN >= 2 && SPAN <= kMaxKeep, "register-kept spans hold 2 .. kMaxKeep chunks");
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    SmemRK& sk = *reinterpret_cast<SmemRK*>(smem_raw);
+    Smem& sm = sk.s;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+
+    const int local_seq = blockIdx.x / a.n_spans;
+    const int j = blockIdx.x - local_seq * a.n_spans;
+    const int seq = a.seq0 + local_seq;
+    const int b = seq / a.H, h = seq - (seq / a.H) * a.H;
+    const int c_first = j * SPAN;
+    const int n_c = min(SPAN, a.n_chunks - c_first);
+
+    const long long seq_slot = (long long)local_seq * a.n_spans;
+    const unsigned int ep = __builtin_amdgcn_raw_buffer_load_b32(
+        rsrc(a.epoch + seq_slot, 4 * a.n_spans), 4 * tid, 0, kDevScope);
+    dma_gkv(a, sk, b, h, c_first * kC, w, lane);
+    u4 qn[2];
+    load_q(a, b, h, c_first * kC, w, lane, qn);
+    if (tid < kD) {
+        sm.P[0][tid] = 0.f;
+        sm.Pend[tid] = 0.f;
+    }
+
+    // ---- 1. local pass: SPAN chunks, always (past the sequence end the
+    // staged rows are zeros: state and decay unchanged, outputs not stored)
+    f4 S[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) S[n] = f4{0.f, 0.f, 0.f, 0.f};
+    // kept per chunk: fp16 intra-chunk outputs (C layout) and Qs; chunk c
+    // ends up at index SPAN - 1 - c (the arrays shift by one per chunk, so
+    // that the loop body is one copy of the chunk code)
+    h8 KO[SPAN][2], KQ[SPAN][2];
+#pragma unroll 1
+    for (int c = 0; c < SPAN; ++c) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));   // addresses recomputed per chunk, not held live
+        const int rr = ln & 15, gg = ln >> 4;
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // this chunk's staged rows and q have landed
+        lds_barrier();                         // ... those of every wave
+        ChunkRegs R;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            R.q[hh] = qn[hh];
+            R.g[hh] = raw_ld(sk.raw[0], 16 * w + rr, 4 * hh + gg);
+            R.k[hh] = raw_ld(sk.raw[1], 16 * w + rr, 4 * hh + gg);
+            R.v[hh] = raw_ld(sk.raw[2], 16 * w + rr, 4 * hh + gg);
+        }
+        h8 Qt[2];
+        ChunkTmp T;
+        // never under a branch; past the span's end reads zeros
+        const int tn = c + 1 < SPAN ? (c_first + c + 1) * kC : a.L;
+        chunk_front<true>(sm, R, w, ln, c, S, c > 0, Qt, T, [&]() {
+            dma_gkv(a, sk, b, h, tn, w, ln);
+            load_q(a, b, h, tn, w, ln, qn);
+        });
+        if (c + 1 == SPAN) publish_summary<true>(a, sm, S, seq_slot + j, j, ep, w, ln);
+        h8 qs[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            qs[hh] = Qt[hh] * *reinterpret_cast<const h8*>(&sm.cp16[32 * hh + 8 * gg]);
+        f4 O[4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) O[n] = f4{0.f, 0.f, 0.f, 0.f};
+        chunk_back(sm, a, b, h, (c_first + c) * kC, w, ln, c > 0, O, Qt, T);
+#pragma unroll
+        for (int i = SPAN - 1; i > 0; --i) {
+            KO[i][0] = KO[i - 1][0];
+            KO[i][1] = KO[i - 1][1];
+            KQ[i][0] = KQ[i - 1][0];
+            KQ[i][1] = KQ[i - 1][1];
+        }
+        KO[0][0] = h8{(_Float16)O[0][0], (_Float16)O[0][1], (_Float16)O[0][2], (_Float16)O[0][3],
+                      (_Float16)O[1][0], (_Float16)O[1][1], (_Float16)O[1][2], (_Float16)O[1][3]};
+        KO[0][1] = h8{(_Float16)O[2][0], (_Float16)O[2][1], (_Float16)O[2][2], (_Float16)O[2][3],
+                      (_Float16)O[3][0], (_Float16)O[3][1], (_Float16)O[3][2], (_Float16)O[3][3]};
+        KQ[0][0] = qs[0];
+        KQ[0][1] = qs[1];
+    }
+
+    // ---- 2. boundary exchange --------------------------------------------------
+    f4 Sin[4];
+    exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin);
+
+    // ---- 3. outputs: O_c += Qs_c S_in -------------------------------------------
+    if (j > 0) {
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+            st4(sm.ST0, 16 * jt + r, 16 * w + 4 * g, pack4(Sin[jt], 1.f));
+    }
+    lds_barrier();
+#pragma unroll
+    for (int c = 0; c < SPAN; ++c) {
+        if (c < n_c) {
+            const int ki = SPAN - 1 - c;
+            f4 O[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                O[0][e] = (float)KO[ki][0][e];
+                O[1][e] = (float)KO[ki][0][4 + e];
+                O[2][e] = (float)KO[ki][1][e];
+                O[3][e] = (float)KO[ki][1][4 + e];
+            }
+            if (j > 0) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int jt = 0; jt < 4; ++jt)
+                        O[jt] = mfma(ld8(sm.ST0, 16 * jt + r, 32 * hh + 8 * g), KQ[ki][hh], O[jt]);
+            }
+            store_out(sm, a, b, h, (c_first + c) * kC, w, lane, O);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Zero fill, used instead of hipMemsetAsync so that it can sit in a captured graph.
 __global__ void fill_zero_kernel(unsigned char* p, size_t n)
 {
@@ -1149,11 +1366,24 @@ static int device_cus()
     return cached;
 }
 
-// Kept spans are instantiated for these lengths.
+// Kept spans (chunk registers, parking) are instantiated for these lengths;
+// register-kept spans for 2 .. kMaxKeep.
 static bool keep_span_ok(int span) { return span == 1 || span == 2 || span == 4 || span == 8; }
+static bool rk_span_ok(int span) { return span >= 2 && span <= kMaxKeep; }
 
-static const void* pick_kernel(int span, bool keep)
+static const void* pick_kernel(int span, bool keep, bool rk)
 {
+    if (rk) {
+        switch (span) {
+        case 2: return (const void*)gla_fused_rk_kernel<2>;
+        case 3: return (const void*)gla_fused_rk_kernel<3>;
+        case 4: return (const void*)gla_fused_rk_kernel<4>;
+        case 5: return (const void*)gla_fused_rk_kernel<5>;
+        case 6: return (const void*)gla_fused_rk_kernel<6>;
+        case 7: return (const void*)gla_fused_rk_kernel<7>;
+        default: return (const void*)gla_fused_rk_kernel<8>;
+        }
+    }
     if (!keep) return (const void*)gla_fused_kernel<1, false>;
     switch (span) {
     case 1: return (const void*)gla_fused_kernel<1, true>;
@@ -1163,22 +1393,17 @@ static const void* pick_kernel(int span, bool keep)
     }
 }
 
-static size_t smem_bytes(int span, bool keep)
-{
-    (void)span;
-    (void)keep;
-    return sizeof(Smem);
-}
+static size_t smem_bytes(bool rk) { return rk ? sizeof(SmemRK) : sizeof(Smem); }
 
 // Workgroups of one variant that fit on a CU at once.
-static int resident_per_cu(int span, bool keep)
+static int resident_per_cu(int span, bool keep, bool rk)
 {
-    static int cache[2][kMaxKeep + 1] = {};
-    int& c = cache[keep ? 1 : 0][keep ? span : 0];
+    static int cache[3][kMaxKeep + 1] = {};
+    int& c = cache[rk ? 2 : (keep ? 1 : 0)][(keep || rk) ? span : 0];
     if (c == 0) {
-        const void* fn = pick_kernel(span, keep);
+        const void* fn = pick_kernel(span, keep, rk);
         int n = 0;
-        const size_t sh = smem_bytes(span, keep);
+        const size_t sh = smem_bytes(rk);
         if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh) !=
                 hipSuccess ||
             hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, sh) != hipSuccess ||
@@ -1189,16 +1414,17 @@ static int resident_per_cu(int span, bool keep)
     return c;
 }
 
-FusedPlan fused_plan(const Shape& s, int span_override)
+FusedPlan fused_plan(const Shape& s, int span_override, int rk_override)
 {
     FusedPlan p;
     const int n_seq = s.B * s.H;
     const int nc = s.n_chunks;
-    auto fill = [&](int span, bool keep) {
+    auto fill = [&](int span, bool keep, bool rk = false) {
         p.span = span;
-        p.keep = keep;
+        p.keep = keep || rk;
+        p.rk = rk;
         p.n_spans = (nc + span - 1) / span;
-        const long long cap = (long long)resident_per_cu(span, keep) * device_cus();
+        const long long cap = (long long)resident_per_cu(span, keep, rk) * device_cus();
         // sequences per launch, so that every workgroup of a launch is resident
         long long per = cap / p.n_spans;
         if (per < 1) per = 1;
@@ -1210,19 +1436,33 @@ FusedPlan fused_plan(const Shape& s, int span_override)
         p.slice_log2 = 12 - lg;
     };
     auto one_seq_fits = [&]() {
-        return (long long)p.n_spans <= (long long)resident_per_cu(p.span, p.keep) * device_cus();
+        return (long long)p.n_spans <= (long long)resident_per_cu(p.span, p.keep, p.rk) * device_cus();
     };
     if (span_override > 0) {
+        if (rk_override > 0 && rk_span_ok(span_override)) {
+            fill(span_override, false, true);
+            if (one_seq_fits() && p.n_spans <= kMaxSpans) return p;
+        }
         fill(span_override, keep_span_ok(span_override));
         while (!one_seq_fits() || p.n_spans > kMaxSpans) fill(p.span * 2, false);
         return p;
     }
-    // the shortest kept span whose whole grid is resident; else streamed spans
-    for (int sp = 1; sp <= kMaxKeep; sp *= 2) {
-        fill(sp, true);
-        if (p.seq_batch == n_seq && p.n_spans <= kMaxSpans) return p;
+    auto whole = [&]() { return p.seq_batch == n_seq && p.n_spans <= kMaxSpans; };
+    // one chunk per workgroup when every chunk fits on the chip at once
+    fill(1, true);
+    if (whole()) return p;
+    // else the shortest register-kept span whose whole grid is resident
+    // (no outputs round-trip through memory), then parked spans
+    for (int sp = 2; sp <= kMaxKeep; ++sp) {
+        fill(sp, false, true);
+        if (whole()) return p;
     }
-    const long long cap = (long long)resident_per_cu(1, false) * device_cus();
+    for (int sp = 2; sp <= kMaxKeep; sp *= 2) {
+        fill(sp, true);
+        if (whole()) return p;
+    }
+    // else streamed spans
+    const long long cap = (long long)resident_per_cu(1, false, false) * device_cus();
     long long per_seq = cap / n_seq;
     if (per_seq < 1) per_seq = 1;
     if (per_seq > kMaxSpans) per_seq = kMaxSpans;
@@ -1239,7 +1479,8 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // workgroup).
 static size_t park_bytes(const FusedPlan& p)
 {
-    return (p.keep && p.span >= 2) ? (size_t)p.grid * kMaxKeep * kThreads * sizeof(u4) * 4 : 0;
+    return (p.keep && !p.rk && p.span >= 2) ? (size_t)p.grid * kMaxKeep * kThreads * sizeof(u4) * 4
+                                            : 0;
 }
 
 size_t fused_workspace_bytes(const Shape& s, const FusedPlan& p)
@@ -1280,16 +1521,17 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
     a.n_spans = p.n_spans;
     a.slice_log2 = p.slice_log2;
     a.scale = s.scale;
-    if (p.keep && p.span >= 2 && a.park == nullptr) return hipErrorInvalidValue;
-    const void* fn = pick_kernel(p.span, p.keep);
-    resident_per_cu(p.span, p.keep);   // also raises the kernel's dynamic LDS limit
+    if (p.keep && !p.rk && p.span >= 2 && a.park == nullptr) return hipErrorInvalidValue;
+    if (p.rk && !rk_span_ok(p.span)) return hipErrorInvalidValue;
+    const void* fn = pick_kernel(p.span, p.keep, p.rk);
+    resident_per_cu(p.span, p.keep, p.rk);   // also raises the kernel's dynamic LDS limit
     const int n_seq = s.B * s.H;
     for (int s0 = 0; s0 < n_seq; s0 += p.seq_batch) {
         a.seq0 = s0;
         const int nseq = (n_seq - s0 < p.seq_batch) ? (n_seq - s0) : p.seq_batch;
         void* args[] = {&a};
         const hipError_t e = hipLaunchKernel(fn, dim3(nseq * p.n_spans), dim3(kThreads), args,
-                                             smem_bytes(p.span, p.keep), st);
+                                             smem_bytes(p.rk), st);
         if (e != hipSuccess) return e;
     }
     return hipGetLastError();

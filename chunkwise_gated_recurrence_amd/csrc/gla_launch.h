@@ -17,14 +17,17 @@ hipError_t launch_generic(const void* q, const void* k, const void* v, const voi
 // Fused fp16 MFMA path (gla_fused.hip).
 struct FusedPlan {
     int span;        // chunks per workgroup
-    bool keep;       // outputs kept on chip through the boundary scan
+    bool keep;       // outputs kept through the boundary scan
+    bool rk;         // kept in registers, next chunk staged in LDS (two workgroups per CU)
     int n_spans;     // spans (workgroups) per (batch, head) sequence
     int seq_batch;   // sequences per launch (every workgroup of a launch is resident)
     int grid;        // workgroups per launch
     int slice_log2;  // log2 of the state elements each owning workgroup scans
 };
 bool fused_supported(const Shape& s);
-FusedPlan fused_plan(const Shape& s, int span_override);
+// span_override > 0 forces the span; rk_override > 0 then asks for the
+// register-kept variant (when that span has one).
+FusedPlan fused_plan(const Shape& s, int span_override, int rk_override);
 size_t fused_workspace_bytes(const Shape& s, const FusedPlan& p);
 hipError_t launch_fused(const void* q, const void* k, const void* v, const void* lg,
                         const Shape& s, const FusedPlan& p, void* out, float* final_state,

@@ -42,6 +42,12 @@ int span_override_from_env()
     return 0;
 }
 
+int rk_override_from_env()
+{
+    if (const char* env = std::getenv("GTR_GLA_RK")) return std::atoi(env);
+    return 0;
+}
+
 bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
 
 // Validation of sizes and scalars (pointers are checked separately).
@@ -96,7 +102,7 @@ int validate_pointers(const void* q, const void* k, const void* v, const void* l
     return GTR_GLA_OK;
 }
 
-enum Kernel { kGeneric = 1, kFused = 2 };
+enum Kernel { kGeneric = 1, kFused = 2, kFusedRegisterKept = 3 };
 
 struct Choice {
     Kernel kernel;
@@ -108,12 +114,12 @@ Choice choose(const Shape& s, bool is_fp32, int policy)
 {
     Choice c;
     c.kernel = kGeneric;
-    c.plan = FusedPlan{1, false, s.n_chunks, 0, 0, 0};
+    c.plan = FusedPlan{1, false, false, s.n_chunks, 0, 0, 0};
     const bool fused_ok = !is_fp32 && gtrgla::fused_supported(s);
     if (fused_ok && policy != GTR_GLA_POLICY_GENERIC) {
         c.kernel = kFused;
         const int span = (policy == GTR_GLA_POLICY_FUSED_ONE) ? 1 : span_override_from_env();
-        c.plan = gtrgla::fused_plan(s, span);
+        c.plan = gtrgla::fused_plan(s, span, rk_override_from_env());
         c.ws_bytes = gtrgla::fused_workspace_bytes(s, c.plan);
     } else {
         c.ws_bytes = gtrgla::generic_workspace_bytes(s);
@@ -294,7 +300,7 @@ int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chu
     const int r = validate_sizes(B, H, grid_h, grid_w, d_k, d_v, 0, chunk, &s);
     if (r != GTR_GLA_OK) return r;
     const Choice c = choose(s, is_fp32 != 0, current_policy());
-    if (kernel_out) *kernel_out = (int)c.kernel;
+    if (kernel_out) *kernel_out = c.kernel == kFused && c.plan.rk ? kFusedRegisterKept : (int)c.kernel;
     if (span_out) *span_out = c.kernel == kFused ? c.plan.span : 1;
     if (grid_out) *grid_out = c.kernel == kFused ? c.plan.grid : B * H * s.n_chunks;
     return GTR_GLA_OK;

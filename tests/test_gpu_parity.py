@@ -32,6 +32,7 @@ def gpu_ready():
     yield
     gla.gtr_gla_set_policy(gla.POLICY_AUTO)
     os.environ.pop("GTR_GLA_SPAN", None)
+    os.environ.pop("GTR_GLA_RK", None)
 
 
 def say(*a):
@@ -62,7 +63,7 @@ def ref(w, arrays, d, key=None):
 def check(w, arrays, d, tag, key=None, chunk=None, tol=None):
     say(f"[case] {tag} {w.name} B={w.B} H={w.H} grid={w.grid_h}x{w.grid_w} dk={w.d_k} dv={w.d_v} "
         f"{w.dtype} dir={d} chunk={chunk or w.chunk} policy={gla.gtr_gla_get_policy()} "
-        f"span_env={os.environ.get('GTR_GLA_SPAN')}")
+        f"span_env={os.environ.get('GTR_GLA_SPAN')} rk_env={os.environ.get('GTR_GLA_RK')}")
     o, s = run_gpu(w, arrays, d, chunk)
     o_ref, s_ref = ref(w, arrays, d, key)
     eo, es = oracle.rel_err(o, o_ref), oracle.rel_err(s, s_ref)
@@ -111,6 +112,30 @@ def test_fused_spans(name, span):
             check(w, arrays, d, f"fused-span{span}", key=w.name)
     finally:
         os.environ.pop("GTR_GLA_SPAN", None)
+        gla.gtr_gla_set_policy(gla.POLICY_AUTO)
+
+
+@pytest.mark.parametrize("span", [2, 3, 5, 7])
+@pytest.mark.parametrize("name", ["img1024", "ragged30"])
+def test_fused_register_kept(name, span):
+    """Spans whose every chunk's outputs stay in registers through the exchange
+    while the next chunk's g, k, v are staged in LDS (the long-sequence variant);
+    ragged30's last span is shorter than the others and its last chunk partial."""
+    w = gla_synth.WORKLOADS["img1024"]
+    if name == "ragged30":
+        w = w.with_(name="ragged30", B=2, H=3, grid_h=30, grid_w=30, seed=17)
+    arrays = gla_synth.generate(w)
+    gla.gtr_gla_set_policy(gla.POLICY_FUSED)
+    os.environ["GTR_GLA_SPAN"] = str(span)
+    os.environ["GTR_GLA_RK"] = "1"
+    try:
+        kern, sp, _ = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, 64, 64, 64, 0)
+        assert (kern, sp) == (3, span)
+        for d in DIRS:
+            check(w, arrays, d, f"fused-rk-span{span}", key=w.name)
+    finally:
+        os.environ.pop("GTR_GLA_SPAN", None)
+        os.environ.pop("GTR_GLA_RK", None)
         gla.gtr_gla_set_policy(gla.POLICY_AUTO)
 
 
