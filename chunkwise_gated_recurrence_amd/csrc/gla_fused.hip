@@ -886,12 +886,24 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                 compA[tid] = A;
                 compB[tid] = Bv;
                 lds_barrier();
+                // the ranges before mine, four at a time (reads first)
                 f4 run = {0.f, 0.f, 0.f, 0.f};
-                for (int pp = 0; pp < p; ++pp) {
-                    const float ca = compA[pp * Qn + qi0];
-                    const f4 cb = compB[pp * Qn + qi0];
+                for (int pp0 = 0; pp0 < p; pp0 += 4) {
+                    float ca[4];
+                    f4 cb[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) run[e] = ca * run[e] + cb[e];
+                    for (int i = 0; i < 4; ++i) {
+                        const int pp = min(pp0 + i, p - 1);
+                        ca[i] = compA[pp * Qn + qi0];
+                        cb[i] = compB[pp * Qn + qi0];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (pp0 + i < p) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) run[e] = ca[i] * run[e] + cb[i][e];
+                        }
+                    }
                 }
                 for (int m0 = m_lo; m0 < m_hi; m0 += 4) {
                     u4 xb[4];
@@ -928,17 +940,28 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
             const __amdgpu_buffer_rsrc_t rf =
                 rsrc(a.final_state + (a.final_state ? (long long)seq * kD * kD : 0),
                      a.final_state ? kD * kD * 4 : 0);
-            const int n16 = (ns + 1) << lq;            // <= 2048
+            // U pieces (< 2048: ns << lo < 2^13 words), in batches whose LDS
+            // reads are all issued before the batch's stores
+            const int nu = ns << lq;
+            const int oob = 0x7FFFFFF0;
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const int q = tid - 128 + 128 * k;
-                const int m = q >> lq, off = e_first + 4 * (q & ((1 << lq) - 1));
-                const u4 x = *reinterpret_cast<const u4*>(
-                    m < ns ? ubuf + 4 * (q & 2047) : fin + 4 * (q & ((1 << lq) - 1)));
-                const int oob = 0x7FFFFFF0;
-                st_dev4(rs, (q < n16 && m < ns) ? 4 * (m * (kD * kD) + off) : oob, x);
-                __builtin_amdgcn_raw_buffer_store_b128(x, rf, (q < n16 && m == ns) ? 4 * off : oob, 0, 0);
+            for (int k0 = 0; k0 < 16; k0 += 8) {
+                u4 x[8];
+                int o[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int q = tid - 128 + 128 * (k0 + i);
+                    x[i] = *reinterpret_cast<const u4*>(ubuf + 4 * q);
+                    o[i] = q < nu ? 4 * ((q >> lq) * (kD * kD) + e_first + 4 * (q & ((1 << lq) - 1)))
+                                  : oob;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) st_dev4(rs, o[i], x[i]);
             }
+            // the slice of the final state (<= 1024 pieces)
+            for (int q = tid - 128; q < (1 << lq); q += 128)
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u4*>(fin + 4 * q), rf,
+                                                       4 * (e_first + 4 * q), 0, 0);
         }
     }
     lds_barrier();   // scratch free again
