@@ -16,6 +16,9 @@ section 前置知识 › 门控线性注意力(GLA) and section 核心方法):
 
     S_t = Diag(gamma_t) S_{t-1} + k_t^T v_t,   o_t = d_k^{-1/2} q_t S_t,   S_0 = 0
 
+(``recurrent_init``: the same from a given S_0), and the output epilogue that
+the end-to-end operator fuses (0539edu.com page, appendix E.3.1; ``rmsnorm_gate``)
+
 with gamma_t = exp(log_gamma_t) per key dimension, walked along one of four
 scan orders over the patch grid (same sections; see ``scan_order``).
 
@@ -65,6 +68,11 @@ def _load():
             fn.argtypes = [dp, dp, dp, dp, i, i, i, i, i, i, i, dp, dp, i]
         lib.gla_oracle_chunked.restype = i
         lib.gla_oracle_chunked.argtypes = [dp, dp, dp, dp, i, i, i, i, i, i, i, i, dp, dp, i]
+        lib.gla_oracle_recurrent_init.restype = i
+        lib.gla_oracle_recurrent_init.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, i, i, dp, dp,
+                                                  i]
+        lib.gla_oracle_rmsnorm_gate.restype = i
+        lib.gla_oracle_rmsnorm_gate.argtypes = [dp, dp, dp, ctypes.c_double, ctypes.c_long, i, dp]
         lib.gla_oracle_scan_position.restype = ctypes.c_long
         lib.gla_oracle_scan_position.argtypes = [ctypes.c_long, i, i, i]
         _lib = lib
@@ -136,6 +144,41 @@ def recurrent(q, k, v, log_gamma, grid_h: int, grid_w: int, direction,
               threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Token-by-token fp64 recurrence. Returns (o [B,L,H,d_v], final_state [B,H,d_k,d_v])."""
     return _call("gla_oracle_recurrent", q, k, v, log_gamma, grid_h, grid_w, direction, threads)
+
+
+def recurrent_init(q, k, v, log_gamma, initial_state, grid_h: int, grid_w: int, direction,
+                   threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """The recurrence from S_0 = initial_state [B,H,d_k,d_v] instead of zero."""
+    lib = _load()
+    B, L, H, dk, dv = _shapes(q, k, v, log_gamma, grid_h, grid_w)
+    s0 = _f64(initial_state)
+    if s0.shape != (B, H, dk, dv):
+        raise ValueError("initial_state must be [B, H, d_k, d_v]")
+    q64, k64, v64, g64 = _f64(q), _f64(k), _f64(v), _f64(log_gamma)
+    out = np.zeros((B, L, H, dv), dtype=np.float64)
+    fs = np.zeros((B, H, dk, dv), dtype=np.float64)
+    nt = default_threads() if threads is None else int(threads)
+    r = lib.gla_oracle_recurrent_init(_ptr(q64), _ptr(k64), _ptr(v64), _ptr(g64), _ptr(s0), B, H,
+                                      grid_h, grid_w, dk, dv, _dir(direction), _ptr(out), _ptr(fs),
+                                      nt)
+    if r != 0:
+        raise RuntimeError(f"gla_oracle_recurrent_init failed with status {r}")
+    return out, fs
+
+
+def rmsnorm_gate(o, gate, weight, eps: float) -> np.ndarray:
+    """Output epilogue over the last axis: o / sqrt(mean(o^2) + eps) * weight * SiLU(gate)."""
+    lib = _load()
+    o64, z64, w64 = _f64(o), _f64(gate), _f64(weight)
+    if z64.shape != o64.shape or w64.shape != (o64.shape[-1],):
+        raise ValueError("gate must have o's shape and weight o's last dimension")
+    d = o64.shape[-1]
+    rows = o64.size // d
+    y = np.zeros_like(o64)
+    r = lib.gla_oracle_rmsnorm_gate(_ptr(o64), _ptr(z64), _ptr(w64), float(eps), rows, d, _ptr(y))
+    if r != 0:
+        raise RuntimeError(f"gla_oracle_rmsnorm_gate failed with status {r}")
+    return y
 
 
 def bruteforce(q, k, v, log_gamma, grid_h: int, grid_w: int, direction,

@@ -33,8 +33,18 @@
  * dir 3 = column-major raster reversed. Outputs are stored at the spatial
  * position of their token, not in scan order.
  *
- * Three entry points, each independent of the others:
+ * Entry points, each independent of the others:
  *   gla_oracle_recurrent  - the recurrence above, token by token (the oracle);
+ *   gla_oracle_recurrent_init - the same recurrence from a given state S_0
+ *                           instead of zero (the state a preceding span of
+ *                           the scan leaves; the pages' operator fixes S_0 = 0,
+ *                           summary page section 方法步骤详情 step 5, so this
+ *                           is the general form of that recurrence);
+ *   gla_oracle_rmsnorm_gate - the output epilogue that the end-to-end operator
+ *                           fuses (0539edu.com page, appendix E.3.1): per
+ *                           (batch, token, head) row of d_v outputs,
+ *                           y = o / sqrt(mean(o^2) + eps) * w * SiLU(z),
+ *                           SiLU(z) = z / (1 + e^{-z});
  *   gla_oracle_bruteforce - the same outputs as an explicit double sum
  *                           o_t = d_k^{-1/2} sum_{s<=t} (q_t * prod_{r=s+1..t} gamma_r) . k_s  v_s
  *                           (used only to pin the recurrence on small inputs);
@@ -76,6 +86,7 @@ long gla_oracle_scan_position(long t, int grid_h, int grid_w, int dir)
 
 typedef struct {
     const double *q, *k, *v, *lg;
+    const double *init;          /* [B, H, d_k, d_v] state before the first step, or NULL (zero) */
     int B, H, grid_h, grid_w, d_k, d_v, dir, chunk;
     double *out, *final_state;
     int nthreads, tid;
@@ -105,6 +116,8 @@ static int recurrent_one(const job_t *a, int b, int h)
     const double scale = 1.0 / sqrt((double)dk);
     double *S = calloc((size_t)dk * dv, sizeof(double));
     if (!S) return -2;
+    if (a->init)
+        memcpy(S, a->init + ((size_t)b * a->H + h) * dk * dv, (size_t)dk * dv * sizeof(double));
     for (long t = 0; t < L; ++t) {
         long p = gla_oracle_scan_position(t, a->grid_h, a->grid_w, a->dir);
         const double *qt = a->q + at(a, b, p, h, dk);
@@ -337,6 +350,36 @@ int gla_oracle_recurrent(const double *q, const double *k, const double *v, cons
 {
     return run(make_job(q, k, v, lg, B, H, grid_h, grid_w, d_k, d_v, dir, 0, out,
                         final_state, nthreads), recurrent_one);
+}
+
+int gla_oracle_recurrent_init(const double *q, const double *k, const double *v, const double *lg,
+                              const double *init, int B, int H, int grid_h, int grid_w, int d_k,
+                              int d_v, int dir, double *out, double *final_state, int nthreads)
+{
+    job_t a = make_job(q, k, v, lg, B, H, grid_h, grid_w, d_k, d_v, dir, 0, out, final_state,
+                       nthreads);
+    a.init = init;
+    return run(a, recurrent_one);
+}
+
+/* Output epilogue, row by row: rows of d values, o and z [rows, d], w [d]. */
+int gla_oracle_rmsnorm_gate(const double *o, const double *z, const double *w, double eps,
+                            long rows, int d, double *y)
+{
+    if (!o || !z || !w || !y || rows < 0 || d < 1 || !(eps >= 0.0)) return -1;
+    for (long n = 0; n < rows; ++n) {
+        const double *on = o + (size_t)n * d, *zn = z + (size_t)n * d;
+        double *yn = y + (size_t)n * d;
+        double ms = 0.0;
+        for (int j = 0; j < d; ++j) ms += on[j] * on[j];
+        ms /= d;
+        const double inv = 1.0 / sqrt(ms + eps);
+        for (int j = 0; j < d; ++j) {
+            const double silu = zn[j] / (1.0 + exp(-zn[j]));
+            yn[j] = on[j] * inv * w[j] * silu;
+        }
+    }
+    return 0;
 }
 
 int gla_oracle_bruteforce(const double *q, const double *k, const double *v, const double *lg,

@@ -284,3 +284,80 @@ def test_rejects_bad_shapes():
         oracle.recurrent(q, k, v, lg, 3, 4, "l2r")
     with pytest.raises(KeyError):
         oracle.recurrent(q, k, v, lg, 3, 3, "diag")
+
+
+# --------------------------------------------------------------------------- initial state
+@pytest.mark.parametrize("d", ["l2r", "r2l"])
+def test_initial_state_chains_spans(d):
+    """Running the first rows of the scan, then the rest from the state they leave,
+    gives the outputs and final state of one run over the whole grid."""
+    gh, gw, h1 = 7, 5, 3
+    q, k, v, lg = rand_inputs(41, 2, gh, gw, 3, 4, 3)
+    o, S = oracle.recurrent(q, k, v, lg, gh, gw, d)
+    # raster rows [0, h1) are scanned first by l2r; rows [gh - h1, gh) first by r2l
+    first = slice(0, h1 * gw) if d == "l2r" else slice((gh - h1) * gw, gh * gw)
+    rest = slice(h1 * gw, gh * gw) if d == "l2r" else slice(0, (gh - h1) * gw)
+    part = lambda x, sl: x[:, sl]
+    o1, S1 = oracle.recurrent(*(part(x, first) for x in (q, k, v, lg)), h1, gw, d)
+    o2, S2 = oracle.recurrent_init(*(part(x, rest) for x in (q, k, v, lg)), S1, gh - h1, gw, d)
+    np.testing.assert_allclose(o1, o[:, first], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(o2, o[:, rest], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S2, S, rtol=1e-12, atol=1e-12)
+
+
+def test_initial_state_alone_decays_by_the_gate_products():
+    """With k = 0 nothing is added: S_t = Diag(prod_{r<=t} gamma_r) S_0, so
+    o_t = d_k^{-1/2} sum_i q_t[i] prod_{r<=t} gamma_r[i] S_0[i, :]."""
+    gh, gw, dk, dv = 3, 4, 5, 2
+    q, k, v, lg = rand_inputs(42, 1, gh, gw, 2, dk, dv)
+    S0 = np.random.default_rng(43).standard_normal((1, 2, dk, dv))
+    o, S = oracle.recurrent_init(q, 0 * k, v, lg, S0, gh, gw, "t2b")
+    order = np_order(gh, gw, "t2b")
+    P = np.exp(np.cumsum(lg[:, order], axis=1))             # [B, L, H, dk] in scan order
+    expect = np.einsum("blhi,blhi,bhij->blhj", q[:, order], P, S0) / np.sqrt(dk)
+    np.testing.assert_allclose(o[:, order], expect, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S, P[:, -1][..., None] * S0, rtol=1e-12, atol=1e-12)
+
+
+def test_initial_state_is_additive():
+    """o and S are linear in (v, S_0) jointly: the run from S_0 is the zero-state run
+    plus the run of S_0 alone (v = 0)."""
+    q, k, v, lg = rand_inputs(44, 2, 4, 4, 2, 3, 5)
+    S0 = np.random.default_rng(45).standard_normal((2, 2, 3, 5))
+    o, S = oracle.recurrent_init(q, k, v, lg, S0, 4, 4, "b2t")
+    oa, Sa = oracle.recurrent(q, k, v, lg, 4, 4, "b2t")
+    ob, Sb = oracle.recurrent_init(q, k, 0 * v, lg, S0, 4, 4, "b2t")
+    np.testing.assert_allclose(o, oa + ob, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S, Sa + Sb, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- output epilogue
+def test_rmsnorm_gate_pins():
+    rng = np.random.default_rng(46)
+    o = rng.standard_normal((5, 7, 16))
+    w = rng.uniform(0.5, 2.0, 16)
+    ones = np.ones(16)
+    big = np.full(o.shape, 40.0)     # SiLU(40) = 40 (1 - 4e-18): the gate passes the value
+    # a zero gate closes the output
+    assert np.all(oracle.rmsnorm_gate(o, np.zeros(o.shape), w, 1e-5) == 0)
+    # wide-open gate, unit weight, eps = 0: each row is o scaled to unit mean square
+    n = oracle.rmsnorm_gate(o, big, ones, 0.0) / 40.0
+    np.testing.assert_allclose(np.mean(n ** 2, axis=-1), 1.0, rtol=1e-12)
+    ratio = n / o
+    assert np.all(ratio > 0)
+    np.testing.assert_allclose(ratio, ratio[..., :1] * np.ones_like(ratio), rtol=1e-12)
+    # eps equal to the row's mean square halves it
+    ms = np.mean(o ** 2, axis=-1)
+    half = np.stack([oracle.rmsnorm_gate(o[i, j:j + 1], big[i, j:j + 1], ones, ms[i, j])
+                     for i in range(5) for j in range(7)]) / 40.0
+    np.testing.assert_allclose(np.mean(half ** 2, axis=-1), 0.5, rtol=1e-12)
+    # the weight multiplies per channel
+    np.testing.assert_allclose(oracle.rmsnorm_gate(o, big, w, 0.0), w * n * 40.0, rtol=1e-12)
+    # scale invariance without eps
+    np.testing.assert_allclose(oracle.rmsnorm_gate(3.5 * o, big, w, 0.0),
+                               oracle.rmsnorm_gate(o, big, w, 0.0), rtol=1e-12)
+    # SiLU(z) - SiLU(-z) = z, because sigma(z) + sigma(-z) = 1
+    z = rng.uniform(-6, 6, o.shape)
+    diff = oracle.rmsnorm_gate(o, z, w, 1e-3) - oracle.rmsnorm_gate(o, -z, w, 1e-3)
+    np.testing.assert_allclose(diff, z * oracle.rmsnorm_gate(o, big, w, 1e-3) / 40.0,
+                               rtol=1e-10, atol=1e-12)
