@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libgtrgla.so")
 
 # status codes (gtr_gla_status)
 OK, ERR_NULL, ERR_SHAPE, ERR_DIR, ERR_CHUNK, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, \
-    ERR_ALIAS, ERR_POLICY = range(10)
+    ERR_ALIAS, ERR_POLICY, ERR_VALUE = range(11)
 # scan orders (gtr_gla_dir)
 L2R, R2L, T2B, B2T = 0, 1, 2, 3
 DIRS = {"l2r": L2R, "r2l": R2L, "t2b": T2B, "b2t": B2T}
@@ -32,7 +32,8 @@ POLICY_AUTO, POLICY_GENERIC, POLICY_FUSED, POLICY_FUSED_ONE = 0, 1, 2, 3
 
 EXPORTED = (
     "gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_workspace_bytes", "gtr_gla_workspace_init",
-    "gtr_gla_fwd_ws", "gtr_gla_fwd_f32_ws", "gtr_gla_set_policy", "gtr_gla_get_policy",
+    "gtr_gla_fwd_ws", "gtr_gla_fwd_f32_ws", "gtr_gla_fwd_ex", "gtr_gla_set_policy",
+    "gtr_gla_get_policy",
     "gtr_gla_plan", "gtr_gla_status_str",
 )
 
@@ -62,6 +63,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gtr_gla_fwd_f32_ws.argtypes = fwd + [P, Z, P]
     for f in (lib.gtr_gla_fwd, lib.gtr_gla_fwd_f32, lib.gtr_gla_fwd_ws, lib.gtr_gla_fwd_f32_ws):
         f.restype = I
+    lib.gtr_gla_fwd_ex.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, I, I, I, I, I, I, I, I, I,
+                                   P, P, P, Z, P]
+    lib.gtr_gla_fwd_ex.restype = I
     lib.gtr_gla_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
     lib.gtr_gla_workspace_bytes.restype = Z
     lib.gtr_gla_workspace_init.argtypes = [P, Z, P]
@@ -179,6 +183,26 @@ def gtr_gla_fwd_f32_ws(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, dir, 
     _raise(r, "gtr_gla_fwd_f32_ws")
 
 
+def gtr_gla_fwd_ex(q, k, v, log_gamma, initial_state, gate, norm_weight, norm_eps: float, B: int,
+                   H: int, grid_h: int, grid_w: int, d_k: int, d_v: int, dir: int, chunk: int,
+                   is_fp32: int, out, final_state=None, workspace=None, workspace_bytes: int = 0,
+                   stream=None) -> None:
+    """Forward from an initial state and/or with the RMSNorm + SiLU output gate."""
+    import torch
+    dtype = torch.float32 if is_fp32 else torch.float16
+    _check_all(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, out, final_state, dtype)
+    if min(B, H, grid_h, grid_w, d_k, d_v) >= 1:
+        _check(initial_state, "initial_state", torch.float32, B * H * d_k * d_v)
+        _check(gate, "gate", dtype, B * grid_h * grid_w * H * d_v)
+        _check(norm_weight, "norm_weight", torch.float32, d_v)
+    r = load_library().gtr_gla_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma),
+                                      _ptr(initial_state), _ptr(gate), _ptr(norm_weight),
+                                      float(norm_eps), B, H, grid_h, grid_w, d_k, d_v, dir, chunk,
+                                      int(is_fp32), _ptr(out), _ptr(final_state), _ptr(workspace),
+                                      workspace_bytes, _stream(stream))
+    _raise(r, "gtr_gla_fwd_ex")
+
+
 def gtr_gla_set_policy(policy: int) -> None:
     _raise(load_library().gtr_gla_set_policy(int(policy)), "gtr_gla_set_policy")
 
@@ -205,10 +229,12 @@ def gtr_gla_status_str(status: int) -> str:
 
 
 def forward(q, k, v, log_gamma, grid_h: int, grid_w: int, dir, chunk: int = 64,
-            out=None, final_state=None, stream=None):
+            out=None, final_state=None, stream=None, initial_state=None, gate=None,
+            norm_weight=None, norm_eps: float = 1e-5):
     """Allocate outputs (if not given) and run the forward for [B, L, H, d] tensors.
 
-    Returns (out, final_state). fp16 inputs take gtr_gla_fwd, fp32 gtr_gla_fwd_f32.
+    Returns (out, final_state). fp16 inputs take gtr_gla_fwd, fp32 gtr_gla_fwd_f32;
+    with an initial state or an output gate, gtr_gla_fwd_ex.
     """
     import torch
     if isinstance(dir, str):
@@ -219,6 +245,11 @@ def forward(q, k, v, log_gamma, grid_h: int, grid_w: int, dir, chunk: int = 64,
         out = torch.empty((B, L, H, dv), dtype=q.dtype, device=q.device)
     if final_state is None:
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if initial_state is not None or gate is not None:
+        gtr_gla_fwd_ex(q, k, v, log_gamma, initial_state, gate, norm_weight, norm_eps, B, H,
+                       grid_h, grid_w, dk, dv, int(dir), chunk, int(q.dtype == torch.float32), out,
+                       final_state, stream=stream)
+        return out, final_state
     fn = gtr_gla_fwd_f32 if q.dtype == torch.float32 else gtr_gla_fwd
     fn(q, k, v, log_gamma, B, H, grid_h, grid_w, dk, dv, int(dir), chunk, out, final_state, stream)
     return out, final_state

@@ -36,4 +36,13 @@ struct Shape {
     float scale;   // d_k^{-1/2}
 };
 
+// Optional parts of a call: a nonzero initial state, and the RMSNorm + SiLU
+// output gate applied to the outputs.
+struct Extras {
+    const float* init = nullptr;     // [B, H, d_k, d_v] or null (zero)
+    const void* gate = nullptr;      // [B, L, H, d_v] in the input precision, or null
+    const float* norm_w = nullptr;   // [d_v], with gate
+    float eps = 0.f;
+};
+
 }  // namespace gtrgla

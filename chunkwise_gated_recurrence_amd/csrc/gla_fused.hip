@@ -213,6 +213,10 @@ struct FusedArgs {
     int seq0;                   // first sequence of this launch
     int slice_log2;             // log2 of the state elements each owner scans
     float scale;
+    const float* init;          // [B, H, 64, 64] states before the first step, or null (zero)
+    const __half* gate;         // [B, L, H, 64] output gate, or null (outputs as they are)
+    const float* norm_w;        // [64] RMSNorm weight of the output epilogue (with gate)
+    float eps;
 };
 
 struct Smem {
@@ -234,6 +238,7 @@ struct Smem {
     float blast[kD];          // b_last (log2 of d_c)
     float P[kMaxKeep + 1][kD];  // log2 decay from the span start to each chunk start
     float Pend[kD];           // log2 decay of the span so far
+    float nw[kD];             // RMSNorm weight of the output epilogue
     unsigned int tags[kMaxSpans];   // expected tag of every span slot of the sequence
     int fail;
     int stale;
@@ -573,20 +578,61 @@ __device__ __forceinline__ void chunk_back(Smem& sm, const FusedArgs& a, int b, 
     }
 }
 
-// Store O (C layout, rows t = 16w + r) scaled, staged through the wave's rows of Sc.
+// Gate of a chunk's rows for the output epilogue, in store_out's layout (lane
+// (r, g) of wave w: row 16w + r, dims 8g + 32hh .. +7). No gate: zeros, no
+// memory access (an empty buffer resource).
+__device__ __forceinline__ void load_gate(const FusedArgs& a, int b, int h, int t0, int w, int lane,
+                                          u4 (&z)[2])
+{
+    const int t = t0 + 16 * w + (lane & 15);
+    const long long per_batch = (long long)a.L * a.H * kD;
+    const int bytes = a.gate ? (int)(per_batch * 2) : 0;
+    const int voff = t < a.L
+        ? (scan_to_spatial(t, a.L, a.grid_h, a.grid_w, a.dir) * a.H + h) * (kD * 2) + 16 * (lane >> 4)
+        : (int)(per_batch * 2);
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.gate + (a.gate ? b * per_batch : 0)), (short)0, bytes, 0x00020000);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) z[hh] = load16(rz, voff + 64 * hh);
+}
+
+// Store O (C layout, rows t = 16w + r) scaled, staged through the wave's rows
+// of Sc. With a gate, the output epilogue: each row o (scaled) becomes
+// o / sqrt(mean(o^2) + eps) * w * SiLU(z), z from load_gate (the row's mean
+// square is summed over the four lanes that hold it).
 __device__ __forceinline__ void store_out(Smem& sm, const FusedArgs& a, int b, int h, int t0, int w,
-                                          int lane, const f4 (&O)[4])
+                                          int lane, const f4 (&O)[4], const u4 (&z)[2])
 {
     const int r = lane & 15, g = lane >> 4;
     const int t = 16 * w + r;
+    float f = a.scale;
+    if (a.gate) {
+        float ss = 0.f;
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) st4(sm.Sc, t, 16 * jt + 4 * g, pack4(O[jt], a.scale));
+        for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss += O[jt][e] * O[jt][e];
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        f = a.scale * __builtin_amdgcn_rsqf(a.scale * a.scale * ss * (1.f / kD) + a.eps);
+    }
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) st4(sm.Sc, t, 16 * jt + 4 * g, pack4(O[jt], f));
     __builtin_amdgcn_wave_barrier();
     const long long off = row_offset(a, b, h, t0 + t);
     if (off >= 0) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const h8 val = ld8(sm.Sc, t, 8 * g + 32 * hh);
+            h8 val = ld8(sm.Sc, t, 8 * g + 32 * hh);
+            if (a.gate) {
+                float zf[8], wf[8];
+                unpack8(z[hh], zf);
+                ld_f8(&sm.nw[8 * g + 32 * hh], wf);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    val[e] = (_Float16)((float)val[e] * wf[e] * zf[e] *
+                                        rcp(1.f + ex2(-kLog2e * zf[e])));
+            }
             __builtin_nontemporal_store(__builtin_bit_cast(u4, val),
                                         reinterpret_cast<u4*>(a.out + off + 8 * g + 32 * hh));
         }
@@ -886,8 +932,12 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                 compA[tid] = A;
                 compB[tid] = Bv;
                 lds_barrier();
-                // the ranges before mine, four at a time (reads first)
+                // the ranges before mine, four at a time (reads first), from
+                // the initial state
                 f4 run = {0.f, 0.f, 0.f, 0.f};
+                if (a.init)
+                    run = *reinterpret_cast<const f4*>(a.init + (long long)seq * (kD * kD) +
+                                                       e_first + el);
                 for (int pp0 = 0; pp0 < p; pp0 += 4) {
                     float ca[4];
                     f4 cb[4];
@@ -1038,6 +1088,9 @@ gla_fused_kernel(FusedArgs a)
     const long long seq_slot = (long long)local_seq * a.n_spans;
     const unsigned int ep = __builtin_amdgcn_raw_buffer_load_b32(
         rsrc(a.epoch + seq_slot, 4 * a.n_spans), 4 * tid, 0, kDevScope);
+    // RMSNorm weight of the output epilogue (an empty resource without a gate)
+    const float nwr = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        rsrc(a.norm_w, a.gate ? 4 * kD : 0), 4 * (tid & (kD - 1)), 0, 0));
     ChunkRegs cur;
     load_chunk<KEEP>(a, b, h, c_first * kC, w, lane, cur);
     if (tid < kD) {
@@ -1083,12 +1136,17 @@ gla_fused_kernel(FusedArgs a)
     // span's U and D, fold S_in[m+1] = D_m S_in[m] + U_m through the spans, and
     // write every span's incoming state (and the final state) for the slice.
     // Then every workgroup reads its own S_in.
+    u4 zg[2];   // the one-chunk span's gate, fetched while the exchange runs
+    if (KEEP && SPAN == 1) load_gate(a, b, h, c_first * kC, w, lane, zg);
     f4 Sin[4];
     exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin);
 
     // ---- 3. outputs -----------------------------------------------------------
+    // the incoming state is nonzero past the first span, or with an initial state
+    const bool has_in = j > 0 || a.init != nullptr;
+    if (tid < kD) sm.nw[tid] = nwr;
     if (KEEP) {
-        if (j > 0) {
+        if (has_in) {
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
                 st4(sm.ST0, 16 * jt + r, 16 * w + 4 * g, pack4(Sin[jt], 1.f));
@@ -1097,14 +1155,14 @@ gla_fused_kernel(FusedArgs a)
         if constexpr (SPAN == 1) {
             f4 O[4];
             K[0].get(O);
-            if (j > 0) {
+            if (has_in) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                     for (int jt = 0; jt < 4; ++jt)
                         O[jt] = mfma(ld8(sm.ST0, 16 * jt + r, 32 * hh + 8 * g), Qs[0][hh], O[jt]);
             }
-            store_out(sm, a, b, h, c_first * kC, w, lane, O);
+            store_out(sm, a, b, h, c_first * kC, w, lane, O, zg);
         } else {
             // parked chunks: the next chunk's slot loads while this one finishes
             u4 pk[4], pn[4];
@@ -1125,14 +1183,16 @@ gla_fused_kernel(FusedArgs a)
                 }
                 qs[0] = __builtin_bit_cast(h8, pk[2]);
                 qs[1] = __builtin_bit_cast(h8, pk[3]);
-                if (j > 0) {
+                u4 z[2];
+                if (a.gate) load_gate(a, b, h, (c_first + c) * kC, w, lane, z);
+                if (has_in) {
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                         for (int jt = 0; jt < 4; ++jt)
                             O[jt] = mfma(ld8(sm.ST0, 16 * jt + r, 32 * hh + 8 * g), qs[hh], O[jt]);
                 }
-                store_out(sm, a, b, h, (c_first + c) * kC, w, lane, O);
+                store_out(sm, a, b, h, (c_first + c) * kC, w, lane, O, z);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) pk[k] = pn[k];
             }
@@ -1141,7 +1201,8 @@ gla_fused_kernel(FusedArgs a)
         // stream the span again from its incoming state
 #pragma unroll
         for (int n = 0; n < 4; ++n) S[n] = Sin[n];
-        if (j > 0) {
+        lds_barrier();   // the norm weight is in LDS
+        if (has_in) {
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
                 st4(sm.ST0, 16 * jt + r, 16 * w + 4 * g, pack4(S[jt], 1.f));
@@ -1155,10 +1216,12 @@ gla_fused_kernel(FusedArgs a)
 #pragma unroll
             for (int n = 0; n < 4; ++n) Oc[n] = f4{0.f, 0.f, 0.f, 0.f};
             ChunkTmp T;
+            u4 z[2];
+            if (a.gate) load_gate(a, b, h, (c_first + c) * kC, w, ln, z);
             chunk_front<true>(sm, cur, w, ln, kMaxKeep, S, c > 0, qt, T);
             load_chunk<true>(a, b, h, c + 1 < n_c ? (c_first + c + 1) * kC : a.L, w, ln, cur);
-            chunk_back(sm, a, b, h, (c_first + c) * kC, w, ln, (j > 0) || (c > 0), Oc, qt, T);
-            store_out(sm, a, b, h, (c_first + c) * kC, w, ln, Oc);
+            chunk_back(sm, a, b, h, (c_first + c) * kC, w, ln, has_in || (c > 0), Oc, qt, T);
+            store_out(sm, a, b, h, (c_first + c) * kC, w, ln, Oc, z);
         }
     }
 }
@@ -1245,6 +1308,8 @@ gla_fused_rk_kernel(FusedArgs a)
     const long long seq_slot = (long long)local_seq * a.n_spans;
     const unsigned int ep = __builtin_amdgcn_raw_buffer_load_b32(
         rsrc(a.epoch + seq_slot, 4 * a.n_spans), 4 * tid, 0, kDevScope);
+    const float nwr = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        rsrc(a.norm_w, a.gate ? 4 * kD : 0), 4 * (tid & (kD - 1)), 0, 0));
     dma_gkv(a, sk, b, h, c_first * kC, w, lane);
     u4 qn[2];
     load_q(a, b, h, c_first * kC, w, lane, qn);
@@ -1314,14 +1379,20 @@ gla_fused_rk_kernel(FusedArgs a)
     exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin);
 
     // ---- 3. outputs: O_c += Qs_c S_in -------------------------------------------
-    if (j > 0) {
+    const bool has_in = j > 0 || a.init != nullptr;
+    if (tid < kD) sm.nw[tid] = nwr;
+    if (has_in) {
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
             st4(sm.ST0, 16 * jt + r, 16 * w + 4 * g, pack4(Sin[jt], 1.f));
     }
     lds_barrier();
+    // the gate of the next chunk loads while this one finishes
+    u4 zc[2], zn[2];
+    if (a.gate) load_gate(a, b, h, c_first * kC, w, lane, zc);
 #pragma unroll
     for (int c = 0; c < SPAN; ++c) {
+        if (a.gate && c + 1 < n_c) load_gate(a, b, h, (c_first + c + 1) * kC, w, lane, zn);
         if (c < n_c) {
             const int ki = SPAN - 1 - c;
             f4 O[4];
@@ -1332,15 +1403,17 @@ gla_fused_rk_kernel(FusedArgs a)
                 O[2][e] = (float)KO[ki][1][e];
                 O[3][e] = (float)KO[ki][1][4 + e];
             }
-            if (j > 0) {
+            if (has_in) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                     for (int jt = 0; jt < 4; ++jt)
                         O[jt] = mfma(ld8(sm.ST0, 16 * jt + r, 32 * hh + 8 * g), KQ[ki][hh], O[jt]);
             }
-            store_out(sm, a, b, h, (c_first + c) * kC, w, lane, O);
+            store_out(sm, a, b, h, (c_first + c) * kC, w, lane, O, zc);
         }
+        zc[0] = zn[0];
+        zc[1] = zn[1];
     }
 }
 
@@ -1390,9 +1463,9 @@ static int device_cus()
 }
 
 // Kept spans (chunk registers, parking) are instantiated for these lengths;
-// register-kept spans for 2 .. kMaxKeep.
+// register-kept spans for 2 .. 7 (eight chunks' outputs overflow the registers).
 static bool keep_span_ok(int span) { return span == 1 || span == 2 || span == 4 || span == 8; }
-static bool rk_span_ok(int span) { return span >= 2 && span <= kMaxKeep; }
+static bool rk_span_ok(int span) { return span >= 2 && span <= 7; }
 
 static const void* pick_kernel(int span, bool keep, bool rk)
 {
@@ -1403,8 +1476,7 @@ static const void* pick_kernel(int span, bool keep, bool rk)
         case 4: return (const void*)gla_fused_rk_kernel<4>;
         case 5: return (const void*)gla_fused_rk_kernel<5>;
         case 6: return (const void*)gla_fused_rk_kernel<6>;
-        case 7: return (const void*)gla_fused_rk_kernel<7>;
-        default: return (const void*)gla_fused_rk_kernel<8>;
+        default: return (const void*)gla_fused_rk_kernel<7>;
         }
     }
     if (!keep) return (const void*)gla_fused_kernel<1, false>;
@@ -1476,7 +1548,7 @@ FusedPlan fused_plan(const Shape& s, int span_override, int rk_override)
     if (whole()) return p;
     // else the shortest register-kept span whose whole grid is resident
     // (no outputs round-trip through memory), then parked spans
-    for (int sp = 2; sp <= kMaxKeep; ++sp) {
+    for (int sp = 2; rk_span_ok(sp); ++sp) {
         fill(sp, false, true);
         if (whole()) return p;
     }
@@ -1517,10 +1589,14 @@ size_t fused_workspace_bytes(const Shape& s, const FusedPlan& p)
 }
 
 hipError_t launch_fused(const void* q, const void* k, const void* v, const void* lg,
-                        const Shape& s, const FusedPlan& p, void* out, float* final_state,
-                        void* ws, hipStream_t st)
+                        const Shape& s, const Extras& x, const FusedPlan& p, void* out,
+                        float* final_state, void* ws, hipStream_t st)
 {
     FusedArgs a;
+    a.init = x.init;
+    a.gate = (const __half*)x.gate;
+    a.norm_w = x.norm_w;
+    a.eps = x.eps;
     a.q = (const __half*)q;
     a.k = (const __half*)k;
     a.v = (const __half*)v;

@@ -97,11 +97,13 @@ generic_summary_kernel(const T* __restrict__ k, const T* __restrict__ v, const T
     if (j < s.d_k) wsD[cb * s.d_k + j] = expf(lgsum);
 }
 
-// One thread per (b, h, i, j): S_[0] = 0, S_[c+1] = d_c[i] S_[c] + U_c. U_c is
-// replaced in place by S_[c], the state entering chunk c.
+// One thread per (b, h, i, j): S_[0] = the initial state (zero when init is
+// null), S_[c+1] = d_c[i] S_[c] + U_c. U_c is replaced in place by S_[c], the
+// state entering chunk c. init may be final_state itself: each element is
+// read before it is written, by the same thread.
 __global__ void __launch_bounds__(256)
 generic_scan_kernel(Shape s, float* __restrict__ wsU, const float* __restrict__ wsD,
-                    float* __restrict__ final_state, size_t total)
+                    const float* init, float* final_state, size_t total)
 {
     const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= total) return;
@@ -109,7 +111,7 @@ generic_scan_kernel(Shape s, float* __restrict__ wsU, const float* __restrict__ 
     const size_t bh = e / dkdv;
     const size_t ij = e - bh * dkdv;
     const int i = (int)(ij / s.d_v);
-    float S = 0.f;
+    float S = init ? init[e] : 0.f;
     for (int c = 0; c < s.n_chunks; ++c) {
         const size_t cb = bh * s.n_chunks + c;
         float* u = wsU + cb * dkdv + ij;
@@ -164,6 +166,31 @@ generic_output_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     }
 }
 
+// Output epilogue in place on out: one wave per (b, p, h) row of d_v outputs,
+// y = o / sqrt(mean(o^2) + eps) * w * SiLU(z).
+template <typename T>
+__global__ void __launch_bounds__(256)
+generic_gate_kernel(T* __restrict__ out, const T* __restrict__ gate, const float* __restrict__ w,
+                    float eps, int d_v, size_t rows)
+{
+    const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    T* o = out + row * d_v;
+    const T* z = gate + row * d_v;
+    float ss = 0.f;
+    for (int j = lane; j < d_v; j += 64) {
+        const float x = to_f32(o[j]);
+        ss += x * x;
+    }
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    const float f = rsqrtf(ss / (float)d_v + eps);
+    for (int j = lane; j < d_v; j += 64) {
+        const float zz = to_f32(z[j]);
+        o[j] = from_f32<T>(to_f32(o[j]) * f * w[j] * (zz / (1.f + expf(-zz))));
+    }
+}
+
 size_t generic_workspace_bytes(const Shape& s)
 {
     const size_t nb = (size_t)s.B * s.H * s.n_chunks;
@@ -172,7 +199,8 @@ size_t generic_workspace_bytes(const Shape& s)
 
 template <typename T, int DKMAX>
 static hipError_t launch_generic_t(const T* q, const T* k, const T* v, const T* lg, const Shape& s,
-                                   T* out, float* final_state, void* ws, hipStream_t st)
+                                   const Extras& x, T* out, float* final_state, void* ws,
+                                   hipStream_t st)
 {
     const size_t nb = (size_t)s.B * s.H * s.n_chunks;
     float* wsU = static_cast<float*>(ws);
@@ -183,30 +211,36 @@ static hipError_t launch_generic_t(const T* q, const T* k, const T* v, const T* 
                        lg, s, wsU, wsD);
     const size_t total = (size_t)s.B * s.H * s.d_k * s.d_v;
     hipLaunchKernelGGL(generic_scan_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       st, s, wsU, wsD, final_state, total);
+                       st, s, wsU, wsD, x.init, final_state, total);
     hipLaunchKernelGGL((generic_output_kernel<T, DKMAX>), dim3(grid), dim3(threads), 0, st, q, k,
                        v, lg, s, wsU, out);
+    if (x.gate) {
+        const size_t rows = (size_t)s.B * s.L * s.H;
+        hipLaunchKernelGGL((generic_gate_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                           st, out, (const T*)x.gate, x.norm_w, x.eps, s.d_v, rows);
+    }
     return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_generic_dk(const T* q, const T* k, const T* v, const T* lg,
-                                    const Shape& s, T* out, float* fs, void* ws, hipStream_t st)
+                                    const Shape& s, const Extras& x, T* out, float* fs, void* ws,
+                                    hipStream_t st)
 {
-    if (s.d_k <= 32) return launch_generic_t<T, 32>(q, k, v, lg, s, out, fs, ws, st);
-    if (s.d_k <= 64) return launch_generic_t<T, 64>(q, k, v, lg, s, out, fs, ws, st);
-    return launch_generic_t<T, 128>(q, k, v, lg, s, out, fs, ws, st);
+    if (s.d_k <= 32) return launch_generic_t<T, 32>(q, k, v, lg, s, x, out, fs, ws, st);
+    if (s.d_k <= 64) return launch_generic_t<T, 64>(q, k, v, lg, s, x, out, fs, ws, st);
+    return launch_generic_t<T, 128>(q, k, v, lg, s, x, out, fs, ws, st);
 }
 
 hipError_t launch_generic(const void* q, const void* k, const void* v, const void* lg,
-                          bool is_fp32, const Shape& s, void* out, float* final_state, void* ws,
-                          hipStream_t st)
+                          bool is_fp32, const Shape& s, const Extras& x, void* out,
+                          float* final_state, void* ws, hipStream_t st)
 {
     if (is_fp32)
         return launch_generic_dk<float>((const float*)q, (const float*)k, (const float*)v,
-                                        (const float*)lg, s, (float*)out, final_state, ws, st);
+                                        (const float*)lg, s, x, (float*)out, final_state, ws, st);
     return launch_generic_dk<__half>((const __half*)q, (const __half*)k, (const __half*)v,
-                                     (const __half*)lg, s, (__half*)out, final_state, ws, st);
+                                     (const __half*)lg, s, x, (__half*)out, final_state, ws, st);
 }
 
 }  // namespace gtrgla

@@ -11,8 +11,8 @@ namespace gtrgla {
 // Generic three-phase path (gla_generic.hip).
 size_t generic_workspace_bytes(const Shape& s);
 hipError_t launch_generic(const void* q, const void* k, const void* v, const void* lg,
-                          bool is_fp32, const Shape& s, void* out, float* final_state, void* ws,
-                          hipStream_t st);
+                          bool is_fp32, const Shape& s, const Extras& x, void* out,
+                          float* final_state, void* ws, hipStream_t st);
 
 // Fused fp16 MFMA path (gla_fused.hip).
 struct FusedPlan {
@@ -30,8 +30,8 @@ bool fused_supported(const Shape& s);
 FusedPlan fused_plan(const Shape& s, int span_override, int rk_override);
 size_t fused_workspace_bytes(const Shape& s, const FusedPlan& p);
 hipError_t launch_fused(const void* q, const void* k, const void* v, const void* lg,
-                        const Shape& s, const FusedPlan& p, void* out, float* final_state,
-                        void* ws, hipStream_t st);
+                        const Shape& s, const Extras& x, const FusedPlan& p, void* out,
+                        float* final_state, void* ws, hipStream_t st);
 
 // Zero fill by a kernel (graph-capturable); p must be 16-byte aligned.
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);

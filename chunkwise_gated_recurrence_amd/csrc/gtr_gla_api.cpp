@@ -17,6 +17,7 @@
 
 namespace {
 
+using gtrgla::Extras;
 using gtrgla::FusedPlan;
 using gtrgla::Shape;
 
@@ -99,6 +100,29 @@ int validate_pointers(const void* q, const void* k, const void* v, const void* l
         if (fs && overlaps(fs, nf, ins[i], ns[i])) return GTR_GLA_ERR_ALIAS;
     }
     if (fs && overlaps(fs, nf, out, nv)) return GTR_GLA_ERR_ALIAS;
+    return GTR_GLA_OK;
+}
+
+// The additions of gtr_gla_fwd_ex: a gate needs a weight and a finite eps >= 0;
+// no addition may overlap an output, except an initial state that is exactly
+// final_state (updated in place).
+int validate_extras(const Extras& x, const void* out, const float* fs, const Shape& s, size_t elt)
+{
+    const size_t rows = (size_t)s.B * s.L * s.H;
+    const size_t nv = rows * s.d_v * elt;
+    const size_t nf = (size_t)s.B * s.H * s.d_k * s.d_v * sizeof(float);
+    if (x.gate) {
+        if (!x.norm_w) return GTR_GLA_ERR_NULL;
+        if (!std::isfinite(x.eps) || x.eps < 0.f) return GTR_GLA_ERR_VALUE;
+        const size_t nw = (size_t)s.d_v * sizeof(float);
+        if (overlaps(x.gate, nv, out, nv) || overlaps(x.norm_w, nw, out, nv)) return GTR_GLA_ERR_ALIAS;
+        if (fs && (overlaps(x.gate, nv, fs, nf) || overlaps(x.norm_w, nw, fs, nf)))
+            return GTR_GLA_ERR_ALIAS;
+    }
+    if (x.init) {
+        if (overlaps(x.init, nf, out, nv)) return GTR_GLA_ERR_ALIAS;
+        if (fs && x.init != fs && overlaps(x.init, nf, fs, nf)) return GTR_GLA_ERR_ALIAS;
+    }
     return GTR_GLA_OK;
 }
 
@@ -203,12 +227,14 @@ int cached_workspace(size_t need, hipStream_t st, const WsLayout& layout, void**
 
 int run(const void* q, const void* k, const void* v, const void* lg, int B, int H, int gh, int gw,
         int dk, int dv, int dir, int chunk, void* out, float* fs, bool is_fp32, void* ws,
-        size_t ws_bytes, bool own_ws, hipStream_t st)
+        size_t ws_bytes, bool own_ws, hipStream_t st, const Extras& x = Extras{})
 {
     Shape s;
     int r = validate_sizes(B, H, gh, gw, dk, dv, dir, chunk, &s);
     if (r != GTR_GLA_OK) return r;
     r = validate_pointers(q, k, v, lg, out, fs, s, is_fp32 ? 4 : 2);
+    if (r != GTR_GLA_OK) return r;
+    r = validate_extras(x, out, fs, s, is_fp32 ? 4 : 2);
     if (r != GTR_GLA_OK) return r;
     const Choice c = choose(s, is_fp32, current_policy());
     const WsLayout layout = c.kernel == kFused ? WsLayout{kFused, c.plan.n_spans, c.plan.seq_batch}
@@ -222,9 +248,9 @@ int run(const void* q, const void* k, const void* v, const void* lg, int B, int 
     hipError_t e = hipSuccess;
     if (c.kernel == kFused) {
         if (!workspace_ready_for(ws, layout)) e = gtrgla::fill_zero(ws, c.ws_bytes, st);
-        if (e == hipSuccess) e = gtrgla::launch_fused(q, k, v, lg, s, c.plan, out, fs, ws, st);
+        if (e == hipSuccess) e = gtrgla::launch_fused(q, k, v, lg, s, x, c.plan, out, fs, ws, st);
     } else {
-        e = gtrgla::launch_generic(q, k, v, lg, is_fp32, s, out, fs, ws, st);
+        e = gtrgla::launch_generic(q, k, v, lg, is_fp32, s, x, out, fs, ws, st);
     }
     mark_workspace(ws, layout);
     return e == hipSuccess ? GTR_GLA_OK : GTR_GLA_ERR_HIP;
@@ -284,6 +310,21 @@ int gtr_gla_fwd_f32_ws(const float* q, const float* k, const float* v, const flo
                true, workspace, workspace_bytes, false, stream);
 }
 
+int gtr_gla_fwd_ex(const void* q, const void* k, const void* v, const void* log_gamma,
+                   const float* initial_state, const void* gate, const float* norm_weight,
+                   float norm_eps, int B, int H, int grid_h, int grid_w, int d_k, int d_v, int dir,
+                   int chunk, int is_fp32, void* out, float* final_state, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream)
+{
+    Extras x;
+    x.init = initial_state;
+    x.gate = gate;
+    x.norm_w = norm_weight;
+    x.eps = norm_eps;
+    return run(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, dir, chunk, out, final_state,
+               is_fp32 != 0, workspace, workspace_bytes, workspace == nullptr, stream, x);
+}
+
 int gtr_gla_set_policy(int policy)
 {
     if (policy < GTR_GLA_POLICY_AUTO || policy > GTR_GLA_POLICY_FUSED_ONE) return GTR_GLA_ERR_POLICY;
@@ -319,6 +360,7 @@ const char* gtr_gla_status_str(int status)
     case GTR_GLA_ERR_HIP: return "HIP runtime error";
     case GTR_GLA_ERR_ALIAS: return "an output overlaps an input or the other output";
     case GTR_GLA_ERR_POLICY: return "unknown policy";
+    case GTR_GLA_ERR_VALUE: return "invalid scalar argument (norm_eps must be finite and >= 0)";
     default: return "unknown status";
     }
 }

@@ -65,7 +65,8 @@ typedef enum {
     GTR_GLA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required          */
     GTR_GLA_ERR_HIP = 7,         /* the HIP runtime reported an error               */
     GTR_GLA_ERR_ALIAS = 8,       /* an output overlaps an input or the other output  */
-    GTR_GLA_ERR_POLICY = 9       /* unknown policy value                             */
+    GTR_GLA_ERR_POLICY = 9,      /* unknown policy value                             */
+    GTR_GLA_ERR_VALUE = 10       /* invalid scalar argument (norm_eps not finite or < 0) */
 } gtr_gla_status;
 
 /* Launch policies (the pages' length-aware scheduling: short sequences take
@@ -76,7 +77,8 @@ typedef enum {
     GTR_GLA_POLICY_GENERIC = 1,  /* three generic fp32 kernels: summaries, scan,
                                     outputs. Any supported shape, fp16 or fp32.     */
     GTR_GLA_POLICY_FUSED = 2,    /* one fp16 MFMA kernel, one workgroup per span of
-                                    chunks, decoupled look-back across spans.       */
+                                    chunks, boundary states exchanged between the
+                                    resident workgroups of a launch.                */
     GTR_GLA_POLICY_FUSED_ONE = 3 /* the fused kernel with one chunk per span        */
 } gtr_gla_policy;
 
@@ -108,6 +110,35 @@ int gtr_gla_fwd_f32(const float* q, const float* k, const float* v, const float*
  * be used by two calls that may run at the same time.
  * The _ws entry points allocate nothing and may be captured in a HIP graph.
  */
+/*
+ * gtr_gla_fwd_ex -- gtr_gla_fwd (is_fp32 = 0) or gtr_gla_fwd_f32 (is_fp32 = 1)
+ * with the two additions the pages' end-to-end operator has around the
+ * recurrence (summary page, section 方法步骤详情 step 5, specialises it to a
+ * zero initial state and fuses RMSNorm and the output gate into the output
+ * epilogue; 0539edu.com page, appendix E.3.1):
+ *   initial_state [B, H, d_k, d_v] fp32: S_0 instead of zero, e.g. the
+ *     final_state of the preceding part of a scan. NULL: zero. It may be the
+ *     very pointer passed as final_state (then updated in place); any other
+ *     overlap with an output is GTR_GLA_ERR_ALIAS.
+ *   gate [B, L, H, d_v] (fp16, or fp32 when is_fp32), norm_weight [d_v] fp32,
+ *     norm_eps: out = o / sqrt(mean_j o_j^2 + norm_eps) * norm_weight *
+ *     SiLU(gate), SiLU(z) = z / (1 + e^-z), the mean taken over the d_v
+ *     outputs o of one (batch, token, head). norm_weight is shared by the
+ *     heads. gate NULL: out = o, and norm_weight and norm_eps are ignored.
+ *     With a gate, norm_weight must not be NULL (GTR_GLA_ERR_NULL) and
+ *     norm_eps must be finite and >= 0 (GTR_GLA_ERR_VALUE).
+ *   final_state is the state after the last step, before the epilogue (which
+ *     touches only out).
+ * workspace NULL: the library's own workspace, as gtr_gla_fwd. Otherwise a
+ * caller-managed one, as gtr_gla_fwd_ws (size from gtr_gla_workspace_bytes,
+ * which does not depend on the additions).
+ */
+int gtr_gla_fwd_ex(const void* q, const void* k, const void* v, const void* log_gamma,
+                   const float* initial_state, const void* gate, const float* norm_weight,
+                   float norm_eps, int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                   int dir, int chunk, int is_fp32, void* out, float* final_state,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v,
                                int chunk, int is_fp32);
 int gtr_gla_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -127,3 +127,36 @@ def test_status_strings(lib):
         seen.add(txt)
     assert len(seen) == 10
     assert lib.gtr_gla_status_str(99).decode() == "unknown status"
+
+
+def _fwd_ex(lib, ptrs, init=None, gate=None, nw=None, eps=1e-5, B=1, H=2, gh=4, gw=4, dk=64,
+            dv=64, f32=0, fs="auto"):
+    q, k, v, g, o, f = ptrs
+    if fs != "auto":
+        f = fs
+    return lib.gtr_gla_fwd_ex(q, k, v, g, init, gate, nw, eps, B, H, gh, gw, dk, dv, 0, 64, f32,
+                              o, f, None, 0, None)
+
+
+def test_fwd_ex_checks_its_additions(lib):
+    """gtr_gla_fwd_ex: a gate needs a weight and a finite eps >= 0; an addition may not
+    overlap an output, except an initial state that is the final state itself."""
+    far = BASE + 10 * SEP
+    # a gate without a weight
+    assert _fwd_ex(lib, PTRS, gate=far) == gla.ERR_NULL
+    # eps must be finite and >= 0
+    for eps in (-1e-3, float("nan"), float("inf")):
+        assert _fwd_ex(lib, PTRS, gate=far, nw=far + SEP, eps=eps) == gla.ERR_VALUE
+    # the additions must not overlap the outputs
+    out, fs = PTRS[4], PTRS[5]
+    assert _fwd_ex(lib, PTRS, gate=out + 64, nw=far) == gla.ERR_ALIAS
+    assert _fwd_ex(lib, PTRS, gate=far, nw=out) == gla.ERR_ALIAS
+    assert _fwd_ex(lib, PTRS, gate=far, nw=fs + 8) == gla.ERR_ALIAS
+    assert _fwd_ex(lib, PTRS, init=out + 16) == gla.ERR_ALIAS
+    assert _fwd_ex(lib, PTRS, init=fs + 16) == gla.ERR_ALIAS
+    # the base checks still apply first
+    assert _fwd_ex(lib, PTRS, gate=far, nw=far + SEP, B=0) == gla.ERR_SHAPE
+    ptrs = list(PTRS)
+    ptrs[0] = None
+    assert _fwd_ex(lib, ptrs, init=far) == gla.ERR_NULL
+    assert "norm_eps" in gla.gtr_gla_status_str(gla.ERR_VALUE)
