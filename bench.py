@@ -40,11 +40,28 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 DIRS = (0, 1, 2, 3)
 
 
-def alg_bytes(w) -> int:
-    """Bytes the method must move per call: read q, k, v, log_gamma, write o and final_state."""
+def alg_bytes(w, gate: bool = False, init: bool = False) -> int:
+    """Bytes the method must move per call: read q, k, v, log_gamma, write o and final_state
+    (with the output gate also read the gate and the norm weight; with an initial state
+    also read that)."""
     s = 2 if w.dtype == "fp16" else 4
     rows = w.B * w.L * w.H
-    return rows * (3 * w.d_k + 2 * w.d_v) * s + w.B * w.H * w.d_k * w.d_v * 4
+    n = rows * (3 * w.d_k + 2 * w.d_v) * s + w.B * w.H * w.d_k * w.d_v * 4
+    if gate:
+        n += rows * w.d_v * s + w.d_v * 4
+    if init:
+        n += w.B * w.H * w.d_k * w.d_v * 4
+    return n
+
+
+def split_name(name: str):
+    """'long2048+gate+init' -> ('long2048', gate, init)."""
+    parts = name.split("+")
+    extra = set(parts[1:])
+    bad = extra - {"gate", "init"}
+    if bad:
+        raise ValueError(f"unknown workload variant {sorted(bad)}")
+    return parts[0], "gate" in extra, "init" in extra
 
 
 def mfma_flops(w) -> int:
@@ -81,12 +98,15 @@ def measured_traffic(workload: str):
         return None
 
 
-def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = True):
+def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = True,
+                 gate: bool = False, init: bool = False):
     """Time `steps` steps of the workload. A step is four calls (the four scan
     orders), each on its own input set; the sets rotate over >= 512 MiB. The
     steps are captured into HIP graphs (one graph per four sets) and replayed,
     so the timed region holds the kernels back to back, as the pages measure
-    their operator (under CUDA Graph); --no-graph times direct calls."""
+    their operator (under CUDA Graph); --no-graph times direct calls. gate /
+    init: calls through gtr_gla_fwd_ex with the RMSNorm + SiLU output gate and /
+    or an initial state (each set has its own)."""
     import numpy as np
     import torch
 
@@ -94,13 +114,21 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
     import gla_synth
 
     arrays = gla_synth.generate(w)
-    per_call = alg_bytes(w)
+    per_call = alg_bytes(w, gate, init)
     nsets = len(DIRS)
     if rotate:
         nsets = max(nsets, math.ceil(ROTATE_BYTES / per_call))
         nsets = (nsets + len(DIRS) - 1) // len(DIRS) * len(DIRS)
     dev = torch.device("cuda:0")
     base = [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in arrays]
+    rng = np.random.default_rng(w.seed + 1000)
+    if gate:
+        base.append(torch.from_numpy(rng.standard_normal((w.B, w.L, w.H, w.d_v)).astype(
+            arrays[0].dtype)).to(dev))
+    if init:
+        base.append(torch.from_numpy(0.5 * rng.standard_normal(
+            (w.B, w.H, w.d_k, w.d_v)).astype(np.float32)).to(dev))
+    norm_w = torch.from_numpy(rng.uniform(0.5, 1.5, w.d_v).astype(np.float32)).to(dev)
     sets = []
     for i in range(nsets):
         ins = base if i == 0 else [t.clone() for t in base]
@@ -115,9 +143,17 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
     fn = gla.gtr_gla_fwd_f32_ws if is_fp32 else gla.gtr_gla_fwd_ws
 
     def call(i, d):
-        (q, k, v, lg), out, fs = sets[i % nsets]
-        fn(q, k, v, lg, w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, d, w.chunk, out, fs, ws,
-           ws.numel())
+        ins, out, fs = sets[i % nsets]
+        q, k, v, lg = ins[:4]
+        if gate or init:
+            z = ins[4] if gate else None
+            s0 = ins[-1] if init else None
+            gla.gtr_gla_fwd_ex(q, k, v, lg, s0, z, norm_w if gate else None, 1e-5, w.B, w.H,
+                               w.grid_h, w.grid_w, w.d_k, w.d_v, d, w.chunk, int(is_fp32), out,
+                               fs, ws, ws.numel())
+        else:
+            fn(q, k, v, lg, w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, d, w.chunk, out, fs, ws,
+               ws.numel())
 
     n_groups = nsets // len(DIRS)
     for d in DIRS:   # eager calls first: plan caches, kernel attributes
@@ -202,8 +238,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="img640")
-    ap.add_argument("--secondary", default="img1024,long2048,batched640",
-                    help="comma-separated extra workloads reported beside the main one")
+    ap.add_argument("--secondary", default="img1024,long2048,batched640,img640+gate,long2048+gate",
+                    help="comma-separated extra workloads reported beside the main one "
+                         "(NAME+gate: with the RMSNorm + SiLU output gate; NAME+init: from an "
+                         "initial state)")
     ap.add_argument("--warm", action="store_true", help="reuse one input set (cache-warm)")
     ap.add_argument("--no-graph", action="store_true", help="time direct calls, not graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -240,9 +278,10 @@ def main() -> int:
     traffic = measured_traffic(w.name)
     secondary = []
     for name in [s for s in args.secondary.split(",") if s and s != w.name]:
-        ws = gla_synth.WORKLOADS[name]
+        base_name, with_gate, with_init = split_name(name)
+        ws = gla_synth.WORKLOADS[base_name]
         rs = run_workload(ws, max(20, args.steps // 4), args.warmup, rotate=not args.warm,
-                          use_graph=graph)
+                          use_graph=graph, gate=with_gate, init=with_init)
         gbs = rs["alg_bytes_per_call"] / (rs["call_us_mean"] * 1e-6) / 1e9
         secondary.append({
             "workload": name, "tokens_per_s": rs["tokens_per_s"], "ms_per_step": rs["ms_per_step"],
