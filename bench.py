@@ -74,6 +74,8 @@ def kernel_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "chunkwise_gated_recurrence_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f == "stream_ceiling.hip":   # the benchmark's own kernel, not the operator's
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -98,8 +100,21 @@ def measured_traffic(workload: str):
         return None
 
 
+def rotation_groups(per_call: int, steps: int, rotate: bool) -> int:
+    """Input sets per scan order: enough that the sets span >= ROTATE_BYTES, and a
+    divisor of `steps` (so that whole replays of one graph over every set time exactly
+    `steps` steps) when `steps` allows that (else `steps` itself)."""
+    if not rotate:
+        return 1
+    need = math.ceil(ROTATE_BYTES / (per_call * len(DIRS)))
+    for g in range(need, steps + 1):
+        if steps % g == 0:
+            return g
+    return max(1, steps)
+
+
 def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = True,
-                 gate: bool = False, init: bool = False):
+                 gate: bool = False, init: bool = False, per_dir: bool = False):
     """Time `steps` steps of the workload. A step is four calls (the four scan
     orders), each on its own input set; the sets rotate over >= 512 MiB. The
     steps are captured into HIP graphs (one graph per four sets) and replayed,
@@ -115,10 +130,7 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
 
     arrays = gla_synth.generate(w)
     per_call = alg_bytes(w, gate, init)
-    nsets = len(DIRS)
-    if rotate:
-        nsets = max(nsets, math.ceil(ROTATE_BYTES / per_call))
-        nsets = (nsets + len(DIRS) - 1) // len(DIRS) * len(DIRS)
+    nsets = len(DIRS) * rotation_groups(per_call, steps, rotate)
     dev = torch.device("cuda:0")
     base = [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in arrays]
     rng = np.random.default_rng(w.seed + 1000)
@@ -160,35 +172,57 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
         call(d, d)
     torch.cuda.synchronize()
     if use_graph:
-        graphs = []
-        for g in range(n_groups):
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
+        # one graph holds n_groups consecutive steps over every input set, as a model's
+        # forward graph holds its blocks back to back; a replay runs n_groups steps
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for g in range(n_groups):
                 for d in DIRS:
                     call(len(DIRS) * g + d, d)
-            graphs.append(graph)
         torch.cuda.synchronize()
 
-        def step(n):
-            graphs[n % n_groups].replay()
+        def run_steps(first, count):
+            assert first % n_groups == 0 and count % n_groups == 0
+            for _ in range(count // n_groups):
+                graph.replay()
     else:
-        def step(n):
-            for d in DIRS:
-                call(len(DIRS) * (n % n_groups) + d, d)
+        def run_steps(first, count):
+            for n in range(first, first + count):
+                for d in DIRS:
+                    call(len(DIRS) * (n % n_groups) + d, d)
 
-    for n in range(warmup):
-        step(n)
+    warm = (warmup + n_groups - 1) // n_groups * n_groups if use_graph else warmup
+    run_steps(0, warm)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for n in range(steps):
-        step(warmup + n)
+    run_steps(warm, steps)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     ncalls = steps * len(DIRS)
+    dir_us = None
+    if per_dir and use_graph:
+        # each scan order on its own: graphs of one direction's calls over the rotating sets
+        dir_us = {}
+        reps = max(5, steps // 8)
+        for d in DIRS:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(nsets):
+                    call(i, d)
+            graph.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            dir_us[("l2r", "r2l", "t2b", "b2t")[d]] = 1e3 * e0.elapsed_time(e1) / (reps * nsets)
     kern, span, grid = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, w.chunk,
                                         int(is_fp32))
     return {
@@ -202,7 +236,57 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
         "kernel": {1: "generic", 2: "fused", 3: "fused-rk"}.get(kern, str(kern)),
         "span": span,
         "grid": grid,
+        "per_dir_us": dir_us,
     }
+
+
+def run_ceiling(w, steps: int, warmup: int):
+    """Practical ceiling: a plain streaming kernel (libgtrgla_ceiling.so) that reads four
+    fp16 tensors and writes one, each of the workload's [B, L, H, 64] size, i.e. the
+    operator's q, k, v, log_gamma and out bytes, timed like the operator (four calls per
+    step, graph replay, sets rotated over >= 512 MiB). Returns microseconds per call."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "chunkwise_gated_recurrence_amd", "libgtrgla_ceiling.so")
+    lib = ctypes.CDLL(path)
+    lib.gtr_stream_ceiling.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_int,
+                                                                ctypes.c_void_p]
+    lib.gtr_stream_ceiling.restype = ctypes.c_int
+    n = w.B * w.L * w.H * w.d_v
+    per_call = 5 * n * 2
+    n_groups = rotation_groups(per_call, steps, True)
+    nsets = len(DIRS) * n_groups
+    dev = torch.device("cuda:0")
+    sets = [[torch.full((n,), 0.01 * (i + 1), dtype=torch.float16, device=dev) for i in range(5)]
+            for _ in range(nsets)]
+    blocks = max(1, min((n // 8 + 255) // 256, 2048))
+
+    def call(i):
+        a, b, c, d, o = sets[i % nsets]
+        r = lib.gtr_stream_ceiling(a.data_ptr(), b.data_ptr(), c.data_ptr(), d.data_ptr(),
+                                   o.data_ptr(), n, blocks, torch.cuda.current_stream().cuda_stream)
+        if r != 0:
+            raise RuntimeError(f"gtr_stream_ceiling failed ({r})")
+
+    for i in range(len(DIRS)):
+        call(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(nsets):
+            call(i)
+    for _ in range(max(1, warmup // n_groups)):
+        graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps // n_groups):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * t0.elapsed_time(t1) / ((steps // n_groups) * nsets)
 
 
 def cpu_baseline(w, budget_s: float):
@@ -273,7 +357,8 @@ def main() -> int:
 
     w = gla_synth.WORKLOADS[args.workload]
     graph = not args.no_graph
-    r = run_workload(w, args.steps, args.warmup, rotate=not args.warm, use_graph=graph)
+    r = run_workload(w, args.steps, args.warmup, rotate=not args.warm, use_graph=graph,
+                     per_dir=True)
     achieved = r["alg_bytes_per_call"] / (r["call_us_mean"] * 1e-6) / 1e9
     traffic = measured_traffic(w.name)
     secondary = []
@@ -283,14 +368,25 @@ def main() -> int:
         rs = run_workload(ws, max(20, args.steps // 4), args.warmup, rotate=not args.warm,
                           use_graph=graph, gate=with_gate, init=with_init)
         gbs = rs["alg_bytes_per_call"] / (rs["call_us_mean"] * 1e-6) / 1e9
+        ceil_us = run_ceiling(ws, max(20, args.steps // 4), args.warmup) if not (
+            with_gate or with_init) else None
         secondary.append({
             "workload": name, "tokens_per_s": rs["tokens_per_s"], "ms_per_step": rs["ms_per_step"],
+            "ceiling_us": ceil_us,
             "call_us_mean": rs["call_us_mean"], "achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "mfma_frac": mfma_flops(ws) / (rs["call_us_mean"] * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
             "kernel": rs["kernel"], "span": rs["span"], "grid": rs["grid"],
             "traffic": measured_traffic(name),
         })
 
+    ceil_us = run_ceiling(w, max(20, args.steps // 4), args.warmup)
+    ceiling = {
+        "kind": "plain streaming kernel: read 4 fp16 tensors, write 1 (the operator's q, k, v, "
+                "log_gamma, out bytes), same timing",
+        "us_per_call": ceil_us,
+        "GBs": 5 * w.B * w.L * w.H * w.d_v * 2 / (ceil_us * 1e-6) / 1e9,
+        "operator_over_ceiling": r["call_us_mean"] / ceil_us,
+    }
     line = {
         "metric": "key-only GLA fwd tokens/s at 1.6K & 16.4K tokens; % of HBM/MFMA roofline",
         "value": r["tokens_per_s"],
@@ -323,8 +419,10 @@ def main() -> int:
                 r["kernel"], "generic (3 kernels)"),
             "alg_bytes_per_launch": r["alg_bytes_per_call"],
             "launch_us_mean": r["call_us_mean"],
+            "launch_us_per_dir": r["per_dir_us"],
             "mfma_frac": mfma_flops(w) / (r["call_us_mean"] * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
         },
+        "ceiling": ceiling,
         "secondary": secondary,
         "kernel_hash": kernel_hash(),
     }

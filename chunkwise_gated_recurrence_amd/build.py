@@ -3,7 +3,8 @@
     python -m chunkwise_gated_recurrence_amd.build [-v]
 
 Objects go to chunkwise_gated_recurrence_amd/_build/, the library to
-chunkwise_gated_recurrence_amd/libgtrgla.so. Every call recompiles.
+chunkwise_gated_recurrence_amd/libgtrgla.so, and the benchmark's streaming
+ceiling kernel to libgtrgla_ceiling.so. Every call recompiles.
 """
 from __future__ import annotations
 
@@ -19,6 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libgtrgla.so")
+CEILING_PATH = os.path.join(PKG, "libgtrgla_ceiling.so")
 ARCH = "gfx950"
 
 SOURCES = ["gla_generic.hip", "gla_fused.hip", "gtr_gla_api.cpp"]
@@ -70,6 +72,13 @@ def build(verbose: bool = False, extra_flags: List[str] | None = None) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
     os.replace(tmp, LIB_PATH)
+    # the benchmark's streaming ceiling, a library of its own
+    tmp = CEILING_PATH + ".tmp"
+    cmd = [cc, "-shared", os.path.join(CSRC, "stream_ceiling.hip"), "-o", tmp] + flags
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, CEILING_PATH)
     return LIB_PATH
 
 
