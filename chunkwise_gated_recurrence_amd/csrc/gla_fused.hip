@@ -844,39 +844,109 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
         unsigned int* fin = ubuf + ow;                                // final state of the slice
         const int lq = lo - 2;                         // log2 of 16 B pieces per span
         const int nl = ow >> 2;
+        // Fold, one state element per thread: the slice's E = 2^lo elements,
+        // with P = 256 / E contiguous span ranges per element (combined through
+        // LDS) when E < 256, else E / 256 elements per thread in turn. Words are
+        // checked for their tag as the fold reads them; any stale word sends
+        // the owner back to poll. The incoming states overwrite the U words in
+        // place (tagged); the final state goes to fin.
+        const int lT = lo < 8 ? 8 - lo : 0;            // log2 P
+        const int P = 1 << lT;
+        const int per = (ns + P - 1) >> lT;            // spans per range
+        const int lW = lo < 8 ? lo : 8;                // log2 elements per pass
+        const int ei = tid & ((1 << lW) - 1), p = tid >> lW;
+        const int m_lo = min(p * per, ns), m_hi = min(m_lo + per, ns);
+        const int n_pass = 1 << (lo - lW);
+        float* compA = reinterpret_cast<float*>(scr + kScanD + 2048);   // [256]
+        float* compB = reinterpret_cast<float*>(scr + kScanD + 3072);   // [256]
+        // the initial state's slice is staged in fin by the loader waves (a
+        // global load here would make the storer waves wait for their stores)
+        const float* finf = reinterpret_cast<const float*>(fin);
+        // the decays of every (span, row) of the slice, tag-checked and decoded
+        // once into LDS floats (dfl), so that the fold reads plain values
+        float* dfl = reinterpret_cast<float*>(scr + kScanD + 4096);   // [ns << lrows] <= 128
+        const int nd = ns << lrows;
+        // fold spans [m0, m1) of element e from `run` (writes S_in words when put)
+        auto fold = [&](int e, int m0, int m1, float& A, float& run, bool put, bool& ok) {
+            const int su = 1 << lo, sd = 1 << lrows;
+            unsigned int* pu = ubuf + (m0 << lo) + e;
+            const float* pd = dfl + (m0 << lrows) + (e >> 6);
+            const unsigned int* pt = sm.tags + m0;
+            int m = m0;
+            for (; m + 4 <= m1; m += 4) {
+                unsigned int xu[4], tg[4];
+                float d[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    xu[k] = pu[k * su];
+                    d[k] = pd[k * sd];
+                    tg[k] = pt[k];
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    ok &= ll_ok(xu[k], tg[k]);
+                    if (put) pu[k * su] = ll_word(run, tg[k]);
+                    A *= d[k];
+                    run = d[k] * run + ll_value(xu[k]);
+                }
+                pu += 4 * su;
+                pd += 4 * sd;
+                pt += 4;
+            }
+            for (; m < m1; ++m) {
+                const unsigned int xu = *pu, tg = *pt;
+                const float d = *pd;
+                ok &= ll_ok(xu, tg);
+                if (put) *pu = ll_word(run, tg);
+                A *= d;
+                run = d * run + ll_value(xu);
+                pu += su;
+                pd += sd;
+                ++pt;
+            }
+        };
+        float run0 = 0.f;   // ranged fold: the initial state of my element
         for (unsigned int polls = 0;; ++polls) {
-            bool ok = true;
             if (w < 2) {   // loader waves
                 for (int k0 = 64 * w; k0 < nl; k0 += 128) {
                     if (k0 + lane < nl)
                         __builtin_amdgcn_global_load_lds(src + 4 * (k0 + lane), ubuf + 4 * k0, 16, 0,
                                                          kDevScope);
                 }
+                if (a.init) {   // every poll: a stale pass has overwritten fin
+                    const float* isrc = a.init + (long long)seq * (kD * kD) + e_first;
+                    for (int k0 = 64 * w; k0 < (1 << lq); k0 += 128) {
+                        if (k0 + lane < (1 << lq))
+                            __builtin_amdgcn_global_load_lds(isrc + 4 * (k0 + lane), fin + 4 * k0,
+                                                             16, 0, 0);
+                    }
+                }
                 __builtin_amdgcn_s_waitcnt(0x0F70);
             }
             if (tid == 0) sm.stale = 0;
+            bool ok = true;
             lds_barrier();
-            {
-                // U pieces (four words of one span each), every LDS read issued
-                // before the first compare; then the D words, one per thread
-                const int nu = ns << lq;                // <= 2048 pieces
-                u4 xs[8];
-                unsigned int tg[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int q = min(tid + kThreads * i, nu - 1);
-                    xs[i] = *reinterpret_cast<const u4*>(ubuf + 4 * q);
-                    tg[i] = sm.tags[q >> lq];
+            if (tid < nd) {
+                const unsigned int x = ubuf[(ns << lo) + tid];
+                ok &= ll_ok(x, sm.tags[tid >> lrows]);
+                dfl[tid] = ll_value(x);
+            }
+            lds_barrier();
+            if (P == 1) {
+                // the whole fold in one pass, from the initial state
+                for (int ps = 0; ps < n_pass; ++ps) {
+                    const int e = (ps << 8) + tid;
+                    float A = 1.f, run = a.init ? finf[e] : 0.f;
+                    fold(e, 0, ns, A, run, true, ok);
+                    reinterpret_cast<float*>(fin)[e] = run;
                 }
-                const int nd = ns << lrows;              // <= 128 words
-                const int wd = min(tid, nd - 1);
-                const unsigned int xd = ubuf[(ns << lo) + wd];
-                const unsigned int td = sm.tags[wd >> lrows];
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    ok &= ll_ok(xs[i][0], tg[i]) & ll_ok(xs[i][1], tg[i]) & ll_ok(xs[i][2], tg[i]) &
-                          ll_ok(xs[i][3], tg[i]);
-                ok &= ll_ok(xd, td);
+            } else {
+                // my range's product of decays and fold from zero
+                float A = 1.f, run = 0.f;
+                fold(ei, m_lo, m_hi, A, run, false, ok);
+                compA[tid] = A;
+                compB[tid] = run;
+                run0 = a.init ? finf[ei] : 0.f;
             }
             if (!__all(ok) && lane == 0) sm.stale = 1;
             lds_barrier();
@@ -889,99 +959,22 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
             lds_barrier();   // every thread has read the flag before it is reset
             __builtin_amdgcn_s_sleep(2);
         }
-        // Fold, four elements (one 16 B word group, same state row, so one
-        // decay) per thread: P = 256 / Qn contiguous span ranges per group,
-        // Qn = min(slice / 4, 256) groups at a time; LDS combines the ranges.
-        // The incoming states overwrite the U words in place (tagged); the
-        // final state goes to fin.
-        {
-            const int lQ = lo - 2;
-            const int lQn = lQ < 8 ? lQ : 8;
-            const int Qn = 1 << lQn;
-            const int P = kThreads >> lQn;
-            const int per = (ns + P - 1) / P;
-            const int qi0 = tid & (Qn - 1), p = tid >> lQn;
-            const int m_lo = min(p * per, ns), m_hi = min(m_lo + per, ns);
-            float* compA = reinterpret_cast<float*>(scr + kScanD + 2048);   // [256]
-            f4* compB = reinterpret_cast<f4*>(scr + kScanD + 3072);        // [256]
-            for (int g0 = 0; g0 < (1 << lQ); g0 += Qn) {
-                const int el = 4 * (g0 + qi0);
-                const float* drow = dbuf + (el >> 6);
-                const unsigned int* ucol = ubuf + el;
-                // spans in blocks of 4, every LDS read of a block issued first
-                float A = 1.f;
-                f4 Bv = {0.f, 0.f, 0.f, 0.f};
-                for (int m0 = m_lo; m0 < m_hi; m0 += 4) {
-                    u4 xb[4];
-                    float db[4];
+        if (P > 1) {
+            // the ranges before mine (at most three), from the initial state;
+            // then my range again, writing the incoming states
+            float run = run0;
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int m = min(m0 + k, m_hi - 1);
-                        xb[k] = *reinterpret_cast<const u4*>(ucol + (m << lo));
-                        db[k] = drow[m << lrows];
-                    }
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const float d = m0 + k < m_hi ? db[k] : 1.f;
-                        const float z = m0 + k < m_hi ? 1.f : 0.f;
-                        A *= d;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) Bv[e] = d * Bv[e] + z * ll_value(xb[k][e]);
-                    }
+            for (int pp = 0; pp < 3; ++pp) {
+                if (pp < p) {
+                    const float ca = compA[(pp << lW) + ei], cb = compB[(pp << lW) + ei];
+                    run = ca * run + cb;
                 }
-                compA[tid] = A;
-                compB[tid] = Bv;
-                lds_barrier();
-                // the ranges before mine, four at a time (reads first), from
-                // the initial state
-                f4 run = {0.f, 0.f, 0.f, 0.f};
-                if (a.init)
-                    run = *reinterpret_cast<const f4*>(a.init + (long long)seq * (kD * kD) +
-                                                       e_first + el);
-                for (int pp0 = 0; pp0 < p; pp0 += 4) {
-                    float ca[4];
-                    f4 cb[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int pp = min(pp0 + i, p - 1);
-                        ca[i] = compA[pp * Qn + qi0];
-                        cb[i] = compB[pp * Qn + qi0];
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if (pp0 + i < p) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) run[e] = ca[i] * run[e] + cb[i][e];
-                        }
-                    }
-                }
-                for (int m0 = m_lo; m0 < m_hi; m0 += 4) {
-                    u4 xb[4];
-                    float db[4];
-                    unsigned int tb[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int m = min(m0 + k, m_hi - 1);
-                        xb[k] = *reinterpret_cast<const u4*>(ucol + (m << lo));
-                        db[k] = drow[m << lrows];
-                        tb[k] = sm.tags[m];
-                    }
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        if (m0 + k < m_hi) {
-                            u4 y;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                y[e] = ll_word(run[e], tb[k]);
-                                run[e] = db[k] * run[e] + ll_value(xb[k][e]);
-                            }
-                            *reinterpret_cast<u4*>(ubuf + el + ((m0 + k) << lo)) = y;
-                        }
-                    }
-                }
-                if (p == P - 1) *reinterpret_cast<f4*>(fin + el) = run;
-                lds_barrier();   // comp reusable; rows complete
             }
+            float A = 1.f;
+            bool ok = true;
+            fold(ei, m_lo, m_hi, A, run, true, ok);
+            if (p == P - 1) reinterpret_cast<float*>(fin)[ei] = run;
+            lds_barrier();   // rows complete
         }
         // storer waves: rows 0..ns-1 to the incoming-state slots, fin to
         // final_state (a null final_state gives an empty resource: dropped)
