@@ -322,7 +322,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="img640")
-    ap.add_argument("--secondary", default="img1024,long2048,batched640,img640+gate,long2048+gate",
+    ap.add_argument("--secondary",
+                    default="img1024,long2048,batched640,img640_dk32,img640+gate,long2048+gate",
                     help="comma-separated extra workloads reported beside the main one "
                          "(NAME+gate: with the RMSNorm + SiLU output gate; NAME+init: from an "
                          "initial state)")

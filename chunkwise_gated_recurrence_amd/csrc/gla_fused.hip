@@ -212,6 +212,7 @@ struct FusedArgs {
     int n_spans;                // workgroups per sequence
     int seq0;                   // first sequence of this launch
     int slice_log2;             // log2 of the state elements each owner scans
+    int dk;                     // key dim of q, k, log_gamma: 64, or 32 (zero-padded to 64 on load)
     float scale;
     const float* init;          // [B, H, 64, 64] states before the first step, or null (zero)
     const __half* gate;         // [B, L, H, 64] output gate, or null (outputs as they are)
@@ -257,17 +258,32 @@ __device__ __forceinline__ long long row_offset(const FusedArgs& a, int b, int h
     return (((long long)b * a.L + p) * a.H + h) * kD;
 }
 
-// Buffer resource over batch b of a [B, L, H, 64] fp16 tensor. Buffer loads
+// Buffer resource over batch b of a [B, L, H, d] fp16 tensor. Buffer loads
 // past num_records return zeros, so rows beyond the sequence end read as zero
 // without a branch (a branch around a load makes the compiler wait for it).
 constexpr int kNT = 0;   // cache policy of the chunk loads: default (a streaming hint measured slower)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t batch_rsrc(const __half* base, const FusedArgs& a,
-                                                             int b)
+                                                             int b, int d = kD)
 {
-    const long long per_batch = (long long)a.L * a.H * kD;
+    const long long per_batch = (long long)a.L * a.H * d;
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + b * per_batch), (short)0,
                                              (int)(per_batch * 2), 0x00020000);
+}
+
+// Byte offsets of 16-byte block blk (dims 8 blk .. 8 blk + 7) of scan step t of
+// head h: key side (q, k, log_gamma: rows of dk halves; blocks past dk read
+// zeros, so a 32-wide key dim is zero-padded to 64) and value side (v: rows of
+// 64 halves). Past the sequence end both read zeros.
+struct RowOff {
+    int key, val;
+};
+__device__ __forceinline__ RowOff row_off(const FusedArgs& a, int h, int t, int blk)
+{
+    const int kbytes = a.L * a.H * a.dk * 2, vbytes = a.L * a.H * kD * 2;
+    if (t >= a.L) return RowOff{kbytes, vbytes};
+    const int ph = scan_to_spatial(t, a.L, a.grid_h, a.grid_w, a.dir) * a.H + h;
+    return RowOff{8 * blk < a.dk ? ph * (a.dk * 2) + 16 * blk : kbytes, ph * (kD * 2) + 16 * blk};
 }
 
 __device__ __forceinline__ u4 load16(__amdgpu_buffer_rsrc_t rs, int voff)
@@ -281,18 +297,15 @@ __device__ __forceinline__ void load_chunk(const FusedArgs& a, int b, int h, int
                                            int lane, ChunkRegs& R)
 {
     const int t = t0 + 16 * w + (lane & 15);
-    const int bytes = a.L * a.H * kD * 2;
-    const int voff = t < a.L
-        ? (scan_to_spatial(t, a.L, a.grid_h, a.grid_w, a.dir) * a.H + h) * (kD * 2) + 16 * (lane >> 4)
-        : bytes;
-    const __amdgpu_buffer_rsrc_t rk = batch_rsrc(a.k, a, b), rv = batch_rsrc(a.v, a, b),
-                                 rg = batch_rsrc(a.lg, a, b);
+    const __amdgpu_buffer_rsrc_t rk = batch_rsrc(a.k, a, b, a.dk), rv = batch_rsrc(a.v, a, b),
+                                 rg = batch_rsrc(a.lg, a, b, a.dk);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-        if (WITH_Q) R.q[hh] = load16(batch_rsrc(a.q, a, b), voff + 64 * hh);
-        R.k[hh] = load16(rk, voff + 64 * hh);
-        R.v[hh] = load16(rv, voff + 64 * hh);
-        R.g[hh] = load16(rg, voff + 64 * hh);
+        const RowOff o = row_off(a, h, t, (lane >> 4) + 4 * hh);
+        if (WITH_Q) R.q[hh] = load16(batch_rsrc(a.q, a, b, a.dk), o.key);
+        R.k[hh] = load16(rk, o.key);
+        R.v[hh] = load16(rv, o.val);
+        R.g[hh] = load16(rg, o.key);
     }
 }
 
@@ -914,11 +927,14 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                                                          kDevScope);
                 }
                 if (a.init) {   // every poll: a stale pass has overwritten fin
-                    const float* isrc = a.init + (long long)seq * (kD * kD) + e_first;
+                    // dk x 64 per sequence; the padded rows read zeros
+                    const __amdgpu_buffer_rsrc_t ri =
+                        rsrc(a.init + (long long)seq * a.dk * kD, a.dk * kD * 4);
                     for (int k0 = 64 * w; k0 < (1 << lq); k0 += 128) {
                         if (k0 + lane < (1 << lq))
-                            __builtin_amdgcn_global_load_lds(isrc + 4 * (k0 + lane), fin + 4 * k0,
-                                                             16, 0, 0);
+                            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                                ri, (__attribute__((address_space(3))) void*)(fin + 4 * k0), 16,
+                                4 * (e_first + 4 * (k0 + lane)), 0, 0, 0);
                     }
                 }
                 __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -980,9 +996,11 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
         // final_state (a null final_state gives an empty resource: dropped)
         if (w >= 2) {
             const __amdgpu_buffer_rsrc_t rs = rsrc(a.sin + seq_slot * (kD * kD), ns * (kD * kD * 4));
+            // final_state holds dk x 64 per sequence: rows past dk (the zero
+            // padding of a 32-wide key dim) fall outside the resource
             const __amdgpu_buffer_rsrc_t rf =
-                rsrc(a.final_state + (a.final_state ? (long long)seq * kD * kD : 0),
-                     a.final_state ? kD * kD * 4 : 0);
+                rsrc(a.final_state + (a.final_state ? (long long)seq * a.dk * kD : 0),
+                     a.final_state ? a.dk * kD * 4 : 0);
             // U pieces (< 2048: ns << lo < 2^13 words), in batches whose LDS
             // reads are all issued before the batch's stores
             const int nu = ns << lq;
@@ -1237,24 +1255,19 @@ struct SmemRK {
 __device__ __forceinline__ void dma_gkv(const FusedArgs& a, SmemRK& sk, int b, int h, int t0, int w,
                                         int lane)
 {
-    const int bytes = a.L * a.H * kD * 2;
-    const __amdgpu_buffer_rsrc_t rg = batch_rsrc(a.lg, a, b), rk = batch_rsrc(a.k, a, b),
+    const __amdgpu_buffer_rsrc_t rg = batch_rsrc(a.lg, a, b, a.dk), rk = batch_rsrc(a.k, a, b, a.dk),
                                  rv = batch_rsrc(a.v, a, b);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int row = 16 * w + 8 * i + (lane >> 3);
-        const int t = t0 + row;
-        const int blk = (lane & 7) ^ (row & 7);
-        const int voff = t < a.L
-            ? (scan_to_spatial(t, a.L, a.grid_h, a.grid_w, a.dir) * a.H + h) * (kD * 2) + 16 * blk
-            : bytes;
+        const RowOff o = row_off(a, h, t0 + row, (lane & 7) ^ (row & 7));
         const int base = (16 * w + 8 * i) * kD;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rg, (__attribute__((address_space(3))) void*)(sk.raw[0] + base), 16, voff, 0, 0, kNT);
+            rg, (__attribute__((address_space(3))) void*)(sk.raw[0] + base), 16, o.key, 0, 0, kNT);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (__attribute__((address_space(3))) void*)(sk.raw[1] + base), 16, voff, 0, 0, kNT);
+            rk, (__attribute__((address_space(3))) void*)(sk.raw[1] + base), 16, o.key, 0, 0, kNT);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void*)(sk.raw[2] + base), 16, voff, 0, 0, kNT);
+            rv, (__attribute__((address_space(3))) void*)(sk.raw[2] + base), 16, o.val, 0, 0, kNT);
     }
 }
 
@@ -1268,13 +1281,9 @@ __device__ __forceinline__ void load_q(const FusedArgs& a, int b, int h, int t0,
                                        u4 (&q)[2])
 {
     const int t = t0 + 16 * w + (lane & 15);
-    const int bytes = a.L * a.H * kD * 2;
-    const int voff = t < a.L
-        ? (scan_to_spatial(t, a.L, a.grid_h, a.grid_w, a.dir) * a.H + h) * (kD * 2) + 16 * (lane >> 4)
-        : bytes;
-    const __amdgpu_buffer_rsrc_t rq = batch_rsrc(a.q, a, b);
+    const __amdgpu_buffer_rsrc_t rq = batch_rsrc(a.q, a, b, a.dk);
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) q[hh] = load16(rq, voff + 64 * hh);
+    for (int hh = 0; hh < 2; ++hh) q[hh] = load16(rq, row_off(a, h, t, (lane >> 4) + 4 * hh).key);
 }
 
 template <int SPAN>
@@ -1436,8 +1445,9 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t st)
 // ---------------------------------------------------------------------------
 bool fused_supported(const Shape& s)
 {
-    // buffer offsets within one batch are 32-bit
-    return s.d_k == kD && s.d_v == kD && s.chunk == kC &&
+    // d_v = 64; d_k = 64, or 32 (the pages' operator shape) zero-padded to 64
+    // in the kernel; buffer offsets within one batch are 32-bit
+    return (s.d_k == kD || s.d_k == 32) && s.d_v == kD && s.chunk == kC &&
            (long long)s.L * s.H * kD * 2 + 256 <= 0x7FFFFFFFLL;
 }
 
@@ -1612,6 +1622,7 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
     a.span = p.span;
     a.n_spans = p.n_spans;
     a.slice_log2 = p.slice_log2;
+    a.dk = s.d_k;
     a.scale = s.scale;
     if (p.keep && !p.rk && p.span >= 2 && a.park == nullptr) return hipErrorInvalidValue;
     if (p.rk && !rk_span_ok(p.span)) return hipErrorInvalidValue;

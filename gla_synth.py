@@ -65,6 +65,8 @@ WORKLOADS: Dict[str, Workload] = {
                  note="2048x2048 image, 16384 tokens, 12 heads"),
         Workload("long2048_near1", 1, 12, 128, 128, 64, 64, "fp16", 5, gate_mu=3.0,
                  note="16384 tokens with gates near 1 (long memory)"),
+        Workload("img640_dk32", 1, 6, 40, 40, 32, 64, "fp16", 6,
+                 note="640x640 image with the pages' operator head shape, d_k = 32, d_v = 64"),
     ]
 }
 

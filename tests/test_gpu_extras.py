@@ -36,6 +36,10 @@ CASES = [
     ("generic-fp16", BASE.with_(H=2, grid_h=24, grid_w=20, seed=55), gla.POLICY_GENERIC, None, None),
     ("generic-fp32", TINY.with_(d_k=64, d_v=64, grid_h=20, grid_w=21, H=2, seed=56),
      gla.POLICY_AUTO, None, None),
+    # the pages' operator shape, d_k = 32 (zero-padded to 64 inside the fused kernels)
+    ("fused-one-dk32", BASE.with_(d_k=32, H=3, seed=57), gla.POLICY_AUTO, None, None),
+    ("fused-rk-dk32", BASE.with_(d_k=32, B=2, H=2, grid_h=30, grid_w=30, seed=58),
+     gla.POLICY_FUSED, "3", "1"),
 ]
 
 

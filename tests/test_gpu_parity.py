@@ -139,6 +139,29 @@ def test_fused_register_kept(name, span):
         gla.gtr_gla_set_policy(gla.POLICY_AUTO)
 
 
+@pytest.mark.parametrize("span,rk,kernel", [(1, None, 2), (4, None, 2), (3, None, 2), (3, "1", 3)],
+                         ids=["one-chunk", "parked4", "streamed3", "rk3"])
+def test_fused_dk32(span, rk, kernel):
+    """The pages' operator shape (d_k = 32, d_v = 64) on every fused kernel family:
+    the key dim is zero-padded to 64 on load, the final state keeps its 32 rows."""
+    w = gla_synth.WORKLOADS["img640_dk32"].with_(name="dk32-30x30", B=2, H=2, grid_h=30, grid_w=30,
+                                                 seed=19)
+    arrays = gla_synth.generate(w)
+    gla.gtr_gla_set_policy(gla.POLICY_FUSED)
+    os.environ["GTR_GLA_SPAN"] = str(span)
+    if rk:
+        os.environ["GTR_GLA_RK"] = rk
+    try:
+        kern, sp, _ = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, 32, 64, 64, 0)
+        assert (kern, sp) == (kernel, span)
+        for d in DIRS:
+            check(w, arrays, d, f"fused-dk32-span{span}", key=w.name)
+    finally:
+        os.environ.pop("GTR_GLA_SPAN", None)
+        os.environ.pop("GTR_GLA_RK", None)
+        gla.gtr_gla_set_policy(gla.POLICY_AUTO)
+
+
 # --------------------------------------------------------------------------- odd shapes
 BASE16 = gla_synth.WORKLOADS["img640"]
 BASE32 = gla_synth.WORKLOADS["tiny"]
