@@ -154,8 +154,9 @@ int gtr_gla_fwd_f32_ws(const float* q, const float* k, const float* v, const flo
 /*
  * Policy control, for A/B measurement and tests. The setting is process-wide
  * and read at each call; it is not synchronised with calls running on other
- * host threads. A policy that cannot serve a call (fused with fp32 inputs or
- * with head sizes other than 64) falls back to the generic kernels, as the
+ * host threads. A policy that cannot serve a call (fused with fp32 inputs, or
+ * with d_v other than 64 or d_k other than 32 and 64) falls back to the
+ * generic kernels, as the
  * pages' specialised operator falls back to a generic implementation
  * (summary page, section 局限与改进).
  */
