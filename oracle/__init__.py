@@ -16,8 +16,10 @@ section 前置知识 › 门控线性注意力(GLA) and section 核心方法):
 
     S_t = Diag(gamma_t) S_{t-1} + k_t^T v_t,   o_t = d_k^{-1/2} q_t S_t,   S_0 = 0
 
-(``recurrent_init``: the same from a given S_0), and the output epilogue that
-the end-to-end operator fuses (0539edu.com page, appendix E.3.1; ``rmsnorm_gate``)
+(``recurrent_init``: the same from a given S_0), the data-dependent gate
+gamma_t = sigma(x_t W1 W2 + b)^{1/tau} of section 核心方法 (rank 16, tau = 16;
+``lowrank_gate`` gives log_gamma), and the output epilogue that the end-to-end
+operator fuses (0539edu.com page, appendix E.3.1; ``rmsnorm_gate``)
 
 with gamma_t = exp(log_gamma_t) per key dimension, walked along one of four
 scan orders over the patch grid (same sections; see ``scan_order``).
@@ -71,6 +73,9 @@ def _load():
         lib.gla_oracle_recurrent_init.restype = i
         lib.gla_oracle_recurrent_init.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, i, i, dp, dp,
                                                   i]
+        lib.gla_oracle_lowrank_gate.restype = i
+        lib.gla_oracle_lowrank_gate.argtypes = [dp, dp, dp, dp, ctypes.c_double, ctypes.c_long, i,
+                                                i, i, dp]
         lib.gla_oracle_rmsnorm_gate.restype = i
         lib.gla_oracle_rmsnorm_gate.argtypes = [dp, dp, dp, ctypes.c_double, ctypes.c_long, i, dp]
         lib.gla_oracle_scan_position.restype = ctypes.c_long
@@ -164,6 +169,25 @@ def recurrent_init(q, k, v, log_gamma, initial_state, grid_h: int, grid_w: int, 
     if r != 0:
         raise RuntimeError(f"gla_oracle_recurrent_init failed with status {r}")
     return out, fs
+
+
+def lowrank_gate(x, w1, w2, bias, inv_tau: float = 1.0 / 16) -> np.ndarray:
+    """log_gamma = inv_tau * logsigmoid(x W1 W2 + bias) over the last axis of x
+    ([..., C] -> [..., K]); W1 [C, R], W2 [R, K], bias [K]."""
+    lib = _load()
+    x64, a64, b64, c64 = _f64(x), _f64(w1), _f64(w2), _f64(bias)
+    C = x64.shape[-1]
+    R = a64.shape[1]
+    K = b64.shape[1]
+    if a64.shape != (C, R) or b64.shape != (R, K) or c64.shape != (K,):
+        raise ValueError("W1 must be [C, R], W2 [R, K] and bias [K]")
+    rows = x64.size // C
+    lg = np.zeros(x64.shape[:-1] + (K,), dtype=np.float64)
+    r = lib.gla_oracle_lowrank_gate(_ptr(x64), _ptr(a64), _ptr(b64), _ptr(c64), float(inv_tau),
+                                    rows, C, R, K, _ptr(lg))
+    if r != 0:
+        raise RuntimeError(f"gla_oracle_lowrank_gate failed with status {r}")
+    return lg
 
 
 def rmsnorm_gate(o, gate, weight, eps: float) -> np.ndarray:

@@ -40,6 +40,11 @@
  *                           the scan leaves; the pages' operator fixes S_0 = 0,
  *                           summary page section 方法步骤详情 step 5, so this
  *                           is the general form of that recurrence);
+ *   gla_oracle_lowrank_gate - the data-dependent gate of the summary page,
+ *                           section 核心方法: gamma_t = sigma(x_t W1 W2 + b)^{1/tau}
+ *                           with a rank-16 factorisation W1 W2 and tau = 16, so
+ *                           log_gamma = (1/tau) logsigmoid(x W1 W2 + b), per
+ *                           token, over the H * d_k key dims of all heads;
  *   gla_oracle_rmsnorm_gate - the output epilogue that the end-to-end operator
  *                           fuses (0539edu.com page, appendix E.3.1): per
  *                           (batch, token, head) row of d_v outputs,
@@ -360,6 +365,33 @@ int gla_oracle_recurrent_init(const double *q, const double *k, const double *v,
                        nthreads);
     a.init = init;
     return run(a, recurrent_one);
+}
+
+/* Low-rank gate: x [rows, C], W1 [C, R], W2 [R, K], b [K] -> lg [rows, K],
+ * lg = inv_tau * logsigmoid(x W1 W2 + b), logsigmoid(y) = -log(1 + e^{-y}). */
+int gla_oracle_lowrank_gate(const double *x, const double *w1, const double *w2, const double *b,
+                            double inv_tau, long rows, int C, int R, int K, double *lg)
+{
+    if (!x || !w1 || !w2 || !b || !lg || rows < 0 || C < 1 || R < 1 || K < 1) return -1;
+    double *z = malloc((size_t)R * sizeof(double));
+    if (!z) return -2;
+    for (long n = 0; n < rows; ++n) {
+        const double *xn = x + (size_t)n * C;
+        for (int r = 0; r < R; ++r) {
+            double acc = 0.0;
+            for (int c = 0; c < C; ++c) acc += xn[c] * w1[(size_t)c * R + r];
+            z[r] = acc;
+        }
+        for (int kk = 0; kk < K; ++kk) {
+            double y = b[kk];
+            for (int r = 0; r < R; ++r) y += z[r] * w2[(size_t)r * K + kk];
+            /* log sigma(y) without overflow on either side */
+            const double ls = y < 0.0 ? y - log1p(exp(y)) : -log1p(exp(-y));
+            lg[(size_t)n * K + kk] = inv_tau * ls;
+        }
+    }
+    free(z);
+    return 0;
 }
 
 /* Output epilogue, row by row: rows of d values, o and z [rows, d], w [d]. */

@@ -361,3 +361,36 @@ def test_rmsnorm_gate_pins():
     diff = oracle.rmsnorm_gate(o, z, w, 1e-3) - oracle.rmsnorm_gate(o, -z, w, 1e-3)
     np.testing.assert_allclose(diff, z * oracle.rmsnorm_gate(o, big, w, 1e-3) / 40.0,
                                rtol=1e-10, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- low-rank gate
+def _lowrank_inputs(seed, rows=37, C=24, R=16, K=12):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((rows, C)), rng.standard_normal((C, R)) / np.sqrt(C),
+            rng.standard_normal((R, K)) / 4.0, rng.standard_normal(K))
+
+
+def test_lowrank_gate_pins():
+    x, w1, w2, b = _lowrank_inputs(61)
+    lg = oracle.lowrank_gate(x, w1, w2, b)
+    assert lg.shape == (37, 12) and np.all(lg <= 0)
+    # no projection: a constant gate; logsigmoid(0) = -ln 2, logsigmoid(ln 3) = ln(3/4)
+    const = oracle.lowrank_gate(x, w1, 0 * w2, np.array([0.0, np.log(3.0)] * 6), inv_tau=1.0)
+    np.testing.assert_allclose(const[:, 0], -np.log(2.0), rtol=1e-15)
+    np.testing.assert_allclose(const[:, 1], np.log(0.75), rtol=1e-15)
+    # sigma(y) / sigma(-y) = e^y: flipping the sign of the projection and the bias
+    # moves log_gamma by exactly inv_tau * (x W1 W2 + b), a plain matrix product
+    flip = oracle.lowrank_gate(x, w1, -w2, -b)
+    np.testing.assert_allclose(lg - flip, (x @ w1 @ w2 + b) / 16.0, rtol=1e-12, atol=1e-14)
+    # sigma(y) + sigma(-y) = 1: the two gates raised to tau add up to one
+    np.testing.assert_allclose(np.exp(16 * lg) + np.exp(16 * flip), 1.0, rtol=1e-13)
+    # tau divides the log
+    np.testing.assert_allclose(oracle.lowrank_gate(x, w1, w2, b, inv_tau=1.0), 16 * lg, rtol=1e-14)
+    # x enters only through x W1: a component outside W1's column space changes nothing
+    q_, _ = np.linalg.qr(w1)
+    perp = np.random.default_rng(62).standard_normal(x.shape)
+    perp -= perp @ q_ @ q_.T
+    np.testing.assert_allclose(oracle.lowrank_gate(x + perp, w1, w2, b), lg, rtol=1e-11, atol=1e-13)
+    # no overflow for large pre-activations
+    big = oracle.lowrank_gate(x, w1, 1e4 * w2, b)
+    assert np.isfinite(big).all() and np.all(big <= 0)
