@@ -32,8 +32,8 @@ POLICY_AUTO, POLICY_GENERIC, POLICY_FUSED, POLICY_FUSED_ONE = 0, 1, 2, 3
 
 EXPORTED = (
     "gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_workspace_bytes", "gtr_gla_workspace_init",
-    "gtr_gla_fwd_ws", "gtr_gla_fwd_f32_ws", "gtr_gla_fwd_ex", "gtr_gla_set_policy",
-    "gtr_gla_get_policy",
+    "gtr_gla_fwd_ws", "gtr_gla_fwd_f32_ws", "gtr_gla_fwd_ex", "gtr_gla_fwd_lowrank",
+    "gtr_gla_lowrank_workspace_bytes", "gtr_gla_set_policy", "gtr_gla_get_policy",
     "gtr_gla_plan", "gtr_gla_status_str",
 )
 
@@ -66,6 +66,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gtr_gla_fwd_ex.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, I, I, I, I, I, I, I, I, I,
                                    P, P, P, Z, P]
     lib.gtr_gla_fwd_ex.restype = I
+    lib.gtr_gla_fwd_lowrank.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, I, P, P, P,
+                                        ctypes.c_float, I, I, I, I, I, I, I, I, I, P, P, P, Z, P]
+    lib.gtr_gla_fwd_lowrank.restype = I
+    lib.gtr_gla_lowrank_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.gtr_gla_lowrank_workspace_bytes.restype = Z
     lib.gtr_gla_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
     lib.gtr_gla_workspace_bytes.restype = Z
     lib.gtr_gla_workspace_init.argtypes = [P, Z, P]
@@ -203,6 +208,38 @@ def gtr_gla_fwd_ex(q, k, v, log_gamma, initial_state, gate, norm_weight, norm_ep
     _raise(r, "gtr_gla_fwd_ex")
 
 
+def gtr_gla_fwd_lowrank(q, k, v, x, w1, w2, gate_bias, inv_tau: float, C: int, initial_state,
+                        gate, norm_weight, norm_eps: float, B: int, H: int, grid_h: int,
+                        grid_w: int, d_k: int, d_v: int, dir: int, chunk: int, is_fp32: int, out,
+                        final_state=None, workspace=None, workspace_bytes: int = 0,
+                        stream=None) -> None:
+    """Forward with the gate computed from x by the rank-16 projection:
+    log_gamma = inv_tau * log sigmoid(x w1 w2 + gate_bias)."""
+    import torch
+    dtype = torch.float32 if is_fp32 else torch.float16
+    _check_all(q, k, v, None, B, H, grid_h, grid_w, d_k, d_v, out, final_state, dtype)
+    if min(B, H, grid_h, grid_w, d_k, d_v, C) >= 1:
+        _check(x, "x", dtype, B * grid_h * grid_w * C)
+        _check(w1, "w1", torch.float32, C * 16)
+        _check(w2, "w2", torch.float32, 16 * H * d_k)
+        _check(gate_bias, "gate_bias", torch.float32, H * d_k)
+        _check(initial_state, "initial_state", torch.float32, B * H * d_k * d_v)
+        _check(gate, "gate", dtype, B * grid_h * grid_w * H * d_v)
+        _check(norm_weight, "norm_weight", torch.float32, d_v)
+    r = load_library().gtr_gla_fwd_lowrank(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(w1), _ptr(w2), _ptr(gate_bias), float(inv_tau),
+        C, _ptr(initial_state), _ptr(gate), _ptr(norm_weight), float(norm_eps), B, H, grid_h,
+        grid_w, d_k, d_v, dir, chunk, int(is_fp32), _ptr(out), _ptr(final_state),
+        _ptr(workspace), workspace_bytes, _stream(stream))
+    _raise(r, "gtr_gla_fwd_lowrank")
+
+
+def gtr_gla_lowrank_workspace_bytes(B: int, H: int, grid_h: int, grid_w: int, d_k: int,
+                                    d_v: int, chunk: int, is_fp32: int) -> int:
+    return int(load_library().gtr_gla_lowrank_workspace_bytes(B, H, grid_h, grid_w, d_k, d_v,
+                                                              chunk, int(is_fp32)))
+
+
 def gtr_gla_set_policy(policy: int) -> None:
     _raise(load_library().gtr_gla_set_policy(int(policy)), "gtr_gla_set_policy")
 
@@ -252,4 +289,28 @@ def forward(q, k, v, log_gamma, grid_h: int, grid_w: int, dir, chunk: int = 64,
         return out, final_state
     fn = gtr_gla_fwd_f32 if q.dtype == torch.float32 else gtr_gla_fwd
     fn(q, k, v, log_gamma, B, H, grid_h, grid_w, dk, dv, int(dir), chunk, out, final_state, stream)
+    return out, final_state
+
+
+def forward_lowrank(q, k, v, x, w1, w2, gate_bias, grid_h: int, grid_w: int, dir,
+                    chunk: int = 64, inv_tau: float = 1.0 / 16, out=None, final_state=None,
+                    stream=None, initial_state=None, gate=None, norm_weight=None,
+                    norm_eps: float = 1e-5):
+    """forward() with the gate projected from x [B, L, C] (gtr_gla_fwd_lowrank).
+
+    w1 [C, 16], w2 [16, H d_k] and gate_bias [H d_k] are fp32. Returns (out, final_state).
+    """
+    import torch
+    if isinstance(dir, str):
+        dir = DIRS[dir]
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    C = x.shape[-1]
+    if out is None:
+        out = torch.empty((B, L, H, dv), dtype=q.dtype, device=q.device)
+    if final_state is None:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    gtr_gla_fwd_lowrank(q, k, v, x, w1, w2, gate_bias, inv_tau, C, initial_state, gate,
+                        norm_weight, norm_eps, B, H, grid_h, grid_w, dk, dv, int(dir), chunk,
+                        int(q.dtype == torch.float32), out, final_state, stream=stream)
     return out, final_state

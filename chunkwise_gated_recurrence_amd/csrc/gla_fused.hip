@@ -218,7 +218,45 @@ struct FusedArgs {
     const __half* gate;         // [B, L, H, 64] output gate, or null (outputs as they are)
     const float* norm_w;        // [64] RMSNorm weight of the output epilogue (with gate)
     float eps;
+    // log_gamma computed in the kernel from the low-rank gate (else read from lg):
+    // lg = inv_tau * logsigmoid(z W2 + bias), z = x W1 per token
+    const float* z;             // [B, L, 16] x W1, each row stored permuted: z[4k + s] = (x W1)[4s + k]
+    const float* w2;            // [16, H * dk]
+    const float* gbias;         // [H * dk]
+    float inv_tau;
+    int gtab_off;               // byte offset of the low-rank gate tables in dynamic LDS
 };
+
+// Dynamic LDS of every fused kernel: its Smem (or SmemRK), then, for the
+// low-rank gate, the W2 operand table and the bias.
+extern __shared__ __align__(16) unsigned char smem_raw[];
+
+// Low-rank gate tables: the A operand of the 16x16x4 fp32 MFMA for each lane,
+// tile jt (16 key dims) and rank step s, with the tile's rows (dims) permuted
+// so that the product lands in the layout of the chunk operands (lane (r, g)
+// of a wave: row r, dims 8g + e + 32hh); and the bias per key dim.
+struct GateTab {
+    float w2[64][16];   // [lane][4 jt + s] = W2[4 s + (lane >> 4)][h dk + col(lane & 15, jt)]
+    float bias[kD];
+};
+__device__ __forceinline__ int gate_col(int m, int jt)
+{
+    return 8 * (m >> 2) + 4 * (jt & 1) + (m & 3) + 32 * (jt >> 1);
+}
+
+// Fill head h's gate tables (every thread of the workgroup; the caller puts a
+// barrier before their first use). Key dims past dk get zero weight and bias.
+__device__ __forceinline__ void fill_gate_tables(const FusedArgs& a, int h, int tid)
+{
+    GateTab& gt = *reinterpret_cast<GateTab*>(smem_raw + a.gtab_off);
+    const int K = a.H * a.dk;
+    for (int q = tid; q < 64 * 16; q += kThreads) {
+        const int ln = q >> 4, idx = q & 15, jt = idx >> 2, sg = idx & 3;
+        const int col = gate_col(ln & 15, jt);
+        gt.w2[ln][idx] = col < a.dk ? a.w2[(4 * sg + (ln >> 4)) * K + h * a.dk + col] : 0.f;
+    }
+    if (tid < kD) gt.bias[tid] = tid < a.dk ? a.gbias[h * a.dk + tid] : 0.f;
+}
 
 struct Smem {
     // Kh and Sc are adjacent: the exact-score path uses them as one fp32 table.
@@ -291,6 +329,18 @@ __device__ __forceinline__ u4 load16(__amdgpu_buffer_rsrc_t rs, int voff)
     return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, kNT));
 }
 
+// Low-rank gate input of scan step t for lane l: z[4(l >> 4) .. +3] of the
+// row (the B operand of the gate MFMAs); zeros past the sequence end.
+__device__ __forceinline__ u4 load_z(const FusedArgs& a, int b, int t, int lane)
+{
+    const int bytes = a.L * 64;
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.z + (long long)b * a.L * 16), (short)0, bytes, 0x00020000);
+    const int voff = t < a.L ? scan_to_spatial(t, a.L, a.grid_h, a.grid_w, a.dir) * 64 + 16 * (lane >> 4)
+                             : bytes;
+    return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rz, voff, 0, kNT));
+}
+
 // Lane l of wave w loads row 16w + (l & 15), dims 8(l >> 4) + 32h .. +7.
 template <bool WITH_Q>
 __device__ __forceinline__ void load_chunk(const FusedArgs& a, int b, int h, int t0, int w,
@@ -305,7 +355,11 @@ __device__ __forceinline__ void load_chunk(const FusedArgs& a, int b, int h, int
         if (WITH_Q) R.q[hh] = load16(batch_rsrc(a.q, a, b, a.dk), o.key);
         R.k[hh] = load16(rk, o.key);
         R.v[hh] = load16(rv, o.val);
-        R.g[hh] = load16(rg, o.key);
+        if (!a.z) R.g[hh] = load16(rg, o.key);
+    }
+    if (a.z) {   // z, and whether the row is a token (rows past the end get no decay)
+        R.g[0] = load_z(a, b, t, lane);
+        R.g[1][0] = t < a.L;
     }
 }
 
@@ -389,8 +443,39 @@ struct NoHook {
     __device__ void operator()() const {}
 };
 
+// log_gamma of the lane's chunk operands (row r, dims 8g + e + 32hh) from the
+// low-rank gate: 16 MFMAs (4 dim tiles x 4 rank steps) of the permuted W2
+// table with z (the lane's z[4g .. 4g+3], zr), the bias as the accumulator's
+// start, then inv_tau * logsigmoid. A 32-wide key dim leaves dims 32..63 zero,
+// and so does a row past the sequence end (valid false: gamma = 1 there, as
+// the zero log_gamma that a read past the end gives on the other path).
+__device__ __forceinline__ void lowrank_gate(const FusedArgs& a, u4 zr, bool valid, int lane,
+                                             float (&x)[2][8])
+{
+    const GateTab& gt = *reinterpret_cast<const GateTab*>(smem_raw + a.gtab_off);
+    const int g = lane >> 4;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+        const int hh = jt >> 1, e0 = 4 * (jt & 1);
+        f4 acc = *reinterpret_cast<const f4*>(&gt.bias[8 * g + e0 + 32 * hh]);
+        const f4 wa = *reinterpret_cast<const f4*>(&gt.w2[lane][4 * jt]);
+#pragma unroll
+        for (int sg = 0; sg < 4; ++sg)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[sg], __uint_as_float(zr[sg]), acc, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float y = acc[e];
+            // log sigma(y) = min(y, 0) - ln(1 + e^{-|y|})
+            const float ls = fminf(y, 0.f) -
+                             0.69314718f * __builtin_amdgcn_logf(1.f + ex2(-kLog2e * fabsf(y)));
+            x[hh][e0 + e] = (valid && 8 * g + e0 + e + 32 * hh < a.dk) ? a.inv_tau * ls : 0.f;
+        }
+    }
+}
+
 template <bool FULL, class AfterA = NoHook>
-__device__ __forceinline__ void chunk_front(Smem& sm, const ChunkRegs& R, int w, int lane, int c,
+__device__ __forceinline__ void chunk_front(const FusedArgs& a, Smem& sm, const ChunkRegs& R, int w,
+                                            int lane, int c,
                                             f4 (&S)[4], bool stage_state, h8 (&Qt)[2], ChunkTmp& T,
                                             AfterA after_a = AfterA{})
 {
@@ -399,9 +484,14 @@ __device__ __forceinline__ void chunk_front(Smem& sm, const ChunkRegs& R, int w,
 
     // -- log2 gates, inclusive prefix over the wave's 16 rows
     float x[2][8];
+    if (a.z) {
+        lowrank_gate(a, R.g[0], R.g[1][0] != 0, lane, x);
+    } else {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) unpack8(R.g[hh], x[hh]);
+    }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-        unpack8(R.g[hh], x[hh]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float y = x[hh][e] * kLog2e;
@@ -771,7 +861,7 @@ __device__ __forceinline__ void keep_pass1(const FusedArgs& a, Smem& sm, const C
     const int g = lane >> 4;
     ChunkTmp T;
     h8 Qt[2];
-    chunk_front<true>(sm, R, w, lane, 0, S, false, Qt, T);
+    chunk_front<true>(a, sm, R, w, lane, 0, S, false, Qt, T);
     publish_summary<false>(a, sm, S, slot, j, ep, w, lane);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
@@ -807,7 +897,7 @@ __device__ __forceinline__ void keep_pass_loop(const FusedArgs& a, Smem& sm, Chu
         const int g = lane >> 4;
         ChunkTmp T;
         h8 Qt[2];
-        chunk_front<true>(sm, R, w, lane, c, S, c > 0, Qt, T);
+        chunk_front<true>(a, sm, R, w, lane, c, S, c > 0, Qt, T);
         // never under a branch; past the span's end reads zeros
         load_chunk<true>(a, b, h, c + 1 < NC ? (c_first + c + 1) * kC : a.L, w, lane, R);
         if (c + 1 == NC) publish_summary<true>(a, sm, S, slot, j, ep, w, lane);
@@ -1076,7 +1166,6 @@ __global__ void __launch_bounds__(kThreads, 3)
 gla_fused_kernel(FusedArgs a)
 {
     static_assert(!KEEP || SPAN <= kMaxKeep, "a kept span holds at most kMaxKeep chunks");
-    extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
 
     const int tid = threadIdx.x;
@@ -1108,6 +1197,10 @@ gla_fused_kernel(FusedArgs a)
         sm.P[0][tid] = 0.f;
         sm.Pend[tid] = 0.f;
     }
+    if (a.z) {
+        fill_gate_tables(a, h, tid);
+        lds_barrier();
+    }
 
     // ---- 1. local pass --------------------------------------------------------
     // The span summary is published right after the last chunk's state update,
@@ -1135,7 +1228,7 @@ gla_fused_kernel(FusedArgs a)
         for (int c = 0; c < n_c; ++c) {
             int ln = lane;
             asm volatile("" : "+v"(ln));   // addresses recomputed per chunk, not held live
-            chunk_front<false>(sm, cur, w, ln, c, S, false, qdummy, T);
+            chunk_front<false>(a, sm, cur, w, ln, c, S, false, qdummy, T);
             load_chunk<false>(a, b, h, c + 1 < n_c ? (c_first + c + 1) * kC : a.L, w, lane, cur);
         }
         publish_summary<false>(a, sm, S, seq_slot + j, j, ep, w, lane);
@@ -1229,7 +1322,7 @@ gla_fused_kernel(FusedArgs a)
             ChunkTmp T;
             u4 z[2];
             if (a.gate) load_gate(a, b, h, (c_first + c) * kC, w, ln, z);
-            chunk_front<true>(sm, cur, w, ln, kMaxKeep, S, c > 0, qt, T);
+            chunk_front<true>(a, sm, cur, w, ln, kMaxKeep, S, c > 0, qt, T);
             load_chunk<true>(a, b, h, c + 1 < n_c ? (c_first + c + 1) * kC : a.L, w, ln, cur);
             chunk_back(sm, a, b, h, (c_first + c) * kC, w, ln, has_in || (c > 0), Oc, qt, T);
             store_out(sm, a, b, h, (c_first + c) * kC, w, ln, Oc, z);
@@ -1262,13 +1355,28 @@ __device__ __forceinline__ void dma_gkv(const FusedArgs& a, SmemRK& sk, int b, i
         const int row = 16 * w + 8 * i + (lane >> 3);
         const RowOff o = row_off(a, h, t0 + row, (lane & 7) ^ (row & 7));
         const int base = (16 * w + 8 * i) * kD;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rg, (__attribute__((address_space(3))) void*)(sk.raw[0] + base), 16, o.key, 0, 0, kNT);
+        if (!a.z)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rg, (__attribute__((address_space(3))) void*)(sk.raw[0] + base), 16, o.key, 0, 0, kNT);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rk, (__attribute__((address_space(3))) void*)(sk.raw[1] + base), 16, o.key, 0, 0, kNT);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rv, (__attribute__((address_space(3))) void*)(sk.raw[2] + base), 16, o.val, 0, 0, kNT);
     }
+}
+
+// With the low-rank gate, raw[0] holds z instead of g: the wave's 16 rows of
+// 16 floats, one DMA per wave (lane l: row 16w + (l >> 2), floats 4(l & 3) ..).
+__device__ __forceinline__ void dma_z(const FusedArgs& a, SmemRK& sk, int b, int t0, int w, int lane)
+{
+    const int bytes = a.L * 64;
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.z + (long long)b * a.L * 16), (short)0, bytes, 0x00020000);
+    const int t = t0 + 16 * w + (lane >> 2);
+    const int voff = t < a.L ? scan_to_spatial(t, a.L, a.grid_h, a.grid_w, a.dir) * 64 + 16 * (lane & 3)
+                             : bytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rz, (__attribute__((address_space(3))) void*)(sk.raw[0] + 16 * w * 32), 16, voff, 0, 0, kNT);
 }
 
 __device__ __forceinline__ u4 raw_ld(const _Float16* tile, int row, int blk)
@@ -1291,7 +1399,6 @@ __global__ void __launch_bounds__(kThreads, 2)
 gla_fused_rk_kernel(FusedArgs a)
 {
     static_assert(SPAN >= 2 && SPAN <= kMaxKeep, "register-kept spans hold 2 .. kMaxKeep chunks");
-    extern __shared__ __align__(16) unsigned char smem_raw[];
     SmemRK& sk = *reinterpret_cast<SmemRK*>(smem_raw);
     Smem& sm = sk.s;
 
@@ -1313,12 +1420,14 @@ gla_fused_rk_kernel(FusedArgs a)
     const float nwr = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
         rsrc(a.norm_w, a.gate ? 4 * kD : 0), 4 * (tid & (kD - 1)), 0, 0));
     dma_gkv(a, sk, b, h, c_first * kC, w, lane);
+    if (a.z) dma_z(a, sk, b, c_first * kC, w, lane);
     u4 qn[2];
     load_q(a, b, h, c_first * kC, w, lane, qn);
     if (tid < kD) {
         sm.P[0][tid] = 0.f;
         sm.Pend[tid] = 0.f;
     }
+    if (a.z) fill_gate_tables(a, h, tid);   // the loop's first barrier orders it
 
     // ---- 1. local pass: SPAN chunks, always (past the sequence end the
     // staged rows are zeros: state and decay unchanged, outputs not stored)
@@ -1344,12 +1453,18 @@ gla_fused_rk_kernel(FusedArgs a)
             R.k[hh] = raw_ld(sk.raw[1], 16 * w + rr, 4 * hh + gg);
             R.v[hh] = raw_ld(sk.raw[2], 16 * w + rr, 4 * hh + gg);
         }
+        if (a.z) {   // z rows of the chunk: 16 floats per row, the lane's four at 4 gg
+            R.g[0] = *reinterpret_cast<const u4*>(reinterpret_cast<const float*>(sk.raw[0]) +
+                                                  (16 * w + rr) * 16 + 4 * gg);
+            R.g[1][0] = (c_first + c) * kC + 16 * w + rr < a.L;
+        }
         h8 Qt[2];
         ChunkTmp T;
         // never under a branch; past the span's end reads zeros
         const int tn = c + 1 < SPAN ? (c_first + c + 1) * kC : a.L;
-        chunk_front<true>(sm, R, w, ln, c, S, c > 0, Qt, T, [&]() {
+        chunk_front<true>(a, sm, R, w, ln, c, S, c > 0, Qt, T, [&]() {
             dma_gkv(a, sk, b, h, tn, w, ln);
+            if (a.z) dma_z(a, sk, b, tn, w, ln);
             load_q(a, b, h, tn, w, ln, qn);
         });
         if (c + 1 == SPAN) publish_summary<true>(a, sm, S, seq_slot + j, j, ep, w, ln);
@@ -1491,17 +1606,22 @@ static const void* pick_kernel(int span, bool keep, bool rk)
     }
 }
 
-static size_t smem_bytes(bool rk) { return rk ? sizeof(SmemRK) : sizeof(Smem); }
+// Dynamic LDS: the variant's Smem, then (low-rank gate) the gate tables.
+static size_t gate_tab_offset(bool rk) { return ((rk ? sizeof(SmemRK) : sizeof(Smem)) + 15) / 16 * 16; }
+static size_t smem_bytes(bool rk, bool lowrank)
+{
+    return lowrank ? gate_tab_offset(rk) + sizeof(GateTab) : (rk ? sizeof(SmemRK) : sizeof(Smem));
+}
 
 // Workgroups of one variant that fit on a CU at once.
-static int resident_per_cu(int span, bool keep, bool rk)
+static int resident_per_cu(int span, bool keep, bool rk, bool lowrank)
 {
-    static int cache[3][kMaxKeep + 1] = {};
-    int& c = cache[rk ? 2 : (keep ? 1 : 0)][(keep || rk) ? span : 0];
+    static int cache[2][3][kMaxKeep + 1] = {};
+    int& c = cache[lowrank ? 1 : 0][rk ? 2 : (keep ? 1 : 0)][(keep || rk) ? span : 0];
     if (c == 0) {
         const void* fn = pick_kernel(span, keep, rk);
         int n = 0;
-        const size_t sh = smem_bytes(rk);
+        const size_t sh = smem_bytes(rk, lowrank);
         if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh) !=
                 hipSuccess ||
             hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, sh) != hipSuccess ||
@@ -1512,9 +1632,10 @@ static int resident_per_cu(int span, bool keep, bool rk)
     return c;
 }
 
-FusedPlan fused_plan(const Shape& s, int span_override, int rk_override)
+FusedPlan fused_plan(const Shape& s, int span_override, int rk_override, bool lowrank)
 {
     FusedPlan p;
+    p.lowrank = lowrank;
     const int n_seq = s.B * s.H;
     const int nc = s.n_chunks;
     auto fill = [&](int span, bool keep, bool rk = false) {
@@ -1522,7 +1643,7 @@ FusedPlan fused_plan(const Shape& s, int span_override, int rk_override)
         p.keep = keep || rk;
         p.rk = rk;
         p.n_spans = (nc + span - 1) / span;
-        const long long cap = (long long)resident_per_cu(span, keep, rk) * device_cus();
+        const long long cap = (long long)resident_per_cu(span, keep, rk, lowrank) * device_cus();
         // sequences per launch, so that every workgroup of a launch is resident
         long long per = cap / p.n_spans;
         if (per < 1) per = 1;
@@ -1534,7 +1655,8 @@ FusedPlan fused_plan(const Shape& s, int span_override, int rk_override)
         p.slice_log2 = 12 - lg;
     };
     auto one_seq_fits = [&]() {
-        return (long long)p.n_spans <= (long long)resident_per_cu(p.span, p.keep, p.rk) * device_cus();
+        return (long long)p.n_spans <=
+               (long long)resident_per_cu(p.span, p.keep, p.rk, lowrank) * device_cus();
     };
     if (span_override > 0) {
         if (rk_override > 0 && rk_span_ok(span_override)) {
@@ -1560,7 +1682,7 @@ FusedPlan fused_plan(const Shape& s, int span_override, int rk_override)
         if (whole()) return p;
     }
     // else streamed spans
-    const long long cap = (long long)resident_per_cu(1, false, false) * device_cus();
+    const long long cap = (long long)resident_per_cu(1, false, false, lowrank) * device_cus();
     long long per_seq = cap / n_seq;
     if (per_seq < 1) per_seq = 1;
     if (per_seq > kMaxSpans) per_seq = kMaxSpans;
@@ -1600,6 +1722,12 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
     a.gate = (const __half*)x.gate;
     a.norm_w = x.norm_w;
     a.eps = x.eps;
+    a.z = x.z;
+    a.w2 = x.w2;
+    a.gbias = x.gbias;
+    a.inv_tau = x.inv_tau;
+    a.gtab_off = (int)gate_tab_offset(p.rk);
+    if (p.lowrank != (x.z != nullptr)) return hipErrorInvalidValue;
     a.q = (const __half*)q;
     a.k = (const __half*)k;
     a.v = (const __half*)v;
@@ -1627,14 +1755,14 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
     if (p.keep && !p.rk && p.span >= 2 && a.park == nullptr) return hipErrorInvalidValue;
     if (p.rk && !rk_span_ok(p.span)) return hipErrorInvalidValue;
     const void* fn = pick_kernel(p.span, p.keep, p.rk);
-    resident_per_cu(p.span, p.keep, p.rk);   // also raises the kernel's dynamic LDS limit
+    resident_per_cu(p.span, p.keep, p.rk, p.lowrank);   // also raises the kernel's dynamic LDS limit
     const int n_seq = s.B * s.H;
     for (int s0 = 0; s0 < n_seq; s0 += p.seq_batch) {
         a.seq0 = s0;
         const int nseq = (n_seq - s0 < p.seq_batch) ? (n_seq - s0) : p.seq_batch;
         void* args[] = {&a};
         const hipError_t e = hipLaunchKernel(fn, dim3(nseq * p.n_spans), dim3(kThreads), args,
-                                             smem_bytes(p.rk), st);
+                                             smem_bytes(p.rk, p.lowrank), st);
         if (e != hipSuccess) return e;
     }
     return hipGetLastError();

@@ -23,11 +23,12 @@ struct FusedPlan {
     int seq_batch;   // sequences per launch (every workgroup of a launch is resident)
     int grid;        // workgroups per launch
     int slice_log2;  // log2 of the state elements each owning workgroup scans
+    bool lowrank;    // log_gamma computed in the kernel from the low-rank gate
 };
 bool fused_supported(const Shape& s);
 // span_override > 0 forces the span; rk_override > 0 then asks for the
 // register-kept variant (when that span has one).
-FusedPlan fused_plan(const Shape& s, int span_override, int rk_override);
+FusedPlan fused_plan(const Shape& s, int span_override, int rk_override, bool lowrank);
 size_t fused_workspace_bytes(const Shape& s, const FusedPlan& p);
 hipError_t launch_fused(const void* q, const void* k, const void* v, const void* lg,
                         const Shape& s, const Extras& x, const FusedPlan& p, void* out,
@@ -35,5 +36,14 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
 
 // Zero fill by a kernel (graph-capturable); p must be 16-byte aligned.
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
+
+// Low-rank gate (gla_gate.hip): z = x W1 per token, [rows, 16] fp32 with each
+// row permuted (z[4k + s] = (x W1)[4s + k]); and log_gamma [rows, K] (K = H dk,
+// the input precision) = inv_tau * logsigmoid(z W2 + bias) for the generic path.
+hipError_t launch_lowrank_project(const void* x, bool is_fp32, const float* w1, size_t rows, int C,
+                                  float* z, hipStream_t st);
+hipError_t launch_lowrank_log_gamma(const float* z, const float* w2, const float* bias,
+                                    float inv_tau, size_t rows, int K, bool is_fp32, void* lg,
+                                    hipStream_t st);
 
 }  // namespace gtrgla

@@ -128,25 +128,42 @@ int validate_extras(const Extras& x, const void* out, const float* fs, const Sha
 
 enum Kernel { kGeneric = 1, kFused = 2, kFusedRegisterKept = 3 };
 
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of a call: the kernels' own part, then for the low-rank gate
+// z = x W1 (fp32, 16 per token) and, on the generic path, log_gamma.
 struct Choice {
     Kernel kernel;
     FusedPlan plan;
-    size_t ws_bytes;
+    size_t ws_bytes;     // everything
+    size_t base_bytes;   // the kernels' part (offset of z)
+    size_t lg_offset;    // generic + low-rank: offset of log_gamma
 };
 
-Choice choose(const Shape& s, bool is_fp32, int policy)
+Choice choose(const Shape& s, bool is_fp32, int policy, bool lowrank = false)
 {
     Choice c;
     c.kernel = kGeneric;
-    c.plan = FusedPlan{1, false, false, s.n_chunks, 0, 0, 0};
+    c.plan = FusedPlan{1, false, false, s.n_chunks, 0, 0, 0, lowrank};
     const bool fused_ok = !is_fp32 && gtrgla::fused_supported(s);
     if (fused_ok && policy != GTR_GLA_POLICY_GENERIC) {
         c.kernel = kFused;
         const int span = (policy == GTR_GLA_POLICY_FUSED_ONE) ? 1 : span_override_from_env();
-        c.plan = gtrgla::fused_plan(s, span, rk_override_from_env());
-        c.ws_bytes = gtrgla::fused_workspace_bytes(s, c.plan);
+        c.plan = gtrgla::fused_plan(s, span, rk_override_from_env(), lowrank);
+        c.base_bytes = gtrgla::fused_workspace_bytes(s, c.plan);
     } else {
-        c.ws_bytes = gtrgla::generic_workspace_bytes(s);
+        c.base_bytes = gtrgla::generic_workspace_bytes(s);
+    }
+    c.ws_bytes = c.base_bytes;
+    c.lg_offset = 0;
+    if (lowrank) {
+        const size_t rows = (size_t)s.B * s.L;
+        c.base_bytes = align256(c.base_bytes);
+        c.ws_bytes = c.base_bytes + align256(rows * 16 * sizeof(float));
+        if (c.kernel == kGeneric) {
+            c.lg_offset = c.ws_bytes;
+            c.ws_bytes += align256(rows * s.H * (size_t)s.d_k * (is_fp32 ? 4 : 2));
+        }
     }
     return c;
 }
@@ -225,18 +242,53 @@ int cached_workspace(size_t need, hipStream_t st, const WsLayout& layout, void**
     return GTR_GLA_OK;
 }
 
+// The low-rank gate's inputs (gtr_gla_fwd_lowrank), when given.
+struct LowRank {
+    const void* x = nullptr;   // [B, L, C], the input precision
+    const float* w1 = nullptr; // [C, 16]
+    const float* w2 = nullptr; // [16, H d_k]
+    const float* bias = nullptr;
+    float inv_tau = 0.f;
+    int C = 0;
+};
+
+int validate_lowrank(const LowRank& g, const void* out, const float* fs, const Shape& s, size_t elt)
+{
+    if (!g.x || !g.w1 || !g.w2 || !g.bias) return GTR_GLA_ERR_NULL;
+    if (g.C < 1 || g.C > (1 << 16)) return GTR_GLA_ERR_SHAPE;
+    if (!std::isfinite(g.inv_tau) || !(g.inv_tau > 0.f)) return GTR_GLA_ERR_VALUE;
+    const size_t rows = (size_t)s.B * s.L;
+    const size_t K = (size_t)s.H * s.d_k;
+    const void* ins[4] = {g.x, g.w1, g.w2, g.bias};
+    const size_t ns[4] = {rows * g.C * elt, (size_t)g.C * 16 * 4, 16 * K * 4, K * 4};
+    const size_t nv = rows * s.H * (size_t)s.d_v * elt;
+    const size_t nf = (size_t)s.B * s.H * s.d_k * s.d_v * sizeof(float);
+    for (int i = 0; i < 4; ++i) {
+        if (overlaps(ins[i], ns[i], out, nv)) return GTR_GLA_ERR_ALIAS;
+        if (fs && overlaps(ins[i], ns[i], fs, nf)) return GTR_GLA_ERR_ALIAS;
+    }
+    return GTR_GLA_OK;
+}
+
 int run(const void* q, const void* k, const void* v, const void* lg, int B, int H, int gh, int gw,
         int dk, int dv, int dir, int chunk, void* out, float* fs, bool is_fp32, void* ws,
-        size_t ws_bytes, bool own_ws, hipStream_t st, const Extras& x = Extras{})
+        size_t ws_bytes, bool own_ws, hipStream_t st, const Extras& x0 = Extras{},
+        const LowRank* lr = nullptr)
 {
     Shape s;
     int r = validate_sizes(B, H, gh, gw, dk, dv, dir, chunk, &s);
     if (r != GTR_GLA_OK) return r;
-    r = validate_pointers(q, k, v, lg, out, fs, s, is_fp32 ? 4 : 2);
+    // log_gamma is not an input with the low-rank gate: check the rest with q in its place
+    r = validate_pointers(q, k, v, lr ? q : lg, out, fs, s, is_fp32 ? 4 : 2);
     if (r != GTR_GLA_OK) return r;
-    r = validate_extras(x, out, fs, s, is_fp32 ? 4 : 2);
+    r = validate_extras(x0, out, fs, s, is_fp32 ? 4 : 2);
     if (r != GTR_GLA_OK) return r;
-    const Choice c = choose(s, is_fp32, current_policy());
+    if (lr) {
+        r = validate_lowrank(*lr, out, fs, s, is_fp32 ? 4 : 2);
+        if (r != GTR_GLA_OK) return r;
+    }
+    Extras x = x0;
+    const Choice c = choose(s, is_fp32, current_policy(), lr != nullptr);
     const WsLayout layout = c.kernel == kFused ? WsLayout{kFused, c.plan.n_spans, c.plan.seq_batch}
                                                : WsLayout{kGeneric, 0, 0};
     if (own_ws) {
@@ -246,10 +298,25 @@ int run(const void* q, const void* k, const void* v, const void* lg, int B, int 
         return GTR_GLA_ERR_WORKSPACE;
     }
     hipError_t e = hipSuccess;
-    if (c.kernel == kFused) {
-        if (!workspace_ready_for(ws, layout)) e = gtrgla::fill_zero(ws, c.ws_bytes, st);
+    if (lr) {
+        float* z = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + c.base_bytes);
+        e = gtrgla::launch_lowrank_project(lr->x, is_fp32, lr->w1, (size_t)s.B * s.L, lr->C, z, st);
+        if (c.kernel == kFused) {
+            x.z = z;
+            x.w2 = lr->w2;
+            x.gbias = lr->bias;
+            x.inv_tau = lr->inv_tau;
+        } else if (e == hipSuccess) {
+            void* lgw = static_cast<unsigned char*>(ws) + c.lg_offset;
+            e = gtrgla::launch_lowrank_log_gamma(z, lr->w2, lr->bias, lr->inv_tau,
+                                                 (size_t)s.B * s.L, s.H * s.d_k, is_fp32, lgw, st);
+            lg = lgw;
+        }
+    }
+    if (e == hipSuccess && c.kernel == kFused) {
+        if (!workspace_ready_for(ws, layout)) e = gtrgla::fill_zero(ws, c.base_bytes, st);
         if (e == hipSuccess) e = gtrgla::launch_fused(q, k, v, lg, s, x, c.plan, out, fs, ws, st);
-    } else {
+    } else if (e == hipSuccess) {
         e = gtrgla::launch_generic(q, k, v, lg, is_fp32, s, x, out, fs, ws, st);
     }
     mark_workspace(ws, layout);
@@ -325,6 +392,38 @@ int gtr_gla_fwd_ex(const void* q, const void* k, const void* v, const void* log_
                is_fp32 != 0, workspace, workspace_bytes, workspace == nullptr, stream, x);
 }
 
+int gtr_gla_fwd_lowrank(const void* q, const void* k, const void* v, const void* x,
+                        const float* w1, const float* w2, const float* gate_bias, float inv_tau,
+                        int C, const float* initial_state, const void* gate,
+                        const float* norm_weight, float norm_eps, int B, int H, int grid_h,
+                        int grid_w, int d_k, int d_v, int dir, int chunk, int is_fp32, void* out,
+                        float* final_state, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream)
+{
+    Extras e;
+    e.init = initial_state;
+    e.gate = gate;
+    e.norm_w = norm_weight;
+    e.eps = norm_eps;
+    LowRank lr;
+    lr.x = x;
+    lr.w1 = w1;
+    lr.w2 = w2;
+    lr.bias = gate_bias;
+    lr.inv_tau = inv_tau;
+    lr.C = C;
+    return run(q, k, v, nullptr, B, H, grid_h, grid_w, d_k, d_v, dir, chunk, out, final_state,
+               is_fp32 != 0, workspace, workspace_bytes, workspace == nullptr, stream, e, &lr);
+}
+
+size_t gtr_gla_lowrank_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                                       int chunk, int is_fp32)
+{
+    Shape s;
+    if (validate_sizes(B, H, grid_h, grid_w, d_k, d_v, 0, chunk, &s) != GTR_GLA_OK) return 0;
+    return choose(s, is_fp32 != 0, current_policy(), true).ws_bytes;
+}
+
 int gtr_gla_set_policy(int policy)
 {
     if (policy < GTR_GLA_POLICY_AUTO || policy > GTR_GLA_POLICY_FUSED_ONE) return GTR_GLA_ERR_POLICY;
@@ -360,7 +459,7 @@ const char* gtr_gla_status_str(int status)
     case GTR_GLA_ERR_HIP: return "HIP runtime error";
     case GTR_GLA_ERR_ALIAS: return "an output overlaps an input or the other output";
     case GTR_GLA_ERR_POLICY: return "unknown policy";
-    case GTR_GLA_ERR_VALUE: return "invalid scalar argument (norm_eps must be finite and >= 0)";
+    case GTR_GLA_ERR_VALUE: return "invalid scalar argument (norm_eps must be finite and >= 0, inv_tau finite and > 0)";
     default: return "unknown status";
     }
 }

@@ -96,5 +96,26 @@ def generate(w: Workload) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarra
     raise ValueError(f"unknown dtype {w.dtype}")
 
 
+def generate_lowrank(w: Workload, C: int, seed: int, bias_std: float = 0.5
+                     ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Inputs of the data-dependent low-rank gate (rank 16): (x, W1, W2, bias).
+
+    x [B, L, C] standard normal (rounded to fp16 for fp16 workloads, as a
+    layer-normed feature map); W1 [C, 16] normal with std 1/sqrt(C) and W2
+    [16, H d_k] normal with std 1/4, so that x W1 W2 is about unit normal;
+    bias [H d_k] = gate_mu + bias_std * normal. W1, W2 and bias are float32.
+    """
+    rng = np.random.default_rng(seed)
+    K = w.H * w.d_k
+    x = rng.standard_normal((w.B, w.L, C), dtype=np.float32)
+    w1 = rng.standard_normal((C, 16), dtype=np.float32) * np.float32(1.0 / np.sqrt(C))
+    w2 = rng.standard_normal((16, K), dtype=np.float32) * np.float32(0.25)
+    bias = (np.float32(w.gate_mu) + np.float32(bias_std) *
+            rng.standard_normal(K, dtype=np.float32)).astype(np.float32)
+    if w.dtype == "fp16":
+        x = x.astype(np.float16)
+    return x, w1, w2, bias
+
+
 def np_dtype(w: Workload):
     return np.float16 if w.dtype == "fp16" else np.float32

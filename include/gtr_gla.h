@@ -66,7 +66,8 @@ typedef enum {
     GTR_GLA_ERR_HIP = 7,         /* the HIP runtime reported an error               */
     GTR_GLA_ERR_ALIAS = 8,       /* an output overlaps an input or the other output  */
     GTR_GLA_ERR_POLICY = 9,      /* unknown policy value                             */
-    GTR_GLA_ERR_VALUE = 10       /* invalid scalar argument (norm_eps not finite or < 0) */
+    GTR_GLA_ERR_VALUE = 10       /* invalid scalar argument (norm_eps not finite or < 0,
+                                    inv_tau not finite or <= 0)                     */
 } gtr_gla_status;
 
 /* Launch policies (the pages' length-aware scheduling: short sequences take
@@ -138,6 +139,36 @@ int gtr_gla_fwd_ex(const void* q, const void* k, const void* v, const void* log_
                    float norm_eps, int B, int H, int grid_h, int grid_w, int d_k, int d_v,
                    int dir, int chunk, int is_fp32, void* out, float* final_state,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gtr_gla_fwd_lowrank -- gtr_gla_fwd_ex with the gate computed from the input
+ * instead of passed in: the data-dependent low-rank gate of the summary page,
+ * section 核心方法, gamma_t = sigmoid(x_t W1 W2 + b)^(1/tau), read as
+ *     log_gamma_t = inv_tau * log sigmoid(x_t W1 W2 + gate_bias),
+ * per head h the columns h*d_k .. h*d_k + d_k - 1 of the H*d_k products.
+ *   x         [B, L, C]   the token features the gate is projected from
+ *                         (fp16, or fp32 when is_fp32), token order as q.
+ *   w1        [C, 16]     fp32, the rank-16 down projection (C >= 1).
+ *   w2        [16, H*d_k] fp32, the up projection.
+ *   gate_bias [H*d_k]     fp32.
+ *   inv_tau   1/tau, finite and > 0 (the pages use tau = 16); else
+ *             GTR_GLA_ERR_VALUE.
+ * x W1 is computed once per token in fp32 into the workspace; the fused
+ * kernels form log_gamma inside the chunk from it (x W1) W2 on fp32 MFMA and
+ * never write it to memory, the generic kernels read it from the workspace.
+ * None of the four may overlap an output (GTR_GLA_ERR_ALIAS).
+ * workspace NULL: the library's own; otherwise at least
+ * gtr_gla_lowrank_workspace_bytes, cleared once by gtr_gla_workspace_init.
+ */
+int gtr_gla_fwd_lowrank(const void* q, const void* k, const void* v, const void* x,
+                        const float* w1, const float* w2, const float* gate_bias, float inv_tau,
+                        int C, const float* initial_state, const void* gate,
+                        const float* norm_weight, float norm_eps, int B, int H, int grid_h,
+                        int grid_w, int d_k, int d_v, int dir, int chunk, int is_fp32, void* out,
+                        float* final_state, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+size_t gtr_gla_lowrank_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                                       int chunk, int is_fp32);
 
 size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v,
                                int chunk, int is_fp32);

@@ -160,3 +160,49 @@ def test_fwd_ex_checks_its_additions(lib):
     ptrs[0] = None
     assert _fwd_ex(lib, ptrs, init=far) == gla.ERR_NULL
     assert "norm_eps" in gla.gtr_gla_status_str(gla.ERR_VALUE)
+
+
+def _fwd_lr(lib, ptrs, x="far", w1="far", w2="far", bias="far", inv_tau=1.0 / 16, C=96, B=1,
+            H=2, gh=4, gw=4, dk=64, dv=64, f32=0, init=None):
+    q, k, v, _, o, f = ptrs
+    far = BASE + 10 * SEP
+    x = far if x == "far" else x
+    w1 = far + SEP if w1 == "far" else w1
+    w2 = far + 2 * SEP if w2 == "far" else w2
+    bias = far + 3 * SEP if bias == "far" else bias
+    return lib.gtr_gla_fwd_lowrank(q, k, v, x, w1, w2, bias, inv_tau, C, init, None, None, 1e-5,
+                                   B, H, gh, gw, dk, dv, 0, 64, f32, o, f, None, 0, None)
+
+
+def test_fwd_lowrank_checks_its_inputs(lib):
+    """gtr_gla_fwd_lowrank: x, W1, W2 and the bias are required, C >= 1, inv_tau finite and
+    > 0, and none of them may overlap an output; log_gamma is not an input."""
+    for name in ("x", "w1", "w2", "bias"):
+        assert _fwd_lr(lib, PTRS, **{name: None}) == gla.ERR_NULL, name
+    assert _fwd_lr(lib, PTRS, C=0) == gla.ERR_SHAPE
+    for t in (0.0, -1.0, float("nan"), float("inf")):
+        assert _fwd_lr(lib, PTRS, inv_tau=t) == gla.ERR_VALUE, t
+    out, fs = PTRS[4], PTRS[5]
+    assert _fwd_lr(lib, PTRS, x=out + 64) == gla.ERR_ALIAS
+    assert _fwd_lr(lib, PTRS, w2=fs + 4) == gla.ERR_ALIAS
+    assert _fwd_lr(lib, PTRS, bias=out) == gla.ERR_ALIAS
+    # the base checks still apply; no log_gamma is needed
+    assert _fwd_lr(lib, PTRS, B=0) == gla.ERR_SHAPE
+    ptrs = list(PTRS)
+    ptrs[3] = None
+    assert _fwd_lr(lib, ptrs, B=0) == gla.ERR_SHAPE
+    ptrs[0] = None
+    assert _fwd_lr(lib, ptrs) == gla.ERR_NULL
+    assert "inv_tau" in gla.gtr_gla_status_str(gla.ERR_VALUE)
+
+
+def test_lowrank_workspace_size(lib):
+    """The low-rank call's workspace: the kernels' own, then x W1 in fp32 (16 per token), and
+    on the generic path log_gamma too."""
+    B, H, gh, gw, dk, dv = 2, 3, 10, 13, 32, 16
+    base = lib.gtr_gla_workspace_bytes(B, H, gh, gw, dk, dv, 64, 1)
+    up = lambda n: (n + 255) // 256 * 256
+    rows = B * gh * gw
+    n = lib.gtr_gla_lowrank_workspace_bytes(B, H, gh, gw, dk, dv, 64, 1)
+    assert n == up(base) + up(rows * 16 * 4) + up(rows * H * dk * 4)
+    assert lib.gtr_gla_lowrank_workspace_bytes(0, H, gh, gw, dk, dv, 64, 1) == 0
