@@ -40,13 +40,25 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 DIRS = (0, 1, 2, 3)
 
 
-def alg_bytes(w, gate: bool = False, init: bool = False) -> int:
+def lowrank_features(w) -> int:
+    """Feature width C of the gate's input x: the model width H * d_v."""
+    return w.H * w.d_v
+
+
+def alg_bytes(w, gate: bool = False, init: bool = False, lowrank: bool = False) -> int:
     """Bytes the method must move per call: read q, k, v, log_gamma, write o and final_state
     (with the output gate also read the gate and the norm weight; with an initial state
-    also read that)."""
+    also read that; with the low-rank gate read x, W1, W2 and the bias instead of
+    log_gamma)."""
     s = 2 if w.dtype == "fp16" else 4
     rows = w.B * w.L * w.H
-    n = rows * (3 * w.d_k + 2 * w.d_v) * s + w.B * w.H * w.d_k * w.d_v * 4
+    n = rows * (2 * w.d_k + 2 * w.d_v) * s + w.B * w.H * w.d_k * w.d_v * 4
+    if lowrank:
+        C = lowrank_features(w)
+        K = w.H * w.d_k
+        n += w.B * w.L * C * s + (C * 16 + 16 * K + K) * 4
+    else:
+        n += rows * w.d_k * s
     if gate:
         n += rows * w.d_v * s + w.d_v * 4
     if init:
@@ -55,13 +67,13 @@ def alg_bytes(w, gate: bool = False, init: bool = False) -> int:
 
 
 def split_name(name: str):
-    """'long2048+gate+init' -> ('long2048', gate, init)."""
+    """'long2048+gate+init' -> ('long2048', {"gate": True, "init": True, "lowrank": False})."""
     parts = name.split("+")
     extra = set(parts[1:])
-    bad = extra - {"gate", "init"}
+    bad = extra - {"gate", "init", "lowrank"}
     if bad:
         raise ValueError(f"unknown workload variant {sorted(bad)}")
-    return parts[0], "gate" in extra, "init" in extra
+    return parts[0], {k: k in extra for k in ("gate", "init", "lowrank")}
 
 
 def mfma_flops(w) -> int:
@@ -114,14 +126,17 @@ def rotation_groups(per_call: int, steps: int, rotate: bool) -> int:
 
 
 def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = True,
-                 gate: bool = False, init: bool = False, per_dir: bool = False):
+                 gate: bool = False, init: bool = False, per_dir: bool = False,
+                 lowrank: bool = False):
     """Time `steps` steps of the workload. A step is four calls (the four scan
     orders), each on its own input set; the sets rotate over >= 512 MiB. The
     steps are captured into HIP graphs (one graph per four sets) and replayed,
     so the timed region holds the kernels back to back, as the pages measure
     their operator (under CUDA Graph); --no-graph times direct calls. gate /
     init: calls through gtr_gla_fwd_ex with the RMSNorm + SiLU output gate and /
-    or an initial state (each set has its own)."""
+    or an initial state (each set has its own). lowrank: calls through
+    gtr_gla_fwd_lowrank, the gate computed from x [B, L, H d_v] by the rank-16
+    projection (each set has its own x; W1, W2 and the bias are shared)."""
     import numpy as np
     import torch
 
@@ -129,7 +144,7 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
     import gla_synth
 
     arrays = gla_synth.generate(w)
-    per_call = alg_bytes(w, gate, init)
+    per_call = alg_bytes(w, gate, init, lowrank)
     nsets = len(DIRS) * rotation_groups(per_call, steps, rotate)
     dev = torch.device("cuda:0")
     base = [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in arrays]
@@ -141,6 +156,11 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
         base.append(torch.from_numpy(0.5 * rng.standard_normal(
             (w.B, w.H, w.d_k, w.d_v)).astype(np.float32)).to(dev))
     norm_w = torch.from_numpy(rng.uniform(0.5, 1.5, w.d_v).astype(np.float32)).to(dev)
+    C = lowrank_features(w)
+    if lowrank:
+        x, w1, w2, gbias = [torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+                            for a in gla_synth.generate_lowrank(w, C, w.seed + 2000)]
+        base[3] = x   # log_gamma is not read; x takes its place in each set
     sets = []
     for i in range(nsets):
         ins = base if i == 0 else [t.clone() for t in base]
@@ -148,8 +168,8 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
         fs = torch.empty((w.B, w.H, w.d_k, w.d_v), dtype=torch.float32, device=dev)
         sets.append((ins, out, fs))
     is_fp32 = w.dtype == "fp32"
-    ws_bytes = gla.gtr_gla_workspace_bytes(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, w.chunk,
-                                           int(is_fp32))
+    ws_fn = gla.gtr_gla_lowrank_workspace_bytes if lowrank else gla.gtr_gla_workspace_bytes
+    ws_bytes = ws_fn(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, w.chunk, int(is_fp32))
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     gla.gtr_gla_workspace_init(ws, ws.numel())
     fn = gla.gtr_gla_fwd_f32_ws if is_fp32 else gla.gtr_gla_fwd_ws
@@ -157,7 +177,14 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
     def call(i, d):
         ins, out, fs = sets[i % nsets]
         q, k, v, lg = ins[:4]
-        if gate or init:
+        if lowrank:
+            z = ins[4] if gate else None
+            s0 = ins[-1] if init else None
+            gla.gtr_gla_fwd_lowrank(q, k, v, lg, w1, w2, gbias, 1.0 / 16, C, s0, z,
+                                    norm_w if gate else None, 1e-5, w.B, w.H, w.grid_h, w.grid_w,
+                                    w.d_k, w.d_v, d, w.chunk, int(is_fp32), out, fs, ws,
+                                    ws.numel())
+        elif gate or init:
             z = ins[4] if gate else None
             s0 = ins[-1] if init else None
             gla.gtr_gla_fwd_ex(q, k, v, lg, s0, z, norm_w if gate else None, 1e-5, w.B, w.H,
@@ -224,7 +251,7 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
             torch.cuda.synchronize()
             dir_us[("l2r", "r2l", "t2b", "b2t")[d]] = 1e3 * e0.elapsed_time(e1) / (reps * nsets)
     kern, span, grid = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, w.chunk,
-                                        int(is_fp32))
+                                        int(is_fp32), lowrank)
     return {
         "total_ms": total_ms,
         "ms_per_step": total_ms / steps,
@@ -323,7 +350,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="img640")
     ap.add_argument("--secondary",
-                    default="img1024,long2048,batched640,img640_dk32,img640+gate,long2048+gate",
+                    default="img1024,long2048,batched640,img640_dk32,img640+gate,long2048+gate,"
+                            "img640_dk32+lowrank,long2048+lowrank",
                     help="comma-separated extra workloads reported beside the main one "
                          "(NAME+gate: with the RMSNorm + SiLU output gate; NAME+init: from an "
                          "initial state)")
@@ -364,13 +392,13 @@ def main() -> int:
     traffic = measured_traffic(w.name)
     secondary = []
     for name in [s for s in args.secondary.split(",") if s and s != w.name]:
-        base_name, with_gate, with_init = split_name(name)
+        base_name, variant = split_name(name)
         ws = gla_synth.WORKLOADS[base_name]
         rs = run_workload(ws, max(20, args.steps // 4), args.warmup, rotate=not args.warm,
-                          use_graph=graph, gate=with_gate, init=with_init)
+                          use_graph=graph, **variant)
         gbs = rs["alg_bytes_per_call"] / (rs["call_us_mean"] * 1e-6) / 1e9
-        ceil_us = run_ceiling(ws, max(20, args.steps // 4), args.warmup) if not (
-            with_gate or with_init) else None
+        ceil_us = run_ceiling(ws, max(20, args.steps // 4), args.warmup) if not any(
+            variant.values()) else None
         secondary.append({
             "workload": name, "tokens_per_s": rs["tokens_per_s"], "ms_per_step": rs["ms_per_step"],
             "ceiling_us": ceil_us,

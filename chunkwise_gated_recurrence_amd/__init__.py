@@ -34,7 +34,7 @@ EXPORTED = (
     "gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_workspace_bytes", "gtr_gla_workspace_init",
     "gtr_gla_fwd_ws", "gtr_gla_fwd_f32_ws", "gtr_gla_fwd_ex", "gtr_gla_fwd_lowrank",
     "gtr_gla_lowrank_workspace_bytes", "gtr_gla_set_policy", "gtr_gla_get_policy",
-    "gtr_gla_plan", "gtr_gla_status_str",
+    "gtr_gla_plan", "gtr_gla_plan_lowrank", "gtr_gla_status_str",
 )
 
 
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     IP = ctypes.POINTER(ctypes.c_int)
     lib.gtr_gla_plan.argtypes = [I, I, I, I, I, I, I, I, IP, IP, IP]
     lib.gtr_gla_plan.restype = I
+    lib.gtr_gla_plan_lowrank.argtypes = [I, I, I, I, I, I, I, I, IP, IP, IP]
+    lib.gtr_gla_plan_lowrank.restype = I
     lib.gtr_gla_status_str.argtypes = [I]
     lib.gtr_gla_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -248,13 +250,17 @@ def gtr_gla_get_policy() -> int:
     return int(load_library().gtr_gla_get_policy())
 
 
-def gtr_gla_plan(B, H, grid_h, grid_w, d_k, d_v, chunk, is_fp32) -> Tuple[int, int, int]:
+def gtr_gla_plan(B, H, grid_h, grid_w, d_k, d_v, chunk, is_fp32,
+                 lowrank: bool = False) -> Tuple[int, int, int]:
     """(kernel, span, grid) of the launch a call would make: kernel 1 generic, 2 fused,
-    3 fused with the outputs kept in registers (long sequences)."""
+    3 fused with the outputs kept in registers (long sequences). lowrank: of a
+    gtr_gla_fwd_lowrank call (gtr_gla_plan_lowrank)."""
     kern, span, grid = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    r = load_library().gtr_gla_plan(B, H, grid_h, grid_w, d_k, d_v, chunk, int(is_fp32),
-                                    ctypes.byref(kern), ctypes.byref(span), ctypes.byref(grid))
-    _raise(r, "gtr_gla_plan")
+    lib = load_library()
+    fn = lib.gtr_gla_plan_lowrank if lowrank else lib.gtr_gla_plan
+    r = fn(B, H, grid_h, grid_w, d_k, d_v, chunk, int(is_fp32), ctypes.byref(kern),
+           ctypes.byref(span), ctypes.byref(grid))
+    _raise(r, "gtr_gla_plan_lowrank" if lowrank else "gtr_gla_plan")
     return kern.value, span.value, grid.value
 
 

@@ -220,7 +220,7 @@ struct FusedArgs {
     float eps;
     // log_gamma computed in the kernel from the low-rank gate (else read from lg):
     // lg = inv_tau * logsigmoid(z W2 + bias), z = x W1 per token
-    const float* z;             // [B, L, 16] x W1, each row stored permuted: z[4k + s] = (x W1)[4s + k]
+    const float* z;             // [B, L, 16] x W1
     const float* w2;            // [16, H * dk]
     const float* gbias;         // [H * dk]
     float inv_tau;
@@ -231,12 +231,15 @@ struct FusedArgs {
 // low-rank gate, the W2 operand table and the bias.
 extern __shared__ __align__(16) unsigned char smem_raw[];
 
-// Low-rank gate tables: the A operand of the 16x16x4 fp32 MFMA for each lane,
-// tile jt (16 key dims) and rank step s, with the tile's rows (dims) permuted
-// so that the product lands in the layout of the chunk operands (lane (r, g)
-// of a wave: row r, dims 8g + e + 32hh); and the bias per key dim.
+// Low-rank gate tables: the A operand of the 16x16x32 fp16 MFMA that forms
+// z W2 for tile jt (16 key dims), with the tile's rows (dims) permuted so that
+// the product lands in the layout of the chunk operands (lane (r, g) of a
+// wave: row r, dims 8g + e + 32hh); and the bias per key dim. W2 enters in two
+// fp16 parts, hi = fp16(W2) and lo = fp16(W2 - hi): the K = 32 of the MFMA
+// runs over (rank, part), lane (m, kb) holding ranks 8(kb & 1) .. + 7 of hi
+// (kb < 2) or of lo (kb >= 2) for dim col(m, jt).
 struct GateTab {
-    float w2[64][16];   // [lane][4 jt + s] = W2[4 s + (lane >> 4)][h dk + col(lane & 15, jt)]
+    h8 w2[4][64];       // [jt][lane]
     float bias[kD];
 };
 __device__ __forceinline__ int gate_col(int m, int jt)
@@ -250,10 +253,12 @@ __device__ __forceinline__ void fill_gate_tables(const FusedArgs& a, int h, int 
 {
     GateTab& gt = *reinterpret_cast<GateTab*>(smem_raw + a.gtab_off);
     const int K = a.H * a.dk;
-    for (int q = tid; q < 64 * 16; q += kThreads) {
-        const int ln = q >> 4, idx = q & 15, jt = idx >> 2, sg = idx & 3;
+    for (int q = tid; q < 4 * 64 * 8; q += kThreads) {
+        const int e = q & 7, ln = (q >> 3) & 63, jt = q >> 9, kb = ln >> 4;
         const int col = gate_col(ln & 15, jt);
-        gt.w2[ln][idx] = col < a.dk ? a.w2[(4 * sg + (ln >> 4)) * K + h * a.dk + col] : 0.f;
+        const float v = col < a.dk ? a.w2[(8 * (kb & 1) + e) * K + h * a.dk + col] : 0.f;
+        const _Float16 hi = (_Float16)v;
+        reinterpret_cast<_Float16*>(&gt.w2[jt][ln])[e] = kb < 2 ? hi : (_Float16)(v - (float)hi);
     }
     if (tid < kD) gt.bias[tid] = tid < a.dk ? a.gbias[h * a.dk + tid] : 0.f;
 }
@@ -285,7 +290,8 @@ struct Smem {
 
 
 struct ChunkRegs {
-    u4 q[2], k[2], v[2], g[2];
+    u4 q[2], k[2], v[2], g[2];   // g: log_gamma, or (low-rank gate) the row's z
+    bool valid;                  // low-rank gate: the row is a token of the sequence
 };
 
 // Row offset (halves) of scan step t of sequence (b, h); -1 past the end.
@@ -329,16 +335,18 @@ __device__ __forceinline__ u4 load16(__amdgpu_buffer_rsrc_t rs, int voff)
     return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, kNT));
 }
 
-// Low-rank gate input of scan step t for lane l: z[4(l >> 4) .. +3] of the
-// row (the B operand of the gate MFMAs); zeros past the sequence end.
-__device__ __forceinline__ u4 load_z(const FusedArgs& a, int b, int t, int lane)
+// Low-rank gate input of scan step t for lane l: z[8((l >> 4) & 1) .. +7] of
+// the row (the B operand of the gate MFMAs); zeros past the sequence end.
+__device__ __forceinline__ void load_z(const FusedArgs& a, int b, int t, int lane, u4 (&z)[2])
 {
     const int bytes = a.L * 64;
     const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.z + (long long)b * a.L * 16), (short)0, bytes, 0x00020000);
-    const int voff = t < a.L ? scan_to_spatial(t, a.L, a.grid_h, a.grid_w, a.dir) * 64 + 16 * (lane >> 4)
+    const int voff = t < a.L ? scan_to_spatial(t, a.L, a.grid_h, a.grid_w, a.dir) * 64 +
+                                   32 * ((lane >> 4) & 1)
                              : bytes;
-    return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rz, voff, 0, kNT));
+    z[0] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rz, voff, 0, kNT));
+    z[1] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rz, voff, 16, kNT));
 }
 
 // Lane l of wave w loads row 16w + (l & 15), dims 8(l >> 4) + 32h .. +7.
@@ -358,8 +366,8 @@ __device__ __forceinline__ void load_chunk(const FusedArgs& a, int b, int h, int
         if (!a.z) R.g[hh] = load16(rg, o.key);
     }
     if (a.z) {   // z, and whether the row is a token (rows past the end get no decay)
-        R.g[0] = load_z(a, b, t, lane);
-        R.g[1][0] = t < a.L;
+        load_z(a, b, t, lane, R.g);
+        R.valid = t < a.L;
     }
 }
 
@@ -444,32 +452,56 @@ struct NoHook {
 };
 
 // log_gamma of the lane's chunk operands (row r, dims 8g + e + 32hh) from the
-// low-rank gate: 16 MFMAs (4 dim tiles x 4 rank steps) of the permuted W2
-// table with z (the lane's z[4g .. 4g+3], zr), the bias as the accumulator's
-// start, then inv_tau * logsigmoid. A 32-wide key dim leaves dims 32..63 zero,
-// and so does a row past the sequence end (valid false: gamma = 1 there, as
-// the zero log_gamma that a read past the end gives on the other path).
-__device__ __forceinline__ void lowrank_gate(const FusedArgs& a, u4 zr, bool valid, int lane,
-                                             float (&x)[2][8])
+// low-rank gate: per dim tile, two 16x16x32 fp16 MFMAs of the W2 table with z
+// (z_hi twice, for W2_hi and W2_lo; then z_lo for W2_hi: the dropped
+// W2_lo z_lo is about 2^-22 of the product), the bias as the accumulator's
+// start, then inv_tau * logsigmoid. z holds the lane's ranks 8(g & 1) .. + 7.
+// A 32-wide key dim leaves dims 32..63 zero, and so does a row past the
+// sequence end (valid false: gamma = 1 there, as the zero log_gamma that a
+// read past the end gives on the other path).
+__device__ __forceinline__ void lowrank_gate(const FusedArgs& a, const u4 (&z)[2], bool valid,
+                                             int lane, float (&x)[2][8])
 {
     const GateTab& gt = *reinterpret_cast<const GateTab*>(smem_raw + a.gtab_off);
     const int g = lane >> 4;
+    h8 bh, bl;
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-        const int hh = jt >> 1, e0 = 4 * (jt & 1);
-        f4 acc = *reinterpret_cast<const f4*>(&gt.bias[8 * g + e0 + 32 * hh]);
-        const f4 wa = *reinterpret_cast<const f4*>(&gt.w2[lane][4 * jt]);
+    for (int e = 0; e < 8; ++e) {
+        const float v = __uint_as_float(z[e >> 2][e & 3]);
+        const _Float16 hi = (_Float16)v;
+        bh[e] = hi;
+        bl[e] = g < 2 ? (_Float16)(v - (float)hi) : (_Float16)0.f;
+    }
+    const float sc = valid ? a.inv_tau : 0.f;
+    // dims 32hh .. 32hh + 31: tiles 2hh and 2hh + 1
+    auto half = [&](int hh) {
+        f4 acc[2];
 #pragma unroll
-        for (int sg = 0; sg < 4; ++sg)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[sg], __uint_as_float(zr[sg]), acc, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float y = acc[e];
-            // log sigma(y) = min(y, 0) - ln(1 + e^{-|y|})
-            const float ls = fminf(y, 0.f) -
-                             0.69314718f * __builtin_amdgcn_logf(1.f + ex2(-kLog2e * fabsf(y)));
-            x[hh][e0 + e] = (valid && 8 * g + e0 + e + 32 * hh < a.dk) ? a.inv_tau * ls : 0.f;
+        for (int j = 0; j < 2; ++j) {
+            const int jt = 2 * hh + j;
+            acc[j] = *reinterpret_cast<const f4*>(&gt.bias[8 * g + 4 * j + 32 * hh]);
+            const h8 wa = gt.w2[jt][lane];
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, bh, acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, bl, acc[j], 0, 0, 0);
         }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float y = acc[j][e];
+                // log sigma(y) = min(y, 0) - ln(1 + e^{-|y|})
+                const float ls = fminf(y, 0.f) -
+                                 0.69314718f * __builtin_amdgcn_logf(1.f + ex2(-kLog2e * fabsf(y)));
+                x[hh][4 * j + e] = sc * ls;
+            }
+        }
+    };
+    half(0);
+    if (a.dk > 32) {
+        half(1);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[1][e] = 0.f;
     }
 }
 
@@ -485,7 +517,7 @@ __device__ __forceinline__ void chunk_front(const FusedArgs& a, Smem& sm, const 
     // -- log2 gates, inclusive prefix over the wave's 16 rows
     float x[2][8];
     if (a.z) {
-        lowrank_gate(a, R.g[0], R.g[1][0] != 0, lane, x);
+        lowrank_gate(a, R.g, R.valid, lane, x);
     } else {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) unpack8(R.g[hh], x[hh]);
@@ -1453,10 +1485,12 @@ gla_fused_rk_kernel(FusedArgs a)
             R.k[hh] = raw_ld(sk.raw[1], 16 * w + rr, 4 * hh + gg);
             R.v[hh] = raw_ld(sk.raw[2], 16 * w + rr, 4 * hh + gg);
         }
-        if (a.z) {   // z rows of the chunk: 16 floats per row, the lane's four at 4 gg
-            R.g[0] = *reinterpret_cast<const u4*>(reinterpret_cast<const float*>(sk.raw[0]) +
-                                                  (16 * w + rr) * 16 + 4 * gg);
-            R.g[1][0] = (c_first + c) * kC + 16 * w + rr < a.L;
+        if (a.z) {   // z rows of the chunk: 16 floats per row, the lane's eight at 8 (gg & 1)
+            const float* zr = reinterpret_cast<const float*>(sk.raw[0]) + (16 * w + rr) * 16 +
+                              8 * (gg & 1);
+            R.g[0] = *reinterpret_cast<const u4*>(zr);
+            R.g[1] = *reinterpret_cast<const u4*>(zr + 4);
+            R.valid = (c_first + c) * kC + 16 * w + rr < a.L;
         }
         h8 Qt[2];
         ChunkTmp T;

@@ -15,9 +15,7 @@ namespace gtrgla {
 constexpr int kRank = 16;
 
 // One thread per (token, rank index r): z[token][r] = sum_c x[token][c] W1[c][r],
-// fp32 accumulation; stored with the row permuted, r = 4s + k at 4k + s, the
-// order in which the fused kernels' MFMAs take it (a lane holds four
-// consecutive floats).
+// fp32 accumulation.
 template <typename T>
 __global__ void __launch_bounds__(256)
 lowrank_project_kernel(const T* __restrict__ x, const float* __restrict__ w1, size_t rows, int C,
@@ -29,7 +27,7 @@ lowrank_project_kernel(const T* __restrict__ x, const float* __restrict__ w1, si
     const T* xr = x + row * C;
     float acc = 0.f;
     for (int c = 0; c < C; ++c) acc += to_f32(xr[c]) * w1[(size_t)c * kRank + r];
-    z[row * kRank + 4 * (r & 3) + (r >> 2)] = acc;
+    z[row * kRank + r] = acc;
 }
 
 // The same for C a multiple of 4 16-byte vectors (and x 16-byte aligned): 64 tokens per workgroup,
@@ -68,16 +66,80 @@ lowrank_project_tiled_kernel(const T* __restrict__ x, const float* __restrict__ 
 #pragma unroll
     for (int r = 0; r < kRank; ++r) part[w][lane][r] = acc[r];
     __syncthreads();
-    // thread: token tid / 4, stored positions 4k .. 4k + 3 (k = tid % 4),
-    // i.e. rank indices r = 4s + k, s = 0 .. 3
+    // thread: token tid / 4, ranks 4k .. 4k + 3 (k = tid % 4)
     const int t = threadIdx.x >> 2, k = threadIdx.x & 3;
     if (r0 + t >= rows) return;
     float o[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        o[s] = part[0][t][4 * s + k] + part[1][t][4 * s + k] + part[2][t][4 * s + k] +
-               part[3][t][4 * s + k];
+        o[s] = part[0][t][4 * k + s] + part[1][t][4 * k + s] + part[2][t][4 * k + s] +
+               part[3][t][4 * k + s];
     *reinterpret_cast<float4*>(z + (r0 + t) * kRank + 4 * k) = make_float4(o[0], o[1], o[2], o[3]);
+}
+
+typedef _Float16 gh8 __attribute__((ext_vector_type(8)));
+typedef float gf4 __attribute__((ext_vector_type(4)));
+
+// fp16 x with C a multiple of 128 (and x 16-byte aligned): the product on
+// fp16 MFMA (16x16x32, fp32 accumulation), z^T = W1^T x^T for 32 tokens per
+// workgroup (two 16-token tiles per wave, sharing the W1 operand), wave w over
+// the w-th quarter of the features. x is exact in fp16; W1 enters as hi + lo,
+// two fp16 parts (hi = fp16(W1), lo = fp16(W1 - hi)), one MFMA each, which
+// keeps it to about 2^-22 of its value above fp16's normal range and to 2^-24
+// absolute below it. The A operand's row m is rank m, so each lane ends with
+// ranks 4g .. 4g + 3 of its token; the four quarters meet in LDS.
+constexpr int kProjTiles = 2;
+__global__ void __launch_bounds__(256)
+lowrank_project_mfma_kernel(const __half* __restrict__ x, const float* __restrict__ w1,
+                            size_t rows, int C, float* __restrict__ z)
+{
+    constexpr int T = kProjTiles;
+    __shared__ gf4 part[4][T][64];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, kb = lane >> 4;
+    const size_t r0 = (size_t)blockIdx.x * 16 * T;
+    const int cq = C >> 2;
+    const int c0 = w * cq + 8 * kb;
+    const float* wr = w1 + (size_t)c0 * kRank + n;
+    const _Float16* xr[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const size_t row = r0 + 16 * t + n < rows ? r0 + 16 * t + n : rows - 1;
+        xr[t] = reinterpret_cast<const _Float16*>(x) + row * C + c0;
+    }
+    gf4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = gf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int c = 0; c < cq; c += 32) {
+        gh8 b[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) b[t] = *reinterpret_cast<const gh8*>(xr[t] + c);
+        gh8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = wr[(size_t)(c + e) * kRank];
+            hi[e] = (_Float16)v;
+            lo[e] = (_Float16)(v - (float)hi[e]);
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, b[t], acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, b[t], acc[t], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) part[w][t][lane] = acc[t];
+    __syncthreads();
+    // thread o < 64 T: tile o / 64, lane o % 64 of the waves' results
+    const int o = threadIdx.x;
+    if (o >= 64 * T) return;
+    const int t = o >> 6, l = o & 63;
+    const size_t row = r0 + 16 * t + (l & 15);
+    if (row >= rows) return;
+    const gf4 s = part[0][t][l] + part[1][t][l] + part[2][t][l] + part[3][t][l];
+    *reinterpret_cast<gf4*>(z + row * kRank + 4 * (l >> 4)) = s;
 }
 
 // One thread per (token, key dim kk of all heads): log_gamma = inv_tau *
@@ -94,7 +156,7 @@ lowrank_log_gamma_kernel(const float* __restrict__ z, const float* __restrict__ 
     const int kk = (int)(idx - row * K);
     const float* zr = z + row * kRank;
     float y = bias[kk];
-    for (int r = 0; r < kRank; ++r) y += zr[4 * (r & 3) + (r >> 2)] * w2[(size_t)r * K + kk];
+    for (int r = 0; r < kRank; ++r) y += zr[r] * w2[(size_t)r * K + kk];
     const float ls = fminf(y, 0.f) - log1pf(expf(-fabsf(y)));
     lg[idx] = from_f32<T>(inv_tau * ls);
 }
@@ -103,8 +165,15 @@ hipError_t launch_lowrank_project(const void* x, bool is_fp32, const float* w1, 
                                   float* z, hipStream_t st)
 {
     if (rows == 0) return hipSuccess;
+    const bool aligned = ((uintptr_t)x & 15) == 0;
+    if (!is_fp32 && C % 128 == 0 && aligned) {
+        hipLaunchKernelGGL(lowrank_project_mfma_kernel,
+                           dim3((unsigned)((rows + 16 * kProjTiles - 1) / (16 * kProjTiles))),
+                           dim3(256), 0, st, (const __half*)x, w1, rows, C, z);
+        return hipGetLastError();
+    }
     const int vec = is_fp32 ? 4 : 8;
-    if (C % (4 * vec) == 0 && ((uintptr_t)x & 15) == 0) {
+    if (C % (4 * vec) == 0 && aligned) {
         const unsigned tiles = (unsigned)((rows + 63) / 64);
         if (is_fp32)
             hipLaunchKernelGGL(lowrank_project_tiled_kernel<float>, dim3(tiles), dim3(256), 0, st,

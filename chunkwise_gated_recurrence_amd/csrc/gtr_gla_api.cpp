@@ -433,17 +433,37 @@ int gtr_gla_set_policy(int policy)
 
 int gtr_gla_get_policy(void) { return current_policy(); }
 
-int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunk, int is_fp32,
-                 int* kernel_out, int* span_out, int* grid_out)
+}  // extern "C"
+
+namespace {
+int describe_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunk, int is_fp32,
+                  bool lowrank, int* kernel_out, int* span_out, int* grid_out)
 {
     Shape s;
     const int r = validate_sizes(B, H, grid_h, grid_w, d_k, d_v, 0, chunk, &s);
     if (r != GTR_GLA_OK) return r;
-    const Choice c = choose(s, is_fp32 != 0, current_policy());
+    const Choice c = choose(s, is_fp32 != 0, current_policy(), lowrank);
     if (kernel_out) *kernel_out = c.kernel == kFused && c.plan.rk ? kFusedRegisterKept : (int)c.kernel;
     if (span_out) *span_out = c.kernel == kFused ? c.plan.span : 1;
     if (grid_out) *grid_out = c.kernel == kFused ? c.plan.grid : B * H * s.n_chunks;
     return GTR_GLA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunk, int is_fp32,
+                 int* kernel_out, int* span_out, int* grid_out)
+{
+    return describe_plan(B, H, grid_h, grid_w, d_k, d_v, chunk, is_fp32, false, kernel_out,
+                         span_out, grid_out);
+}
+
+int gtr_gla_plan_lowrank(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunk,
+                         int is_fp32, int* kernel_out, int* span_out, int* grid_out)
+{
+    return describe_plan(B, H, grid_h, grid_w, d_k, d_v, chunk, is_fp32, true, kernel_out,
+                         span_out, grid_out);
 }
 
 const char* gtr_gla_status_str(int status)

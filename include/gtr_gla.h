@@ -203,6 +203,10 @@ int gtr_gla_get_policy(void);
  */
 int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunk,
                  int is_fp32, int* kernel_out, int* span_out, int* grid_out);
+/* gtr_gla_plan_lowrank -- the same for gtr_gla_fwd_lowrank, whose fused
+ * kernels hold the gate's tables in LDS as well (fewer may be resident).   */
+int gtr_gla_plan_lowrank(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunk,
+                         int is_fp32, int* kernel_out, int* span_out, int* grid_out);
 
 /* Static description of a status code. Never NULL. */
 const char* gtr_gla_status_str(int status);

@@ -88,7 +88,7 @@ def check(tag, w, d, o, s, o_ref, s_ref):
     eo, es = oracle.rel_err(o, o_ref), oracle.rel_err(s, s_ref)
     tol = TOL[w.dtype]
     say(f"[case] {tag} B={w.B} H={w.H} grid={w.grid_h}x{w.grid_w} d_k={w.d_k} {w.dtype} dir={d} "
-        f"plan={gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, w.chunk, int(w.dtype == 'fp32'))} "
+        f"plan={gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, w.chunk, int(w.dtype == 'fp32'), lowrank=True)} "
         f"err_o={eo:.3e} err_S={es:.3e} (tol {tol:g})")
     assert np.isfinite(o.astype(np.float64)).all() and np.isfinite(s).all()
     assert eo <= tol and es <= tol
@@ -121,9 +121,10 @@ def test_lowrank_gate(name, w, C, policy, span, rk, d):
     check(f"lowrank/{name}/C={C}", w, d, o, s, o_ref, s_ref)
 
 
-# feature widths: 1 and 36 take the plain projection kernel, 256 the tiled one;
-# an x that starts 2 bytes into its allocation takes the plain kernel too
-@pytest.mark.parametrize("C,x_offset", [(1, 0), (36, 0), (256, 0), (384, 1)])
+# feature widths: 1 and 36 take the plain projection kernel, 96 the tiled fp32
+# one, 256 (and 384, 768 above) the fp16 MFMA one; an x that starts 2 bytes
+# into its allocation takes the plain kernel too
+@pytest.mark.parametrize("C,x_offset", [(1, 0), (36, 0), (96, 0), (256, 0), (384, 1)])
 @pytest.mark.parametrize("name,w,_c,policy,span,rk", [CASES[0], CASES[4]],
                          ids=[CASES[0][0], CASES[4][0]])
 def test_lowrank_feature_widths(name, w, _c, policy, span, rk, C, x_offset):
