@@ -24,6 +24,10 @@ operator fuses (0539edu.com page, appendix E.3.1; ``rmsnorm_gate``)
 with gamma_t = exp(log_gamma_t) per key dimension, walked along one of four
 scan orders over the patch grid (same sections; see ``scan_order``).
 
+``sswiglu`` (module ``oracle.sswiglu``, numpy fp64) is the block's other
+token-grid operator, the Spatial SwiGLU channel mixer (same page, section
+前置知识 › SwiGLU前馈块), pinned in ``tests/test_oracle_sswiglu.py``.
+
 Pins: every function here is pinned by tests in ``tests/test_oracle.py`` against
 closed forms (causal linear attention, retention with a constant gate, the
 gamma -> 0 limit), hand-computed examples in ``tests/golden/``, the brute-force
