@@ -34,7 +34,8 @@ EXPORTED = (
     "gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_workspace_bytes", "gtr_gla_workspace_init",
     "gtr_gla_fwd_ws", "gtr_gla_fwd_f32_ws", "gtr_gla_fwd_ex", "gtr_gla_fwd_lowrank",
     "gtr_gla_lowrank_workspace_bytes", "gtr_gla_set_policy", "gtr_gla_get_policy",
-    "gtr_gla_plan", "gtr_gla_plan_lowrank", "gtr_gla_status_str",
+    "gtr_gla_plan", "gtr_gla_plan_lowrank", "gtr_gla_status_str", "gtr_sswiglu_fwd",
+    "gtr_sswiglu_workspace_bytes",
 )
 
 
@@ -84,6 +85,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gtr_gla_plan.restype = I
     lib.gtr_gla_plan_lowrank.argtypes = [I, I, I, I, I, I, I, I, IP, IP, IP]
     lib.gtr_gla_plan_lowrank.restype = I
+    lib.gtr_sswiglu_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, Z, P]
+    lib.gtr_sswiglu_fwd.restype = I
+    lib.gtr_sswiglu_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.gtr_sswiglu_workspace_bytes.restype = Z
     lib.gtr_gla_status_str.argtypes = [I]
     lib.gtr_gla_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -320,3 +325,39 @@ def forward_lowrank(q, k, v, x, w1, w2, gate_bias, grid_h: int, grid_w: int, dir
                         norm_weight, norm_eps, B, H, grid_h, grid_w, dk, dv, int(dir), chunk,
                         int(q.dtype == torch.float32), out, final_state, stream=stream)
     return out, final_state
+
+
+def gtr_sswiglu_fwd(x, w_g, w_v, conv_w, conv_b, w_o, B: int, grid_h: int, grid_w: int, C: int,
+                    Hd: int, y, workspace=None, workspace_bytes: int = 0, stream=None) -> None:
+    """Spatial SwiGLU: y = (SiLU(x w_g^T) * DWConv3x3(x w_v^T)) w_o^T (fp16 tensors,
+    fp32 convolution weights [Hd, 3, 3] and bias [Hd] or None)."""
+    import torch
+    if min(B, grid_h, grid_w, C, Hd) >= 1:
+        L = grid_h * grid_w
+        _check(x, "x", torch.float16, B * L * C)
+        _check(w_g, "w_g", torch.float16, Hd * C)
+        _check(w_v, "w_v", torch.float16, Hd * C)
+        _check(conv_w, "conv_w", torch.float32, Hd * 9)
+        _check(conv_b, "conv_b", torch.float32, Hd)
+        _check(w_o, "w_o", torch.float16, C * Hd)
+        _check(y, "y", torch.float16, B * L * C)
+    r = load_library().gtr_sswiglu_fwd(_ptr(x), _ptr(w_g), _ptr(w_v), _ptr(conv_w), _ptr(conv_b),
+                                       _ptr(w_o), B, grid_h, grid_w, C, Hd, _ptr(y),
+                                       _ptr(workspace), workspace_bytes, _stream(stream))
+    _raise(r, "gtr_sswiglu_fwd")
+
+
+def gtr_sswiglu_workspace_bytes(B: int, grid_h: int, grid_w: int, C: int, Hd: int) -> int:
+    return int(load_library().gtr_sswiglu_workspace_bytes(B, grid_h, grid_w, C, Hd))
+
+
+def sswiglu(x, w_g, w_v, conv_w, conv_b, w_o, grid_h: int, grid_w: int, y=None, stream=None):
+    """Allocate y (if not given) and run the Spatial SwiGLU mixer for x [B, L, C]."""
+    import torch
+    B, L, C = x.shape
+    Hd = w_g.shape[0]
+    if y is None:
+        y = torch.empty((B, L, w_o.shape[0]), dtype=x.dtype, device=x.device)
+    gtr_sswiglu_fwd(x, w_g, w_v, conv_w, conv_b, w_o, B, grid_h, grid_w, C, Hd, y,
+                    stream=stream)
+    return y

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(PKG, "libgtrgla.so")
 CEILING_PATH = os.path.join(PKG, "libgtrgla_ceiling.so")
 ARCH = "gfx950"
 
-SOURCES = ["gla_generic.hip", "gla_fused.hip", "gla_gate.hip", "gtr_gla_api.cpp"]
+SOURCES = ["gla_generic.hip", "gla_fused.hip", "gla_gate.hip", "sswiglu.hip", "gtr_gla_api.cpp",
+           "sswiglu_api.cpp"]
 
 # Packed fp32 instructions are turned off for every HIP translation unit.
 COMMON_FLAGS = [

@@ -43,8 +43,8 @@ struct Extras {
     const void* gate = nullptr;      // [B, L, H, d_v] in the input precision, or null
     const float* norm_w = nullptr;   // [d_v], with gate
     float eps = 0.f;
-    // low-rank gate: log_gamma computed from z = x W1 (fp32 [B, L, 16], rows
-    // permuted), W2 [16, H d_k], bias [H d_k] and 1/tau instead of read
+    // low-rank gate: log_gamma computed from z = x W1 (fp32 [B, L, 16]),
+    // W2 [16, H d_k], bias [H d_k] and 1/tau instead of read
     const float* z = nullptr;
     const float* w2 = nullptr;
     const float* gbias = nullptr;

@@ -37,13 +37,20 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
 // Zero fill by a kernel (graph-capturable); p must be 16-byte aligned.
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
 
-// Low-rank gate (gla_gate.hip): z = x W1 per token, [rows, 16] fp32 with each
-// row permuted (z[4k + s] = (x W1)[4s + k]); and log_gamma [rows, K] (K = H dk,
+// Low-rank gate (gla_gate.hip): z = x W1 per token, [rows, 16] fp32 in
+// natural rank order; and log_gamma [rows, K] (K = H dk,
 // the input precision) = inv_tau * logsigmoid(z W2 + bias) for the generic path.
 hipError_t launch_lowrank_project(const void* x, bool is_fp32, const float* w1, size_t rows, int C,
                                   float* z, hipStream_t st);
 hipError_t launch_lowrank_log_gamma(const float* z, const float* w2, const float* bias,
                                     float inv_tau, size_t rows, int K, bool is_fp32, void* lg,
                                     hipStream_t st);
+
+// Spatial SwiGLU: the up kernel (X W_g, X W_v over 8x8 tiles with their halo,
+// the 3x3 depthwise convolution, the bias and the SiLU gate) into a_ws
+// [B, L, Hd] fp16, then the down kernel y = a_ws W_o^T.
+hipError_t launch_sswiglu(const void* x, const void* wg, const void* wv, const float* cw,
+                          const float* cb, const void* wo, int B, int gh, int gw, int C, int Hd,
+                          void* y, void* a_ws, hipStream_t st);
 
 }  // namespace gtrgla

@@ -117,5 +117,25 @@ def generate_lowrank(w: Workload, C: int, seed: int, bias_std: float = 0.5
     return x, w1, w2, bias
 
 
+def generate_sswiglu(B: int, grid_h: int, grid_w: int, C: int, Hd: int, seed: int,
+                     bias: bool = True):
+    """Inputs of the Spatial SwiGLU mixer: (x, W_g, W_v, conv_w, conv_b, W_o).
+
+    x [B, L, C] standard normal (a layer-normed feature map); W_g, W_v [Hd, C]
+    normal with std 1/sqrt(C) and W_o [C, Hd] with std 1/sqrt(Hd) (unit-scale
+    activations at every stage), all rounded to fp16; conv_w [Hd, 3, 3] normal
+    with std 1/3 and conv_b [Hd] normal with std 0.1 (or None), float32.
+    """
+    rng = np.random.default_rng(seed)
+    L = grid_h * grid_w
+    x = rng.standard_normal((B, L, C), dtype=np.float32).astype(np.float16)
+    wg = (rng.standard_normal((Hd, C), dtype=np.float32) / np.float32(np.sqrt(C))).astype(np.float16)
+    wv = (rng.standard_normal((Hd, C), dtype=np.float32) / np.float32(np.sqrt(C))).astype(np.float16)
+    cw = (rng.standard_normal((Hd, 3, 3), dtype=np.float32) / np.float32(3.0)).astype(np.float32)
+    cb = (np.float32(0.1) * rng.standard_normal(Hd, dtype=np.float32)) if bias else None
+    wo = (rng.standard_normal((C, Hd), dtype=np.float32) / np.float32(np.sqrt(Hd))).astype(np.float16)
+    return x, wg, wv, cw, cb, wo
+
+
 def np_dtype(w: Workload):
     return np.float16 if w.dtype == "fp16" else np.float32

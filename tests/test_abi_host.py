@@ -9,7 +9,7 @@ import pytest
 import chunkwise_gated_recurrence_amd as gla
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gtr_gla.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gtr_gla.h", "gtr_sswiglu.h")]
 
 
 @pytest.fixture(scope="module")
@@ -21,14 +21,16 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(gtr_gla_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(gtr_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_api():
     names = declared_functions()
-    assert "gtr_gla_fwd" in names and "gtr_gla_fwd_ws" in names
+    assert "gtr_gla_fwd" in names and "gtr_gla_fwd_ws" in names and "gtr_sswiglu_fwd" in names
     assert set(names) == set(gla.EXPORTED)
 
 
@@ -206,3 +208,28 @@ def test_lowrank_workspace_size(lib):
     n = lib.gtr_gla_lowrank_workspace_bytes(B, H, gh, gw, dk, dv, 64, 1)
     assert n == up(base) + up(rows * 16 * 4) + up(rows * H * dk * 4)
     assert lib.gtr_gla_lowrank_workspace_bytes(0, H, gh, gw, dk, dv, 64, 1) == 0
+
+
+def _ss(lib, x=BASE, wg=BASE + SEP, wv=BASE + 2 * SEP, cw=BASE + 3 * SEP, cb=BASE + 4 * SEP,
+        wo=BASE + 5 * SEP, y=BASE + 6 * SEP, B=1, gh=4, gw=5, C=64, Hd=128, ws=None, nws=0):
+    return lib.gtr_sswiglu_fwd(x, wg, wv, cw, cb, wo, B, gh, gw, C, Hd, y, ws, nws, None)
+
+
+def test_sswiglu_checks():
+    """gtr_sswiglu_fwd: required pointers, sizes (C, Hd multiples of 64), aliasing of y
+    and of a caller workspace, workspace size; nothing launches on a failed check."""
+    lib = gla.load_library()
+    for name in ("x", "wg", "wv", "cw", "wo", "y"):
+        assert _ss(lib, **{name: None}) == gla.ERR_NULL, name
+    for kw in (dict(B=0), dict(gh=0), dict(gw=-1), dict(C=0), dict(Hd=0)):
+        assert _ss(lib, **kw) == gla.ERR_SHAPE, kw
+    for kw in (dict(C=96), dict(Hd=100), dict(C=8256), dict(gh=1 << 15, gw=1 << 15)):
+        assert _ss(lib, **kw) == gla.ERR_UNSUPPORTED, kw
+    assert _ss(lib, y=BASE + 64) == gla.ERR_ALIAS
+    assert _ss(lib, y=BASE + 5 * SEP + 2) == gla.ERR_ALIAS
+    n = lib.gtr_sswiglu_workspace_bytes(2, 4, 5, 64, 128)
+    assert n == 2 * 20 * 128 * 2
+    assert lib.gtr_sswiglu_workspace_bytes(2, 4, 5, 96, 128) == 0
+    assert _ss(lib, B=2, ws=BASE + 8 * SEP, nws=n - 1) == gla.ERR_WORKSPACE
+    assert _ss(lib, B=2, ws=BASE + 6 * SEP + 16, nws=n) == gla.ERR_ALIAS
+    assert _ss(lib, B=2, ws=BASE + 16, nws=n) == gla.ERR_ALIAS
