@@ -267,6 +267,76 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
     }
 
 
+# Spatial SwiGLU workloads: (B, grid_h, grid_w, C, Hd) -- GTR-L's width (C = 384,
+# Hd = 4 C) at 640x640 and 1024x1024 input
+SSWIGLU_WORKLOADS = {
+    "sswiglu640": (1, 40, 40, 384, 1536),
+    "sswiglu1024": (1, 64, 64, 384, 1536),
+}
+
+
+def run_sswiglu(name: str, steps: int, warmup: int, rotate: bool = True):
+    """Time the Spatial SwiGLU mixer like the token mixer: four calls per step (four
+    blocks), each with its own input and weights, sets rotated over >= 512 MiB, all
+    steps in one HIP graph. Returns a dict with us per call, TFLOP/s and MFMA fraction."""
+    import numpy as np
+    import torch
+
+    import chunkwise_gated_recurrence_amd as gla
+    import gla_synth
+
+    B, gh, gw, C, Hd = SSWIGLU_WORKLOADS[name]
+    L = gh * gw
+    dev = torch.device("cuda:0")
+    base = [None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+            for a in gla_synth.generate_sswiglu(B, gh, gw, C, Hd, seed=21)]
+    per_call = (2 * B * L * C + 3 * Hd * C) * 2 + Hd * 40
+    nsets = len(DIRS) * rotation_groups(per_call, steps, rotate)
+    sets = []
+    for i in range(nsets):
+        ins = base if i == 0 else [t.clone() for t in base]
+        sets.append((ins, torch.empty((B, L, C), dtype=torch.float16, device=dev)))
+    nws = gla.gtr_sswiglu_workspace_bytes(B, gh, gw, C, Hd)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+    def call(i):
+        ins, y = sets[i % nsets]
+        gla.gtr_sswiglu_fwd(*ins, B, gh, gw, C, Hd, y, workspace=ws, workspace_bytes=nws)
+
+    for i in range(len(DIRS)):
+        call(i)
+    torch.cuda.synchronize()
+    n_groups = nsets // len(DIRS)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(nsets):
+            call(i)
+    torch.cuda.synchronize()
+    reps_w = max(1, (warmup + n_groups - 1) // n_groups)
+    reps = max(1, (steps + n_groups - 1) // n_groups)
+    for _ in range(reps_w):
+        graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / (reps * nsets)
+    flops = 6 * B * L * C * Hd
+    return {
+        "workload": name, "B": B, "grid": f"{gh}x{gw}", "C": C, "Hd": Hd,
+        "call_us_mean": us, "tokens_per_s": B * L / (us * 1e-6),
+        "flop_per_call": flops, "TFLOPs": flops / (us * 1e-6) / 1e12,
+        "mfma_frac": flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+        "alg_bytes_per_call": per_call,
+        "kernels": "sswiglu_up_kernel + sswiglu_down_kernel",
+    }
+
+
 def run_ceiling(w, steps: int, warmup: int):
     """Practical ceiling: a plain streaming kernel (libgtrgla_ceiling.so) that reads four
     fp16 tensors and writes one, each of the workload's [B, L, H, 64] size, i.e. the
@@ -355,6 +425,8 @@ def main() -> int:
                     help="comma-separated extra workloads reported beside the main one "
                          "(NAME+gate: with the RMSNorm + SiLU output gate; NAME+init: from an "
                          "initial state)")
+    ap.add_argument("--sswiglu", default="sswiglu640,sswiglu1024",
+                    help="Spatial SwiGLU workloads to time as well (comma list, may be empty)")
     ap.add_argument("--warm", action="store_true", help="reuse one input set (cache-warm)")
     ap.add_argument("--no-graph", action="store_true", help="time direct calls, not graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -408,6 +480,9 @@ def main() -> int:
             "traffic": measured_traffic(name),
         })
 
+    mixer = [run_sswiglu(name, max(20, args.steps // 4), args.warmup, rotate=not args.warm)
+             for name in args.sswiglu.split(",") if name]
+
     ceil_us = run_ceiling(w, max(20, args.steps // 4), args.warmup)
     ceiling = {
         "kind": "plain streaming kernel: read 4 fp16 tensors, write 1 (the operator's q, k, v, "
@@ -453,6 +528,7 @@ def main() -> int:
         },
         "ceiling": ceiling,
         "secondary": secondary,
+        "spatial_swiglu": mixer,
         "kernel_hash": kernel_hash(),
     }
     if not args.no_cpu_baseline:

@@ -35,16 +35,19 @@ constexpr int kTileSide = 8;          // core tile: 8 x 8 tokens
 constexpr int kHaloTokens = 100;      // 10 x 10
 constexpr int kRowBlocks = 7;         // MFMA row blocks over the halo (112 rows)
 constexpr int kStageRows = 128;       // X rows staged per step (8 DMA instructions; 112..127 zero)
-constexpr int kSlice = 64;            // hidden channels per workgroup, 16 per wave
-constexpr int kUpStages = 3;          // DMA ring depth of the up kernel
+constexpr int kSlice = 128;           // hidden channels per workgroup, 32 per wave
+constexpr int kWaveCh = kSlice / 4;
+constexpr int kNB = kWaveCh / 16;     // MFMA column blocks per wave
+constexpr int kUpStages = 3;          // DMA ring depth of the up kernel (two workgroups per CU)
 constexpr int kStages = 4;            // DMA ring depth of the down kernel
-// bytes per up-kernel stage (32 features): the X rows, then the W_g and W_v
-// rows of the slice's 64 channels (64 bytes per row each)
-constexpr int kUpStage = kStageRows * 64 + 2 * kSlice * 64;
-constexpr int kHvStride = 17;                      // floats per H_v row in the epilogue
+// bytes per up-kernel stage (32 features): the X rows, then the W_g rows and
+// the W_v rows of the slice's channels (64 bytes per row each)
+constexpr int kUpX = kStageRows * 64;
+constexpr int kUpStage = kUpX + 2 * kSlice * 64;
+constexpr int kHvStride = kWaveCh + 1;             // floats per H_v row in the epilogue
 constexpr int kOtStride = kSlice + 8;              // halves per row of the output tile
-constexpr int kUpHvBytes = 4 * 112 * kHvStride * 4;
-constexpr int kUpLds = kUpHvBytes + 64 * kOtStride * 2;   // epilogue (>= the ring)
+constexpr int kUpHvBytes = 4 * kHaloTokens * kHvStride * 4;
+constexpr int kUpLds = kUpHvBytes + 64 * kOtStride * 2;   // epilogue
 constexpr int kUpRing = kUpStages * kUpStage;
 constexpr int kUpLdsAll = kUpLds > kUpRing ? kUpLds : kUpRing;   // the epilogue reuses the ring
 constexpr int kDownStage = 2 * 64 * 128;           // A and W_o tiles, 64 features each
@@ -69,18 +72,10 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Halo rows: the 64 core tokens first (row-major), then the ring: the row
-// above and the row below (10 each, left to right), the column left and the
-// column right (8 each). (hi, hj) in [-1, 8] relative to the tile corner.
-__device__ __forceinline__ int halo_row(int hi, int hj)
-{
-    if (hi >= 0 && hi < kTileSide && hj >= 0 && hj < kTileSide) return kTileSide * hi + hj;
-    if (hi < 0) return 64 + hj + 1;
-    if (hi >= kTileSide) return 74 + hj + 1;
-    if (hj < 0) return 84 + hi;
-    return 92 + hi;
-}
-
+// Halo rows (the MFMA row order of the halo tile): the 64 core tokens first
+// (row-major), then the ring: the row above and the row below (10 each, left
+// to right), the column left and the column right (8 each). halo_coord gives
+// (hi, hj) in [-1, 8] relative to the tile corner for row r < 100.
 __device__ __forceinline__ void halo_coord(int r, int& hi, int& hj)
 {
     if (r < 64) {
@@ -147,14 +142,10 @@ __global__ void __launch_bounds__(256) sswiglu_up_kernel(SsUpArgs p)
     // DMA of one step (32 features = 64 bytes per row): instruction i covers
     // rows 16i .. 16i + 15, lane l row 16i + (l >> 2) into slot l & 3, which
     // holds the row's piece (l & 3) ^ ((row >> 2) & 3) (conflict-free reads).
-    // Wave w issues X instructions i = w and w + 4, and the W_g and W_v rows of
-    // its own 16 channels. Rows past the halo, or tokens off the grid, read
-    // past the resource: zeros.
+    // Wave w issues instructions i = w and w + 4. Rows past the halo, or
+    // tokens off the grid, read past the resource: zeros.
     const int n = lane & 15, kb = lane >> 4;
-    const int wrow = lane >> 2, wpiece = (lane & 3) ^ ((wrow >> 2) & 3);
-    const unsigned wbytes = (unsigned)p.Hd * (unsigned)p.C * 2u;
-    const __amdgpu_buffer_rsrc_t rg = rsrc_bytes(p.wg, wbytes), rv = rsrc_bytes(p.wv, wbytes);
-    const unsigned vwo = (unsigned)(slice * kSlice + 16 * w + wrow) * (unsigned)p.C * 2u + 16u * wpiece;
+    const int ch0 = slice * kSlice + kWaveCh * w;   // the wave's first channel
     unsigned voff[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -170,80 +161,132 @@ __global__ void __launch_bounds__(256) sswiglu_up_kernel(SsUpArgs p)
         }
         voff[j] = v;
     }
-    auto issue = [&](int s) {
-        unsigned char* slot = lds + (s % kUpStages) * kUpStage;
+    // The W_g and W_v rows of the wave's own channels go through the same
+    // ring: kNB instructions each (rows ch0 + 16c + (l >> 2), same swizzle).
+    const unsigned wbytes = (unsigned)p.Hd * (unsigned)p.C * 2u;
+    const __amdgpu_buffer_rsrc_t rg = rsrc_bytes(p.wg, wbytes), rv = rsrc_bytes(p.wv, wbytes);
+    const int wrow = lane >> 2, wpiece = (lane & 3) ^ ((wrow >> 2) & 3);
+    const unsigned vwo = (unsigned)(ch0 + wrow) * (unsigned)p.C * 2u + 16u * wpiece;
+    constexpr int kPerStage = 2 + 2 * kNB;   // DMA instructions per wave and stage
+    const int nk = p.C >> 5;
+    // Stage t into slot t % kUpStages; stages past nk read past the resources
+    // (zeros) into slots no step reads, so that every step issues the same
+    // instructions and waits for the same count.
+    auto issue = [&](int t) {
+        const bool in = t < nk;
+        unsigned char* slot = lds + (t % kUpStages) * kUpStage;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dma16(rx, slot + (w + 4 * j) * 1024, voff[j] + 64u * s);
-        dma16(rg, slot + kStageRows * 64 + w * 1024, vwo + 64u * s);
-        dma16(rv, slot + kStageRows * 64 + (4 + w) * 1024, vwo + 64u * s);
+        for (int j = 0; j < 2; ++j) dma16(rx, slot + (w + 4 * j) * 1024, in ? voff[j] + 64u * t : xbytes);
+#pragma unroll
+        for (int c = 0; c < kNB; ++c) {
+            const unsigned o = in ? vwo + (unsigned)(16 * c) * (unsigned)p.C * 2u + 64u * t : wbytes;
+            dma16(rg, slot + kUpX + (kNB * w + c) * 1024, o);
+            dma16(rv, slot + kUpX + (4 * kNB + kNB * w + c) * 1024, o);
+        }
     };
 
-    const int ch = slice * kSlice + 16 * w + n;
-    // the lane's convolution taps and bias (used after the loop)
-    float tap[9];
+    // the lane's convolution taps and bias for each of its channels (used after the loop)
+    float tap[kNB][9], bias[kNB];
 #pragma unroll
-    for (int t = 0; t < 9; ++t) tap[t] = p.cw[(size_t)ch * 9 + t];
-    const float bias = p.cb ? p.cb[ch] : 0.f;
-
-    const int nk = p.C >> 5;
-    sf4 accv[kRowBlocks], accg[4];
+    for (int c = 0; c < kNB; ++c) {
+        const int ch = ch0 + 16 * c + n;
 #pragma unroll
-    for (int i = 0; i < kRowBlocks; ++i) accv[i] = sf4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) accg[i] = sf4{0.f, 0.f, 0.f, 0.f};
-
-    for (int s = 0; s < kUpStages - 1 && s < nk; ++s) issue(s);
-    // the fragments of row block i: row 16i + n, piece kb
-    const int frag = n * 64 + 16 * (kb ^ ((n >> 2) & 3));
-    for (int s = 0; s < nk; ++s) {
-        // stage s has landed once only the later stages (four DMA instructions
-        // per wave each) are in flight
-        if (s + 1 < nk) wait_vm<4 * (kUpStages - 2)>();
-        else wait_vm<0>();
-        lds_sync();
-        if (s + kUpStages - 1 < nk) issue(s + kUpStages - 1);   // into the slot read at s - 1
-        const unsigned char* slot = lds + (s % kUpStages) * kUpStage;
-        const sh8 bg = *reinterpret_cast<const sh8*>(slot + kStageRows * 64 + w * 1024 + frag);
-        const sh8 bv = *reinterpret_cast<const sh8*>(slot + kStageRows * 64 + (4 + w) * 1024 + frag);
-#pragma unroll
-        for (int i = 0; i < kRowBlocks; ++i) {
-            const sh8 a = *reinterpret_cast<const sh8*>(slot + i * 1024 + frag);
-            accv[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv, accv[i], 0, 0, 0);
-            if (i < 4) accg[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bg, accg[i], 0, 0, 0);
-        }
+        for (int t = 0; t < 9; ++t) tap[c][t] = p.cw[(size_t)ch * 9 + t];
+        bias[c] = p.cb ? p.cb[ch] : 0.f;
     }
-    lds_sync();   // every wave is done with the ring
 
-    // X W_v of the wave's 16 channels over the halo, to LDS for the neighbours
-    float* hv = reinterpret_cast<float*>(lds) + w * 112 * kHvStride;
+    sf4 accv[kRowBlocks][kNB], accg[4][kNB];
 #pragma unroll
     for (int i = 0; i < kRowBlocks; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hv[(16 * i + 4 * kb + e) * kHvStride + n] = accv[i][e];
+        for (int c = 0; c < kNB; ++c) accv[i][c] = sf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < kNB; ++c) accg[i][c] = sf4{0.f, 0.f, 0.f, 0.f};
+
+    // the fragments of a 16-row block: row n, piece kb
+    const int frag = n * 64 + 16 * (kb ^ ((n >> 2) & 3));
+#pragma unroll
+    for (int t = 0; t < kUpStages - 1; ++t) issue(t);
+    for (int s = 0; s < nk; ++s) {
+        // stage s has landed once only the kUpStages - 2 later stages are in flight
+        wait_vm<kPerStage * (kUpStages - 2)>();
+        lds_sync();
+        issue(s + kUpStages - 1);   // into the slot read at s - 1
+        const unsigned char* slot = lds + (s % kUpStages) * kUpStage;
+        sh8 a[kRowBlocks], bg[kNB], bv[kNB];
+#pragma unroll
+        for (int c = 0; c < kNB; ++c) {
+            bg[c] = *reinterpret_cast<const sh8*>(slot + kUpX + (kNB * w + c) * 1024 + frag);
+            bv[c] = *reinterpret_cast<const sh8*>(slot + kUpX + (4 * kNB + kNB * w + c) * 1024 + frag);
+        }
+#pragma unroll
+        for (int i = 0; i < kRowBlocks; ++i) a[i] = *reinterpret_cast<const sh8*>(slot + i * 1024 + frag);
+#pragma unroll
+        for (int i = 0; i < kRowBlocks; ++i)
+#pragma unroll
+            for (int c = 0; c < kNB; ++c) {
+                accv[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bv[c], accv[i][c], 0, 0, 0);
+                if (i < 4)
+                    accg[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bg[c], accg[i][c], 0, 0, 0);
+            }
+    }
+    wait_vm<0>();   // the stages issued past the end land before the LDS is reused
+    lds_sync();   // every wave is done with the ring
+
+    // X W_v of the wave's channels to LDS as the 10 x 10 halo grid (position
+    // (hi + 1) * 10 + hj + 1), so that the neighbours are at fixed offsets
+    float* hv = reinterpret_cast<float*>(lds) + w * kHaloTokens * kHvStride;
+#pragma unroll
+    for (int i = 0; i < kRowBlocks; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * i + 4 * kb + e;
+            if (row < kHaloTokens) {
+                int hi, hj;
+                halo_coord(row, hi, hj);
+                float* d = hv + ((hi + 1) * 10 + hj + 1) * kHvStride + n;
+#pragma unroll
+                for (int c = 0; c < kNB; ++c) d[16 * c] = accv[i][c][e];
+            }
+        }
     lds_sync();
+    // The lane's core tokens of row block i are four neighbours in one row:
+    // (hi, hj0 + e) with hi = 2i + (kb >> 1), hj0 = 4 (kb & 1); their 3 x 3
+    // windows lie in the 3 x 6 block of the grid at (hi, hj0).
     _Float16* ot = reinterpret_cast<_Float16*>(lds + kUpHvBytes);   // [64][kOtStride]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        const int hi = 2 * i + (kb >> 1), hj0 = 4 * (kb & 1);
+        const float* wbase = hv + (hi * 10 + hj0) * kHvStride + n;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * i + 4 * kb + e;   // core token (r >> 3, r & 7)
-            const int hi = r >> 3, hj = r & 7;
-            float conv = bias;
+        for (int c = 0; c < kNB; ++c) {
+            float win[3][6];
 #pragma unroll
-            for (int di = 0; di < 3; ++di)
+            for (int a = 0; a < 3; ++a)
 #pragma unroll
-                for (int dj = 0; dj < 3; ++dj)
-                    conv += tap[3 * di + dj] * hv[halo_row(hi + di - 1, hj + dj - 1) * kHvStride + n];
-            ot[r * kOtStride + 16 * w + n] = (_Float16)(silu(accg[i][e]) * conv);
+                for (int bb = 0; bb < 6; ++bb) win[a][bb] = wbase[(10 * a + bb) * kHvStride + 16 * c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float conv = bias[c];
+#pragma unroll
+                for (int a = 0; a < 3; ++a)
+#pragma unroll
+                    for (int bb = 0; bb < 3; ++bb) conv += tap[c][3 * a + bb] * win[a][e + bb];
+                ot[(16 * i + 4 * kb + e) * kOtStride + kWaveCh * w + 16 * c + n] =
+                    (_Float16)(silu(accg[i][c][e]) * conv);
+            }
         }
     }
     lds_sync();
-    // 64 tokens x 64 channels, 16 bytes per thread and piece
+    // 64 tokens x kSlice channels, 16 bytes per thread and piece
     const size_t abase = (size_t)b * L;
+    constexpr int kParts = kSlice / 8;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 64 * kParts / 256; ++j) {
         const int q = tid + 256 * j;
-        const int r = q >> 3, part = q & 7;
+        const int r = q / kParts, part = q % kParts;
         const int gi = ti0 + (r >> 3), gj = tj0 + (r & 7);
         if (gi < p.gh && gj < p.gw) {
             const sh8 v = *reinterpret_cast<const sh8*>(ot + r * kOtStride + 8 * part);

@@ -24,7 +24,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 int validate(int B, int gh, int gw, int C, int Hd)
 {
     if (B < 1 || gh < 1 || gw < 1 || C < 1 || Hd < 1) return GTR_GLA_ERR_SHAPE;
-    if (C % 64 != 0 || Hd % 64 != 0 || C > 8192 || Hd > 32768) return GTR_GLA_ERR_UNSUPPORTED;
+    if (C % 64 != 0 || Hd % 128 != 0 || C > 8192 || Hd > 32768) return GTR_GLA_ERR_UNSUPPORTED;
     const long long L = (long long)gh * gw;
     const long long lim = 1LL << 31;
     if (L * C * 2 >= lim || (long long)B * L * Hd * 2 >= lim || (long long)B * L >= lim)

@@ -26,7 +26,7 @@
  * chip, the convolution and the gate are fp32, the gated hidden tile is
  * rounded to fp16 once (the workspace) before the output product.
  *
- * Sizes: B, grid_h, grid_w >= 1; C and Hd multiples of 64 (C <= 8192,
+ * Sizes: B, grid_h, grid_w >= 1; C a multiple of 64 and Hd of 128 (C <= 8192,
  * Hd <= 32768); each of x, y and the hidden tensor [B, L, Hd] under 2^31
  * bytes per batch entry (hidden: in total). Else GTR_GLA_ERR_UNSUPPORTED
  * (GTR_GLA_ERR_SHAPE for sizes < 1).

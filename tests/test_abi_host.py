@@ -223,13 +223,14 @@ def test_sswiglu_checks():
         assert _ss(lib, **{name: None}) == gla.ERR_NULL, name
     for kw in (dict(B=0), dict(gh=0), dict(gw=-1), dict(C=0), dict(Hd=0)):
         assert _ss(lib, **kw) == gla.ERR_SHAPE, kw
-    for kw in (dict(C=96), dict(Hd=100), dict(C=8256), dict(gh=1 << 15, gw=1 << 15)):
+    for kw in (dict(C=96), dict(Hd=100), dict(Hd=192), dict(C=8256), dict(gh=1 << 15, gw=1 << 15)):
         assert _ss(lib, **kw) == gla.ERR_UNSUPPORTED, kw
     assert _ss(lib, y=BASE + 64) == gla.ERR_ALIAS
     assert _ss(lib, y=BASE + 5 * SEP + 2) == gla.ERR_ALIAS
     n = lib.gtr_sswiglu_workspace_bytes(2, 4, 5, 64, 128)
     assert n == 2 * 20 * 128 * 2
     assert lib.gtr_sswiglu_workspace_bytes(2, 4, 5, 96, 128) == 0
+    assert lib.gtr_sswiglu_workspace_bytes(2, 4, 5, 64, 64) == 0
     assert _ss(lib, B=2, ws=BASE + 8 * SEP, nws=n - 1) == gla.ERR_WORKSPACE
     assert _ss(lib, B=2, ws=BASE + 6 * SEP + 16, nws=n) == gla.ERR_ALIAS
     assert _ss(lib, B=2, ws=BASE + 16, nws=n) == gla.ERR_ALIAS

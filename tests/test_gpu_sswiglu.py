@@ -29,10 +29,10 @@ CASES = [
     ("ragged-S", 2, 30, 34, 192, 768, True),
     ("ratio6-X", 1, 24, 20, 384, 2304, True),
     ("no-bias", 1, 17, 23, 128, 256, False),
-    ("grid-1x1", 1, 1, 1, 64, 64, True),
+    ("grid-1x1", 1, 1, 1, 64, 128, True),
     ("grid-1x9", 2, 1, 9, 64, 128, True),
-    ("grid-9x1", 1, 9, 1, 64, 64, True),
-    ("grid-3x3", 3, 3, 3, 64, 192, True),
+    ("grid-9x1", 1, 9, 1, 64, 256, True),
+    ("grid-3x3", 3, 3, 3, 64, 384, True),
 ]
 
 
