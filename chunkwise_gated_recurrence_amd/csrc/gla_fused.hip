@@ -1193,10 +1193,14 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
 }
 
 // ---------------------------------------------------------------------------
-template <int SPAN, bool KEEP>
+// LR: the low-rank gate variant. Without it the kernel's copy of the
+// arguments has a null z, a constant that removes every low-rank branch.
+template <int SPAN, bool KEEP, bool LR>
 __global__ void __launch_bounds__(kThreads, 3)
-gla_fused_kernel(FusedArgs a)
+gla_fused_kernel(FusedArgs a_arg)
 {
+    FusedArgs a = a_arg;
+    if (!LR) a.z = nullptr;
     static_assert(!KEEP || SPAN <= kMaxKeep, "a kept span holds at most kMaxKeep chunks");
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
 
@@ -1426,10 +1430,12 @@ __device__ __forceinline__ void load_q(const FusedArgs& a, int b, int h, int t0,
     for (int hh = 0; hh < 2; ++hh) q[hh] = load16(rq, row_off(a, h, t, (lane >> 4) + 4 * hh).key);
 }
 
-template <int SPAN>
+template <int SPAN, bool LR>
 __global__ void __launch_bounds__(kThreads, 2)
-gla_fused_rk_kernel(FusedArgs a)
+gla_fused_rk_kernel(FusedArgs a_arg)
 {
+    FusedArgs a = a_arg;
+    if (!LR) a.z = nullptr;
     static_assert(SPAN >= 2 && SPAN <= kMaxKeep, "register-kept spans hold 2 .. kMaxKeep chunks");
     SmemRK& sk = *reinterpret_cast<SmemRK*>(smem_raw);
     Smem& sm = sk.s;
@@ -1619,25 +1625,30 @@ static int device_cus()
 static bool keep_span_ok(int span) { return span == 1 || span == 2 || span == 4 || span == 8; }
 static bool rk_span_ok(int span) { return span >= 2 && span <= 7; }
 
-static const void* pick_kernel(int span, bool keep, bool rk)
+template <bool LR>
+static const void* pick_variant(int span, bool keep, bool rk)
 {
     if (rk) {
         switch (span) {
-        case 2: return (const void*)gla_fused_rk_kernel<2>;
-        case 3: return (const void*)gla_fused_rk_kernel<3>;
-        case 4: return (const void*)gla_fused_rk_kernel<4>;
-        case 5: return (const void*)gla_fused_rk_kernel<5>;
-        case 6: return (const void*)gla_fused_rk_kernel<6>;
-        default: return (const void*)gla_fused_rk_kernel<7>;
+        case 2: return (const void*)gla_fused_rk_kernel<2, LR>;
+        case 3: return (const void*)gla_fused_rk_kernel<3, LR>;
+        case 4: return (const void*)gla_fused_rk_kernel<4, LR>;
+        case 5: return (const void*)gla_fused_rk_kernel<5, LR>;
+        case 6: return (const void*)gla_fused_rk_kernel<6, LR>;
+        default: return (const void*)gla_fused_rk_kernel<7, LR>;
         }
     }
-    if (!keep) return (const void*)gla_fused_kernel<1, false>;
+    if (!keep) return (const void*)gla_fused_kernel<1, false, LR>;
     switch (span) {
-    case 1: return (const void*)gla_fused_kernel<1, true>;
-    case 2: return (const void*)gla_fused_kernel<2, true>;
-    case 4: return (const void*)gla_fused_kernel<4, true>;
-    default: return (const void*)gla_fused_kernel<8, true>;
+    case 1: return (const void*)gla_fused_kernel<1, true, LR>;
+    case 2: return (const void*)gla_fused_kernel<2, true, LR>;
+    case 4: return (const void*)gla_fused_kernel<4, true, LR>;
+    default: return (const void*)gla_fused_kernel<8, true, LR>;
     }
+}
+static const void* pick_kernel(int span, bool keep, bool rk, bool lowrank)
+{
+    return lowrank ? pick_variant<true>(span, keep, rk) : pick_variant<false>(span, keep, rk);
 }
 
 // Dynamic LDS: the variant's Smem, then (low-rank gate) the gate tables.
@@ -1653,7 +1664,7 @@ static int resident_per_cu(int span, bool keep, bool rk, bool lowrank)
     static int cache[2][3][kMaxKeep + 1] = {};
     int& c = cache[lowrank ? 1 : 0][rk ? 2 : (keep ? 1 : 0)][(keep || rk) ? span : 0];
     if (c == 0) {
-        const void* fn = pick_kernel(span, keep, rk);
+        const void* fn = pick_kernel(span, keep, rk, lowrank);
         int n = 0;
         const size_t sh = smem_bytes(rk, lowrank);
         if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh) !=
@@ -1788,7 +1799,7 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
     a.scale = s.scale;
     if (p.keep && !p.rk && p.span >= 2 && a.park == nullptr) return hipErrorInvalidValue;
     if (p.rk && !rk_span_ok(p.span)) return hipErrorInvalidValue;
-    const void* fn = pick_kernel(p.span, p.keep, p.rk);
+    const void* fn = pick_kernel(p.span, p.keep, p.rk, p.lowrank);
     resident_per_cu(p.span, p.keep, p.rk, p.lowrank);   // also raises the kernel's dynamic LDS limit
     const int n_seq = s.B * s.H;
     for (int s0 = 0; s0 < n_seq; s0 += p.seq_batch) {
