@@ -1193,14 +1193,28 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
 }
 
 // ---------------------------------------------------------------------------
-// LR: the low-rank gate variant. Without it the kernel's copy of the
-// arguments has a null z, a constant that removes every low-rank branch.
-template <int SPAN, bool KEEP, bool LR>
+// VAR: which optional parts the kernel has code for: kPlain none, kExtras the
+// initial state and the output gate, kLowRank those and the low-rank gate.
+// The kernel's copy of the arguments has constant nulls for the parts it
+// lacks, which removes their branches (and code) from the lighter variants.
+constexpr int kPlain = 0, kExtras = 1, kLowRank = 2;
+template <int VAR>
+__device__ __forceinline__ FusedArgs variant_args(const FusedArgs& in)
+{
+    FusedArgs a = in;
+    if (VAR < kLowRank) a.z = nullptr;
+    if (VAR < kExtras) {
+        a.init = nullptr;
+        a.gate = nullptr;
+    }
+    return a;
+}
+
+template <int SPAN, bool KEEP, int VAR>
 __global__ void __launch_bounds__(kThreads, 3)
 gla_fused_kernel(FusedArgs a_arg)
 {
-    FusedArgs a = a_arg;
-    if (!LR) a.z = nullptr;
+    const FusedArgs a = variant_args<VAR>(a_arg);
     static_assert(!KEEP || SPAN <= kMaxKeep, "a kept span holds at most kMaxKeep chunks");
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
 
@@ -1430,12 +1444,11 @@ __device__ __forceinline__ void load_q(const FusedArgs& a, int b, int h, int t0,
     for (int hh = 0; hh < 2; ++hh) q[hh] = load16(rq, row_off(a, h, t, (lane >> 4) + 4 * hh).key);
 }
 
-template <int SPAN, bool LR>
+template <int SPAN, int VAR>
 __global__ void __launch_bounds__(kThreads, 2)
 gla_fused_rk_kernel(FusedArgs a_arg)
 {
-    FusedArgs a = a_arg;
-    if (!LR) a.z = nullptr;
+    const FusedArgs a = variant_args<VAR>(a_arg);
     static_assert(SPAN >= 2 && SPAN <= kMaxKeep, "register-kept spans hold 2 .. kMaxKeep chunks");
     SmemRK& sk = *reinterpret_cast<SmemRK*>(smem_raw);
     Smem& sm = sk.s;
@@ -1625,7 +1638,7 @@ static int device_cus()
 static bool keep_span_ok(int span) { return span == 1 || span == 2 || span == 4 || span == 8; }
 static bool rk_span_ok(int span) { return span >= 2 && span <= 7; }
 
-template <bool LR>
+template <int LR>
 static const void* pick_variant(int span, bool keep, bool rk)
 {
     if (rk) {
@@ -1646,27 +1659,29 @@ static const void* pick_variant(int span, bool keep, bool rk)
     default: return (const void*)gla_fused_kernel<8, true, LR>;
     }
 }
-static const void* pick_kernel(int span, bool keep, bool rk, bool lowrank)
+static const void* pick_kernel(int span, bool keep, bool rk, int var)
 {
-    return lowrank ? pick_variant<true>(span, keep, rk) : pick_variant<false>(span, keep, rk);
+    return var == kLowRank ? pick_variant<kLowRank>(span, keep, rk)
+                           : var == kExtras ? pick_variant<kExtras>(span, keep, rk)
+                                            : pick_variant<kPlain>(span, keep, rk);
 }
 
 // Dynamic LDS: the variant's Smem, then (low-rank gate) the gate tables.
 static size_t gate_tab_offset(bool rk) { return ((rk ? sizeof(SmemRK) : sizeof(Smem)) + 15) / 16 * 16; }
-static size_t smem_bytes(bool rk, bool lowrank)
+static size_t smem_bytes(bool rk, int var)
 {
-    return lowrank ? gate_tab_offset(rk) + sizeof(GateTab) : (rk ? sizeof(SmemRK) : sizeof(Smem));
+    return var == kLowRank ? gate_tab_offset(rk) + sizeof(GateTab) : (rk ? sizeof(SmemRK) : sizeof(Smem));
 }
 
 // Workgroups of one variant that fit on a CU at once.
-static int resident_per_cu(int span, bool keep, bool rk, bool lowrank)
+static int resident_per_cu(int span, bool keep, bool rk, int var)
 {
-    static int cache[2][3][kMaxKeep + 1] = {};
-    int& c = cache[lowrank ? 1 : 0][rk ? 2 : (keep ? 1 : 0)][(keep || rk) ? span : 0];
+    static int cache[3][3][kMaxKeep + 1] = {};
+    int& c = cache[var][rk ? 2 : (keep ? 1 : 0)][(keep || rk) ? span : 0];
     if (c == 0) {
-        const void* fn = pick_kernel(span, keep, rk, lowrank);
+        const void* fn = pick_kernel(span, keep, rk, var);
         int n = 0;
-        const size_t sh = smem_bytes(rk, lowrank);
+        const size_t sh = smem_bytes(rk, var);
         if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh) !=
                 hipSuccess ||
             hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, sh) != hipSuccess ||
@@ -1677,10 +1692,10 @@ static int resident_per_cu(int span, bool keep, bool rk, bool lowrank)
     return c;
 }
 
-FusedPlan fused_plan(const Shape& s, int span_override, int rk_override, bool lowrank)
+FusedPlan fused_plan(const Shape& s, int span_override, int rk_override, int var)
 {
     FusedPlan p;
-    p.lowrank = lowrank;
+    p.var = var;
     const int n_seq = s.B * s.H;
     const int nc = s.n_chunks;
     auto fill = [&](int span, bool keep, bool rk = false) {
@@ -1688,7 +1703,7 @@ FusedPlan fused_plan(const Shape& s, int span_override, int rk_override, bool lo
         p.keep = keep || rk;
         p.rk = rk;
         p.n_spans = (nc + span - 1) / span;
-        const long long cap = (long long)resident_per_cu(span, keep, rk, lowrank) * device_cus();
+        const long long cap = (long long)resident_per_cu(span, keep, rk, var) * device_cus();
         // sequences per launch, so that every workgroup of a launch is resident
         long long per = cap / p.n_spans;
         if (per < 1) per = 1;
@@ -1701,7 +1716,7 @@ FusedPlan fused_plan(const Shape& s, int span_override, int rk_override, bool lo
     };
     auto one_seq_fits = [&]() {
         return (long long)p.n_spans <=
-               (long long)resident_per_cu(p.span, p.keep, p.rk, lowrank) * device_cus();
+               (long long)resident_per_cu(p.span, p.keep, p.rk, var) * device_cus();
     };
     if (span_override > 0) {
         if (rk_override > 0 && rk_span_ok(span_override)) {
@@ -1727,7 +1742,7 @@ FusedPlan fused_plan(const Shape& s, int span_override, int rk_override, bool lo
         if (whole()) return p;
     }
     // else streamed spans
-    const long long cap = (long long)resident_per_cu(1, false, false, lowrank) * device_cus();
+    const long long cap = (long long)resident_per_cu(1, false, false, var) * device_cus();
     long long per_seq = cap / n_seq;
     if (per_seq < 1) per_seq = 1;
     if (per_seq > kMaxSpans) per_seq = kMaxSpans;
@@ -1772,7 +1787,9 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
     a.gbias = x.gbias;
     a.inv_tau = x.inv_tau;
     a.gtab_off = (int)gate_tab_offset(p.rk);
-    if (p.lowrank != (x.z != nullptr)) return hipErrorInvalidValue;
+    // the planned variant must have code for every part the call has
+    if ((p.var == kLowRank) != (x.z != nullptr)) return hipErrorInvalidValue;
+    if (p.var == kPlain && (x.init || x.gate)) return hipErrorInvalidValue;
     a.q = (const __half*)q;
     a.k = (const __half*)k;
     a.v = (const __half*)v;
@@ -1799,15 +1816,15 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
     a.scale = s.scale;
     if (p.keep && !p.rk && p.span >= 2 && a.park == nullptr) return hipErrorInvalidValue;
     if (p.rk && !rk_span_ok(p.span)) return hipErrorInvalidValue;
-    const void* fn = pick_kernel(p.span, p.keep, p.rk, p.lowrank);
-    resident_per_cu(p.span, p.keep, p.rk, p.lowrank);   // also raises the kernel's dynamic LDS limit
+    const void* fn = pick_kernel(p.span, p.keep, p.rk, p.var);
+    resident_per_cu(p.span, p.keep, p.rk, p.var);   // also raises the kernel's dynamic LDS limit
     const int n_seq = s.B * s.H;
     for (int s0 = 0; s0 < n_seq; s0 += p.seq_batch) {
         a.seq0 = s0;
         const int nseq = (n_seq - s0 < p.seq_batch) ? (n_seq - s0) : p.seq_batch;
         void* args[] = {&a};
         const hipError_t e = hipLaunchKernel(fn, dim3(nseq * p.n_spans), dim3(kThreads), args,
-                                             smem_bytes(p.rk, p.lowrank), st);
+                                             smem_bytes(p.rk, p.var), st);
         if (e != hipSuccess) return e;
     }
     return hipGetLastError();

@@ -23,12 +23,13 @@ struct FusedPlan {
     int seq_batch;   // sequences per launch (every workgroup of a launch is resident)
     int grid;        // workgroups per launch
     int slice_log2;  // log2 of the state elements each owning workgroup scans
-    bool lowrank;    // log_gamma computed in the kernel from the low-rank gate
+    int var;         // kernel variant: 0 plain, 1 with initial state / output gate,
+                     // 2 also with log_gamma computed from the low-rank gate
 };
 bool fused_supported(const Shape& s);
 // span_override > 0 forces the span; rk_override > 0 then asks for the
 // register-kept variant (when that span has one).
-FusedPlan fused_plan(const Shape& s, int span_override, int rk_override, bool lowrank);
+FusedPlan fused_plan(const Shape& s, int span_override, int rk_override, int var);
 size_t fused_workspace_bytes(const Shape& s, const FusedPlan& p);
 hipError_t launch_fused(const void* q, const void* k, const void* v, const void* lg,
                         const Shape& s, const Extras& x, const FusedPlan& p, void* out,

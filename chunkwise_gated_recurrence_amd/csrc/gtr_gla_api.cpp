@@ -140,16 +140,19 @@ struct Choice {
     size_t lg_offset;    // generic + low-rank: offset of log_gamma
 };
 
-Choice choose(const Shape& s, bool is_fp32, int policy, bool lowrank = false)
+// var: the fused kernel variant the call needs (0 plain, 1 with an initial
+// state or output gate, 2 with the low-rank gate)
+Choice choose(const Shape& s, bool is_fp32, int policy, int var = 0)
 {
+    const bool lowrank = var == 2;
     Choice c;
     c.kernel = kGeneric;
-    c.plan = FusedPlan{1, false, false, s.n_chunks, 0, 0, 0, lowrank};
+    c.plan = FusedPlan{1, false, false, s.n_chunks, 0, 0, 0, var};
     const bool fused_ok = !is_fp32 && gtrgla::fused_supported(s);
     if (fused_ok && policy != GTR_GLA_POLICY_GENERIC) {
         c.kernel = kFused;
         const int span = (policy == GTR_GLA_POLICY_FUSED_ONE) ? 1 : span_override_from_env();
-        c.plan = gtrgla::fused_plan(s, span, rk_override_from_env(), lowrank);
+        c.plan = gtrgla::fused_plan(s, span, rk_override_from_env(), var);
         c.base_bytes = gtrgla::fused_workspace_bytes(s, c.plan);
     } else {
         c.base_bytes = gtrgla::generic_workspace_bytes(s);
@@ -288,7 +291,7 @@ int run(const void* q, const void* k, const void* v, const void* lg, int B, int 
         if (r != GTR_GLA_OK) return r;
     }
     Extras x = x0;
-    const Choice c = choose(s, is_fp32, current_policy(), lr != nullptr);
+    const Choice c = choose(s, is_fp32, current_policy(), lr ? 2 : (x0.init || x0.gate) ? 1 : 0);
     const WsLayout layout = c.kernel == kFused ? WsLayout{kFused, c.plan.n_spans, c.plan.seq_batch}
                                                : WsLayout{kGeneric, 0, 0};
     if (own_ws) {
@@ -348,7 +351,10 @@ size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, in
 {
     Shape s;
     if (validate_sizes(B, H, grid_h, grid_w, d_k, d_v, 0, chunk, &s) != GTR_GLA_OK) return 0;
-    return choose(s, is_fp32 != 0, current_policy()).ws_bytes;
+    // enough for gtr_gla_fwd_ex as well, whose kernel variant may plan differently
+    const size_t plain = choose(s, is_fp32 != 0, current_policy(), 0).ws_bytes;
+    const size_t extras = choose(s, is_fp32 != 0, current_policy(), 1).ws_bytes;
+    return plain > extras ? plain : extras;
 }
 
 int gtr_gla_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream)
@@ -421,7 +427,7 @@ size_t gtr_gla_lowrank_workspace_bytes(int B, int H, int grid_h, int grid_w, int
 {
     Shape s;
     if (validate_sizes(B, H, grid_h, grid_w, d_k, d_v, 0, chunk, &s) != GTR_GLA_OK) return 0;
-    return choose(s, is_fp32 != 0, current_policy(), true).ws_bytes;
+    return choose(s, is_fp32 != 0, current_policy(), 2).ws_bytes;
 }
 
 int gtr_gla_set_policy(int policy)
@@ -442,7 +448,7 @@ int describe_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int ch
     Shape s;
     const int r = validate_sizes(B, H, grid_h, grid_w, d_k, d_v, 0, chunk, &s);
     if (r != GTR_GLA_OK) return r;
-    const Choice c = choose(s, is_fp32 != 0, current_policy(), lowrank);
+    const Choice c = choose(s, is_fp32 != 0, current_policy(), lowrank ? 2 : 0);
     if (kernel_out) *kernel_out = c.kernel == kFused && c.plan.rk ? kFusedRegisterKept : (int)c.kernel;
     if (span_out) *span_out = c.kernel == kFused ? c.plan.span : 1;
     if (grid_out) *grid_out = c.kernel == kFused ? c.plan.grid : B * H * s.n_chunks;
