@@ -1485,17 +1485,21 @@ gla_fused_rk_kernel(FusedArgs a_arg)
     f4 S[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) S[n] = f4{0.f, 0.f, 0.f, 0.f};
-    // kept per chunk: fp16 intra-chunk outputs (C layout) and Qs; chunk c
-    // ends up at index SPAN - 1 - c (the arrays shift by one per chunk, so
-    // that the loop body is one copy of the chunk code)
+    // kept per chunk: fp16 intra-chunk outputs (C layout) and Qs at index c.
+    // The loop body is one copy of the chunk code; a scalar branch on c moves
+    // the chunk's results into their slot (registers cannot be indexed, and
+    // shifting the arrays instead costs 16 moves per kept chunk)
     h8 KO[SPAN][2], KQ[SPAN][2];
 #pragma unroll 1
     for (int c = 0; c < SPAN; ++c) {
         int ln = lane;
         asm volatile("" : "+v"(ln));   // addresses recomputed per chunk, not held live
         const int rr = ln & 15, gg = ln >> 4;
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // this chunk's staged rows and q have landed
-        lds_barrier();                         // ... those of every wave
+        // this chunk's staged rows and q have landed; each wave reads only the
+        // rows it staged itself, so only the first chunk needs a barrier (it
+        // orders the set-up above, e.g. the gate tables)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        if (c == 0) lds_barrier();
         ChunkRegs R;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -1529,19 +1533,19 @@ gla_fused_rk_kernel(FusedArgs a_arg)
 #pragma unroll
         for (int n = 0; n < 4; ++n) O[n] = f4{0.f, 0.f, 0.f, 0.f};
         chunk_back(sm, a, b, h, (c_first + c) * kC, w, ln, c > 0, O, Qt, T);
+        const h8 o0 = h8{(_Float16)O[0][0], (_Float16)O[0][1], (_Float16)O[0][2], (_Float16)O[0][3],
+                         (_Float16)O[1][0], (_Float16)O[1][1], (_Float16)O[1][2], (_Float16)O[1][3]};
+        const h8 o1 = h8{(_Float16)O[2][0], (_Float16)O[2][1], (_Float16)O[2][2], (_Float16)O[2][3],
+                         (_Float16)O[3][0], (_Float16)O[3][1], (_Float16)O[3][2], (_Float16)O[3][3]};
+        // c is wave-uniform: one scalar branch picks the slot
 #pragma unroll
-        for (int i = SPAN - 1; i > 0; --i) {
-            KO[i][0] = KO[i - 1][0];
-            KO[i][1] = KO[i - 1][1];
-            KQ[i][0] = KQ[i - 1][0];
-            KQ[i][1] = KQ[i - 1][1];
-        }
-        KO[0][0] = h8{(_Float16)O[0][0], (_Float16)O[0][1], (_Float16)O[0][2], (_Float16)O[0][3],
-                      (_Float16)O[1][0], (_Float16)O[1][1], (_Float16)O[1][2], (_Float16)O[1][3]};
-        KO[0][1] = h8{(_Float16)O[2][0], (_Float16)O[2][1], (_Float16)O[2][2], (_Float16)O[2][3],
-                      (_Float16)O[3][0], (_Float16)O[3][1], (_Float16)O[3][2], (_Float16)O[3][3]};
-        KQ[0][0] = qs[0];
-        KQ[0][1] = qs[1];
+        for (int i = 0; i < SPAN; ++i)
+            if (i == c) {
+                KO[i][0] = o0;
+                KO[i][1] = o1;
+                KQ[i][0] = qs[0];
+                KQ[i][1] = qs[1];
+            }
     }
 
     // ---- 2. boundary exchange --------------------------------------------------
@@ -1564,7 +1568,7 @@ gla_fused_rk_kernel(FusedArgs a_arg)
     for (int c = 0; c < SPAN; ++c) {
         if (a.gate && c + 1 < n_c) load_gate(a, b, h, (c_first + c + 1) * kC, w, lane, zn);
         if (c < n_c) {
-            const int ki = SPAN - 1 - c;
+            const int ki = c;
             f4 O[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
