@@ -522,18 +522,28 @@ __device__ __forceinline__ void chunk_front(const FusedArgs& a, Smem& sm, const 
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) unpack8(R.g[hh], x[hh]);
     }
+    // step-major, so that consecutive DPP adds are independent (a DPP read
+    // of a value written by the previous instruction needs wait states)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float y = x[hh][e] * kLog2e;
-            y += row_shr<1>(y);
-            y += row_shr<2>(y);
-            y += row_shr<4>(y);
-            y += row_shr<8>(y);
-            x[hh][e] = y;
-        }
-    }
+        for (int e = 0; e < 8; ++e) x[hh][e] *= kLog2e;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[hh][e] += row_shr<1>(x[hh][e]);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[hh][e] += row_shr<2>(x[hh][e]);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[hh][e] += row_shr<4>(x[hh][e]);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[hh][e] += row_shr<8>(x[hh][e]);
     if (r == 15) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
@@ -958,6 +968,15 @@ __device__ __forceinline__ void keep_pass_loop(const FusedArgs& a, Smem& sm, Chu
 // state; every workgroup then reads its own incoming state into Sin (C layout:
 // rows 16w + 4g + e, columns 16jt + r) and advances its slot's epoch. Every
 // wave must have finished with the chunk tiles' contents: they become scratch.
+// final_state of sequence seq: dk x 64 fp32; rows past dk (the zero padding
+// of a 32-wide key dim) fall outside the resource, and a null final_state
+// gives an empty one (stores dropped)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t final_rsrc(const FusedArgs& a, int seq)
+{
+    return rsrc(a.final_state + (a.final_state ? (long long)seq * a.dk * kD : 0),
+                a.final_state ? a.dk * kD * 4 : 0);
+}
+
 __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local_seq, int seq, int j,
                                          long long seq_slot, int w, int lane, f4 (&Sin)[4])
 {
@@ -967,15 +986,13 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
     // The chunk tiles are free now: 45 KB of LDS scratch for the exchange.
     unsigned char* scr = reinterpret_cast<unsigned char*>(sm.Kh);
     const int ns = a.n_spans;
-    const int lo = a.slice_log2;
-    const int slice = 1 << lo;
+    const int lo = a.slice_log2;   // 2^lo state elements per owner
     if (j < (kD * kD >> lo)) {
         const int e_first = j << lo;
         const int lrows = lo - 6;                      // log2 of state rows in the slice
         const int ow = owner_region_words(ns, lo);
         const unsigned int* src = a.agg + local_seq * agg_seq_words(ns) + (long long)j * ow;
-        unsigned int* ubuf = reinterpret_cast<unsigned int*>(scr);   // [ns][slice] U, [ns][nrows] D
-        const float* dbuf = reinterpret_cast<const float*>(ubuf + (ns << lo));
+        unsigned int* ubuf = reinterpret_cast<unsigned int*>(scr);   // [ns][2^lo] U, [ns][rows] D
         unsigned int* fin = ubuf + ow;                                // final state of the slice
         const int lq = lo - 2;                         // log2 of 16 B pieces per span
         const int nl = ow >> 2;
@@ -983,8 +1000,10 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
         // with P = 256 / E contiguous span ranges per element (combined through
         // LDS) when E < 256, else E / 256 elements per thread in turn. Words are
         // checked for their tag as the fold reads them; any stale word sends
-        // the owner back to poll. The incoming states overwrite the U words in
-        // place (tagged); the final state goes to fin.
+        // the owner back to poll. With one range (P = 1) the incoming states
+        // overwrite the U words in place (tagged) and the final state goes to
+        // fin, for the storer waves to copy out; with P > 1 the second pass
+        // over each range stores them directly.
         const int lT = lo < 8 ? 8 - lo : 0;            // log2 P
         const int P = 1 << lT;
         const int per = (ns + P - 1) >> lT;            // spans per range
@@ -1108,21 +1127,32 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                     run = ca * run + cb;
                 }
             }
-            float A = 1.f;
-            bool ok = true;
-            fold(ei, m_lo, m_hi, A, run, true, ok);
-            if (p == P - 1) reinterpret_cast<float*>(fin)[ei] = run;
-            lds_barrier();   // rows complete
-        }
-        // storer waves: rows 0..ns-1 to the incoming-state slots, fin to
-        // final_state (a null final_state gives an empty resource: dropped)
-        if (w >= 2) {
+            // every word has passed its tag check: each span's incoming
+            // state goes straight from the fold to its slot, and the last
+            // range ends with the final state
             const __amdgpu_buffer_rsrc_t rs = rsrc(a.sin + seq_slot * (kD * kD), ns * (kD * kD * 4));
-            // final_state holds dk x 64 per sequence: rows past dk (the zero
-            // padding of a 32-wide key dim) fall outside the resource
-            const __amdgpu_buffer_rsrc_t rf =
-                rsrc(a.final_state + (a.final_state ? (long long)seq * a.dk * kD : 0),
-                     a.final_state ? a.dk * kD * 4 : 0);
+            const unsigned int* pu = ubuf + (m_lo << lo) + ei;
+            const float* pd = dfl + (m_lo << lrows) + (ei >> 6);
+            int voff = 4 * (m_lo * (kD * kD) + e_first + ei);
+#pragma unroll 4
+            for (int m = m_lo; m < m_hi; ++m) {
+                const unsigned int xu = *pu;
+                const float d = *pd;
+                st_dev1(rs, voff, ll_word(run, sm.tags[m]));
+                run = d * run + ll_value(xu);
+                pu += 1 << lo;
+                pd += 1 << lrows;
+                voff += 4 * kD * kD;
+            }
+            if (p == P - 1)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(run), final_rsrc(a, seq),
+                                                      4 * (e_first + ei), 0, 0);
+        }
+        // P = 1: the storer waves copy rows 0..ns-1 (written into the U words
+        // by the fold) to the incoming-state slots, and fin to final_state
+        if (P == 1 && w >= 2) {
+            const __amdgpu_buffer_rsrc_t rs = rsrc(a.sin + seq_slot * (kD * kD), ns * (kD * kD * 4));
+            const __amdgpu_buffer_rsrc_t rf = final_rsrc(a, seq);
             // U pieces (< 2048: ns << lo < 2^13 words), in batches whose LDS
             // reads are all issued before the batch's stores
             const int nu = ns << lq;
