@@ -286,6 +286,7 @@ struct Smem {
     unsigned int tags[kMaxSpans];   // expected tag of every span slot of the sequence
     int fail;
     int stale;
+    int dstale;   // exchange: a decay word was stale in this poll
 };
 
 
@@ -993,17 +994,15 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
         const int ow = owner_region_words(ns, lo);
         const unsigned int* src = a.agg + local_seq * agg_seq_words(ns) + (long long)j * ow;
         unsigned int* ubuf = reinterpret_cast<unsigned int*>(scr);   // [ns][2^lo] U, [ns][rows] D
-        unsigned int* fin = ubuf + ow;                                // final state of the slice
+        unsigned int* s0buf = ubuf + ow;                              // initial state of the slice
         const int lq = lo - 2;                         // log2 of 16 B pieces per span
         const int nl = ow >> 2;
         // Fold, one state element per thread: the slice's E = 2^lo elements,
         // with P = 256 / E contiguous span ranges per element (combined through
         // LDS) when E < 256, else E / 256 elements per thread in turn. Words are
         // checked for their tag as the fold reads them; any stale word sends
-        // the owner back to poll. With one range (P = 1) the incoming states
-        // overwrite the U words in place (tagged) and the final state goes to
-        // fin, for the storer waves to copy out; with P > 1 the second pass
-        // over each range stores them directly.
+        // the owner back to poll. Every span's incoming state and the final
+        // state go from the fold straight to their global slots.
         const int lT = lo < 8 ? 8 - lo : 0;            // log2 P
         const int P = 1 << lT;
         const int per = (ns + P - 1) >> lT;            // spans per range
@@ -1013,17 +1012,19 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
         const int n_pass = 1 << (lo - lW);
         float* compA = reinterpret_cast<float*>(scr + kScanD + 2048);   // [256]
         float* compB = reinterpret_cast<float*>(scr + kScanD + 3072);   // [256]
-        // the initial state's slice is staged in fin by the loader waves (a
-        // global load here would make the storer waves wait for their stores)
-        const float* finf = reinterpret_cast<const float*>(fin);
+        // the initial state's slice, staged by the loader waves with the
+        // first poll
+        const float* s0 = reinterpret_cast<const float*>(s0buf);
+        const __amdgpu_buffer_rsrc_t rs = rsrc(a.sin + seq_slot * (kD * kD), ns * (kD * kD * 4));
+        const __amdgpu_buffer_rsrc_t rf = final_rsrc(a, seq);
         // the decays of every (span, row) of the slice, tag-checked and decoded
         // once into LDS floats (dfl), so that the fold reads plain values
         float* dfl = reinterpret_cast<float*>(scr + kScanD + 4096);   // [ns << lrows] <= 128
         const int nd = ns << lrows;
-        // fold spans [m0, m1) of element e from `run` (writes S_in words when put)
-        auto fold = [&](int e, int m0, int m1, float& A, float& run, bool put, bool& ok) {
+        // fold spans [m0, m1) of element e from `run`, checking the tags
+        auto fold = [&](int e, int m0, int m1, float& A, float& run, bool& ok) {
             const int su = 1 << lo, sd = 1 << lrows;
-            unsigned int* pu = ubuf + (m0 << lo) + e;
+            const unsigned int* pu = ubuf + (m0 << lo) + e;
             const float* pd = dfl + (m0 << lrows) + (e >> 6);
             const unsigned int* pt = sm.tags + m0;
             int m = m0;
@@ -1039,7 +1040,6 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     ok &= ll_ok(xu[k], tg[k]);
-                    if (put) pu[k * su] = ll_word(run, tg[k]);
                     A *= d[k];
                     run = d[k] * run + ll_value(xu[k]);
                 }
@@ -1051,7 +1051,6 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                 const unsigned int xu = *pu, tg = *pt;
                 const float d = *pd;
                 ok &= ll_ok(xu, tg);
-                if (put) *pu = ll_word(run, tg);
                 A *= d;
                 run = d * run + ll_value(xu);
                 pu += su;
@@ -1067,43 +1066,71 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                         __builtin_amdgcn_global_load_lds(src + 4 * (k0 + lane), ubuf + 4 * k0, 16, 0,
                                                          kDevScope);
                 }
-                if (a.init) {   // every poll: a stale pass has overwritten fin
+                if (a.init && polls == 0) {
                     // dk x 64 per sequence; the padded rows read zeros
                     const __amdgpu_buffer_rsrc_t ri =
                         rsrc(a.init + (long long)seq * a.dk * kD, a.dk * kD * 4);
                     for (int k0 = 64 * w; k0 < (1 << lq); k0 += 128) {
                         if (k0 + lane < (1 << lq))
                             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                                ri, (__attribute__((address_space(3))) void*)(fin + 4 * k0), 16,
+                                ri, (__attribute__((address_space(3))) void*)(s0buf + 4 * k0), 16,
                                 4 * (e_first + 4 * (k0 + lane)), 0, 0, 0);
                     }
                 }
                 __builtin_amdgcn_s_waitcnt(0x0F70);
             }
-            if (tid == 0) sm.stale = 0;
+            if (tid == 0) {
+                sm.stale = 0;
+                sm.dstale = 0;
+            }
             bool ok = true;
             lds_barrier();
             if (tid < nd) {
                 const unsigned int x = ubuf[(ns << lo) + tid];
-                ok &= ll_ok(x, sm.tags[tid >> lrows]);
+                if (!ll_ok(x, sm.tags[tid >> lrows])) {
+                    ok = false;
+                    sm.dstale = 1;
+                }
                 dfl[tid] = ll_value(x);
             }
             lds_barrier();
             if (P == 1) {
-                // the whole fold in one pass, from the initial state
+                // the whole fold in one pass, from the initial state. The
+                // incoming state of span m depends on the decays and on U of
+                // spans 0 .. m-1 only: it is stored once those words have
+                // passed their checks, so a stale pass stores only correct
+                // words (a later pass stores them again, unchanged)
+                const bool d_ok = sm.dstale == 0;
                 for (int ps = 0; ps < n_pass; ++ps) {
                     const int e = (ps << 8) + tid;
-                    float A = 1.f, run = a.init ? finf[e] : 0.f;
-                    fold(e, 0, ns, A, run, true, ok);
-                    reinterpret_cast<float*>(fin)[e] = run;
+                    float run = a.init ? s0[e] : 0.f;
+                    bool mine = d_ok;
+                    const unsigned int* pu = ubuf + e;
+                    const float* pd = dfl + (e >> 6);
+                    int voff = 4 * (e_first + e);
+#pragma unroll 4
+                    for (int m = 0; m < ns; ++m) {
+                        const unsigned int xu = *pu, tg = sm.tags[m];
+                        const float d = *pd;
+                        if (mine) st_dev1(rs, voff, ll_word(run, tg));
+                        mine = mine && ll_ok(xu, tg);
+                        run = d * run + ll_value(xu);
+                        pu += 1 << lo;
+                        pd += 1 << lrows;
+                        voff += 4 * kD * kD;
+                    }
+                    if (mine)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(run), rf,
+                                                              4 * (e_first + e), 0, 0);
+                    ok = ok && mine;
                 }
             } else {
                 // my range's product of decays and fold from zero
                 float A = 1.f, run = 0.f;
-                fold(ei, m_lo, m_hi, A, run, false, ok);
+                fold(ei, m_lo, m_hi, A, run, ok);
                 compA[tid] = A;
                 compB[tid] = run;
-                run0 = a.init ? finf[ei] : 0.f;
+                run0 = a.init ? s0[ei] : 0.f;
             }
             if (!__all(ok) && lane == 0) sm.stale = 1;
             lds_barrier();
@@ -1130,7 +1157,6 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
             // every word has passed its tag check: each span's incoming
             // state goes straight from the fold to its slot, and the last
             // range ends with the final state
-            const __amdgpu_buffer_rsrc_t rs = rsrc(a.sin + seq_slot * (kD * kD), ns * (kD * kD * 4));
             const unsigned int* pu = ubuf + (m_lo << lo) + ei;
             const float* pd = dfl + (m_lo << lrows) + (ei >> 6);
             int voff = 4 * (m_lo * (kD * kD) + e_first + ei);
@@ -1145,36 +1171,7 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                 voff += 4 * kD * kD;
             }
             if (p == P - 1)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(run), final_rsrc(a, seq),
-                                                      4 * (e_first + ei), 0, 0);
-        }
-        // P = 1: the storer waves copy rows 0..ns-1 (written into the U words
-        // by the fold) to the incoming-state slots, and fin to final_state
-        if (P == 1 && w >= 2) {
-            const __amdgpu_buffer_rsrc_t rs = rsrc(a.sin + seq_slot * (kD * kD), ns * (kD * kD * 4));
-            const __amdgpu_buffer_rsrc_t rf = final_rsrc(a, seq);
-            // U pieces (< 2048: ns << lo < 2^13 words), in batches whose LDS
-            // reads are all issued before the batch's stores
-            const int nu = ns << lq;
-            const int oob = 0x7FFFFFF0;
-#pragma unroll
-            for (int k0 = 0; k0 < 16; k0 += 8) {
-                u4 x[8];
-                int o[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int q = tid - 128 + 128 * (k0 + i);
-                    x[i] = *reinterpret_cast<const u4*>(ubuf + 4 * q);
-                    o[i] = q < nu ? 4 * ((q >> lq) * (kD * kD) + e_first + 4 * (q & ((1 << lq) - 1)))
-                                  : oob;
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) st_dev4(rs, o[i], x[i]);
-            }
-            // the slice of the final state (<= 1024 pieces)
-            for (int q = tid - 128; q < (1 << lq); q += 128)
-                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u4*>(fin + 4 * q), rf,
-                                                       4 * (e_first + 4 * q), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(run), rf, 4 * (e_first + ei), 0, 0);
         }
     }
     lds_barrier();   // scratch free again
