@@ -80,6 +80,7 @@ constexpr unsigned int kMaxPolls = 1u << 22;
 constexpr int kMaxSpans = 64;        // spans per sequence
 constexpr int kScanD = 32 * 1024;    // exchange scratch: byte offset of the decays
 constexpr int kDevScope = 16;        // cache policy: device-scope (sc1) access
+constexpr int kPollSleep = 2;        // s_sleep between incoming-state polls (64 clocks each)
 
 // ---------------------------------------------------------------------------
 // small device helpers
@@ -966,9 +967,11 @@ __device__ __forceinline__ void keep_pass_loop(const FusedArgs& a, Smem& sm, Chu
 
 // Boundary exchange of one span (workgroup j of sequence local_seq): owners
 // fold their slice of every span's summary and write each span's incoming
-// state; every workgroup then reads its own incoming state into Sin (C layout:
-// rows 16w + 4g + e, columns 16jt + r) and advances its slot's epoch. Every
-// wave must have finished with the chunk tiles' contents: they become scratch.
+// state; every workgroup then reads its own incoming state and advances its
+// slot's epoch. The state is returned in Sin (C layout: rows 16w + 4g + e,
+// columns 16jt + r) and, when stage_st0, also staged in ST0 (fp16,
+// transposed). Every wave must have finished with the chunk tiles' contents:
+// they become scratch.
 // final_state of sequence seq: dk x 64 fp32; rows past dk (the zero padding
 // of a 32-wide key dim) fall outside the resource, and a null final_state
 // gives an empty one (stores dropped)
@@ -979,7 +982,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t final_rsrc(const FusedArgs& a,
 }
 
 __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local_seq, int seq, int j,
-                                         long long seq_slot, int w, int lane, f4 (&Sin)[4])
+                                         long long seq_slot, int w, int lane, f4 (&Sin)[4],
+                                         bool stage_st0)
 {
     const int tid = 64 * w + lane;
     const int r = lane & 15, g = lane >> 4;
@@ -1174,48 +1178,48 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(run), rf, 4 * (e_first + ei), 0, 0);
         }
     }
-    lds_barrier();   // scratch free again
 
-    // my incoming state S_in (C layout), by DMA into the scratch; span 0 reads
-    // zeros like the others so that its epoch, too, advances only once every
-    // owner has read it
+    // my incoming state S_in: each wave polls its own rows straight into
+    // registers until every word carries the slot's tag; span 0 reads zeros
+    // like the others so that its epoch, too, advances only once every owner
+    // has read it
     {
         const unsigned int tag = sm.tags[j];
-        const unsigned int* src = a.sin + (seq_slot + j) * (kD * kD);
-        unsigned int* sbuf = reinterpret_cast<unsigned int*>(scr);
+        const __amdgpu_buffer_rsrc_t rsn = rsrc(a.sin + (seq_slot + j) * (kD * kD), kD * kD * 4);
         for (unsigned int polls = 0;; ++polls) {
-            if (w < 2) {   // loader waves
+            asm volatile("" ::: "memory");   // a fresh load every round
+            unsigned int x[4][4];
 #pragma unroll
-                for (int k0 = 0; k0 < kD * kD / 4; k0 += 128)
-                    __builtin_amdgcn_global_load_lds(src + 4 * (k0 + 64 * w + lane),
-                                                     sbuf + 4 * (k0 + 64 * w), 16, 0, kDevScope);
-                __builtin_amdgcn_s_waitcnt(0x0F70);
-            }
-            if (tid == 0) sm.stale = 0;
-            lds_barrier();
+            for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[jt][e] = __builtin_amdgcn_raw_buffer_load_b32(
+                        rsn, 4 * ((16 * w + 4 * g + e) * kD + 16 * jt + r), 0, kDevScope);
             bool ok = true;
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const unsigned int x = sbuf[(16 * w + 4 * g + e) * kD + 16 * jt + r];
-                    ok &= ll_ok(x, tag);
-                    Sin[jt][e] = ll_value(x);
+                    ok &= ll_ok(x[jt][e], tag);
+                    Sin[jt][e] = ll_value(x[jt][e]);
                 }
-            if (!__all(ok) && lane == 0) sm.stale = 1;
-            lds_barrier();
-            const bool stale = sm.stale;
-            if (!stale) break;
+            if (__all(ok)) break;
             if (polls > kMaxPolls) {
-                if (tid == 0) atomicOr(a.err, 1u);
+                if (lane == 0) atomicOr(a.err, 1u);
                 break;
             }
-            lds_barrier();   // every thread has read the flag before it is reset
-            __builtin_amdgcn_s_sleep(2);
+            __builtin_amdgcn_s_sleep(kPollSleep);
         }
         // Every owner has read this slot's epoch (it wrote S_in after reading
-        // the epochs), and so has this workgroup: advance it.
+        // the epochs), and so has every wave here: advance it. The barrier
+        // also frees the scratch (the chunk tiles) for the staging below and
+        // for the caller.
+        lds_barrier();
         if (tid == 0) __hip_atomic_store(a.epoch + seq_slot + j, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (stage_st0) {
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) st4(sm.ST0, 16 * jt + r, 16 * w + 4 * g, pack4(Sin[jt], 1.f));
+        }
     }
 }
 
@@ -1319,20 +1323,15 @@ gla_fused_kernel(FusedArgs a_arg)
     // Then every workgroup reads its own S_in.
     u4 zg[2];   // the one-chunk span's gate, fetched while the exchange runs
     if (KEEP && SPAN == 1) load_gate(a, b, h, c_first * kC, w, lane, zg);
-    f4 Sin[4];
-    exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin);
-
-    // ---- 3. outputs -----------------------------------------------------------
     // the incoming state is nonzero past the first span, or with an initial state
     const bool has_in = j > 0 || a.init != nullptr;
+    f4 Sin[4];
+    exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin, KEEP && has_in);
+
+    // ---- 3. outputs -----------------------------------------------------------
     if (tid < kD) sm.nw[tid] = nwr;
     if (KEEP) {
-        if (has_in) {
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt)
-                st4(sm.ST0, 16 * jt + r, 16 * w + 4 * g, pack4(Sin[jt], 1.f));
-        }
-        lds_barrier();
+        lds_barrier();   // the incoming state is in ST0
         if constexpr (SPAN == 1) {
             f4 O[4];
             K[0].get(O);
@@ -1576,18 +1575,13 @@ gla_fused_rk_kernel(FusedArgs a_arg)
     }
 
     // ---- 2. boundary exchange --------------------------------------------------
+    const bool has_in = j > 0 || a.init != nullptr;
     f4 Sin[4];
-    exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin);
+    exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin, has_in);
 
     // ---- 3. outputs: O_c += Qs_c S_in -------------------------------------------
-    const bool has_in = j > 0 || a.init != nullptr;
     if (tid < kD) sm.nw[tid] = nwr;
-    if (has_in) {
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-            st4(sm.ST0, 16 * jt + r, 16 * w + 4 * g, pack4(Sin[jt], 1.f));
-    }
-    lds_barrier();
+    lds_barrier();   // the incoming state is in ST0
     // the gate of the next chunk loads while this one finishes
     u4 zc[2], zn[2];
     if (a.gate) load_gate(a, b, h, c_first * kC, w, lane, zc);
