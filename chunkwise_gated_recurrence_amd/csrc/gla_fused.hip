@@ -803,6 +803,9 @@ __host__ __device__ inline long long agg_seq_words(int ns) { return (long long)n
 // storer waves through an LDS tile that the chunk's output half does not read:
 // ST0 when that half takes no incoming state (AFTER_STATE false), else KtT,
 // after a barrier (every wave's state update has read its KtT rows by then).
+// Two waves store because a wave's wait for a load also waits for its own
+// earlier stores, and device-scope stores are acknowledged late: storing from
+// every wave made the exchange's first polls return about 1 us later.
 constexpr int kU01 = 68;   // fp32 row stride of the handed-over rows (no bank conflicts)
 
 template <bool AFTER_STATE>
@@ -1016,8 +1019,7 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
         const int n_pass = 1 << (lo - lW);
         float* compA = reinterpret_cast<float*>(scr + kScanD + 2048);   // [256]
         float* compB = reinterpret_cast<float*>(scr + kScanD + 3072);   // [256]
-        // the initial state's slice, staged by the loader waves with the
-        // first poll
+        // the initial state's slice, staged with the first poll
         const float* s0 = reinterpret_cast<const float*>(s0buf);
         const __amdgpu_buffer_rsrc_t rs = rsrc(a.sin + seq_slot * (kD * kD), ns * (kD * kD * 4));
         const __amdgpu_buffer_rsrc_t rf = final_rsrc(a, seq);
@@ -1064,8 +1066,8 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
         };
         float run0 = 0.f;   // ranged fold: the initial state of my element
         for (unsigned int polls = 0;; ++polls) {
-            if (w < 2) {   // loader waves
-                for (int k0 = 64 * w; k0 < nl; k0 += 128) {
+            {   // every wave loads a share of the region
+                for (int k0 = 64 * w; k0 < nl; k0 += 256) {
                     if (k0 + lane < nl)
                         __builtin_amdgcn_global_load_lds(src + 4 * (k0 + lane), ubuf + 4 * k0, 16, 0,
                                                          kDevScope);
@@ -1074,7 +1076,7 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                     // dk x 64 per sequence; the padded rows read zeros
                     const __amdgpu_buffer_rsrc_t ri =
                         rsrc(a.init + (long long)seq * a.dk * kD, a.dk * kD * 4);
-                    for (int k0 = 64 * w; k0 < (1 << lq); k0 += 128) {
+                    for (int k0 = 64 * w; k0 < (1 << lq); k0 += 256) {
                         if (k0 + lane < (1 << lq))
                             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                                 ri, (__attribute__((address_space(3))) void*)(s0buf + 4 * k0), 16,
