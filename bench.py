@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -87,11 +88,16 @@ FUSED_SOURCES = ("gla_common.h", "gla_fused.hip")
 
 
 def kernel_hash() -> str:
+    """Hash of the fused kernels' code: line comments, trailing blanks and
+    empty lines are dropped first, so that a comment edit keeps the counter
+    summaries taken on the same code valid."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "chunkwise_gated_recurrence_amd", "csrc")
     for f in FUSED_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            lines = (re.sub(r"//.*", "", l).rstrip() for l in fh)
+            code = "\n".join(l for l in lines if l)
+        h.update(f.encode() + code.encode())
     return h.hexdigest()[:16]
 
 

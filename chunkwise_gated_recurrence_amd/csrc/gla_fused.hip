@@ -37,10 +37,12 @@
 // previous tag and a workspace is cleared only once. The rounding perturbs an
 // exchanged value by at most 2^-16 of itself.
 //
-// Roles inside a workgroup: waves 0-1 wait on global loads (polls), waves 2-3
-// issue the exchange stores. One counter tracks a wave's loads and stores
-// together, so a wave that waits for a load also waits for every store it has
-// in flight; keeping the roles apart keeps store latency off the polls.
+// One counter tracks a wave's loads and stores together, so a wave that waits
+// for a load also waits for every store it has in flight: the span summary is
+// stored by waves 2-3 only, which keeps its store latency off waves 0-1's
+// first polls. The owners' fold stores the incoming states straight from the
+// fold (all waves), and each wave then polls its own rows of its incoming
+// state.
 //
 // Per chunk (wave w owns rows 16w..16w+15 of the chunk and state rows
 // 16w..16w+15; lane l holds row r = l & 15 and dims 8(l >> 4) + 32h + e):
