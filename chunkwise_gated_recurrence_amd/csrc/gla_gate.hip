@@ -81,19 +81,18 @@ typedef _Float16 gh8 __attribute__((ext_vector_type(8)));
 typedef float gf4 __attribute__((ext_vector_type(4)));
 
 // fp16 x with C a multiple of 128 (and x 16-byte aligned): the product on
-// fp16 MFMA (16x16x32, fp32 accumulation), z^T = W1^T x^T for 32 tokens per
-// workgroup (two 16-token tiles per wave, sharing the W1 operand), wave w over
+// fp16 MFMA (16x16x32, fp32 accumulation), z^T = W1^T x^T for 16 T tokens per
+// workgroup (T 16-token tiles per wave, sharing the W1 operand), wave w over
 // the w-th quarter of the features. x is exact in fp16; W1 enters as hi + lo,
 // two fp16 parts (hi = fp16(W1), lo = fp16(W1 - hi)), one MFMA each, which
 // keeps it to about 2^-22 of its value above fp16's normal range and to 2^-24
 // absolute below it. The A operand's row m is rank m, so each lane ends with
 // ranks 4g .. 4g + 3 of its token; the four quarters meet in LDS.
-constexpr int kProjTiles = 2;
+template <int T>
 __global__ void __launch_bounds__(256)
 lowrank_project_mfma_kernel(const __half* __restrict__ x, const float* __restrict__ w1,
                             size_t rows, int C, float* __restrict__ z)
 {
-    constexpr int T = kProjTiles;
     __shared__ gf4 part[4][T][64];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -111,22 +110,58 @@ lowrank_project_mfma_kernel(const __half* __restrict__ x, const float* __restric
     gf4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = gf4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int c = 0; c < cq; c += 32) {
-        gh8 b[T];
+    if constexpr (T == 1) {
+        // groups of four 32-feature steps: every load of a group is issued
+        // before its MFMAs (C <= 512: the whole product in one group). The loads
+        // are unconditional (a step past the end re-reads the last one, in
+        // bounds) so that they form one block; only the MFMAs are skipped.
+        for (int c0 = 0; c0 < cq; c0 += 128) {
+            gh8 b[4][T];
+            float wv[4][8];
 #pragma unroll
-        for (int t = 0; t < T; ++t) b[t] = *reinterpret_cast<const gh8*>(xr[t] + c);
-        gh8 hi, lo;
+            for (int st = 0; st < 4; ++st) {
+                const int c = min(c0 + 32 * st, cq - 32);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float v = wr[(size_t)(c + e) * kRank];
-            hi[e] = (_Float16)v;
-            lo[e] = (_Float16)(v - (float)hi[e]);
+                for (int t = 0; t < T; ++t) b[st][t] = *reinterpret_cast<const gh8*>(xr[t] + c);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wv[st][e] = wr[(size_t)(c + e) * kRank];
+            }
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                if (c0 + 32 * st < cq) {   // uniform
+                    gh8 hi, lo;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        hi[e] = (_Float16)wv[st][e];
+                        lo[e] = (_Float16)(wv[st][e] - (float)hi[e]);
+                    }
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, b[st][t], acc[t], 0, 0, 0);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, b[st][t], acc[t], 0, 0, 0);
+                    }
+                }
+            }
         }
+    } else {
+        // long inputs (bandwidth-bound): one step at a time measured faster
+        // than the grouped loads above
+        for (int c = 0; c < cq; c += 32) {
+            gh8 b[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, b[t], acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, b[t], acc[t], 0, 0, 0);
+            for (int t = 0; t < T; ++t) b[t] = *reinterpret_cast<const gh8*>(xr[t] + c);
+            gh8 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = wr[(size_t)(c + e) * kRank];
+                hi[e] = (_Float16)v;
+                lo[e] = (_Float16)(v - (float)hi[e]);
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, b[t], acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, b[t], acc[t], 0, 0, 0);
+            }
         }
     }
 #pragma unroll
@@ -167,9 +202,14 @@ hipError_t launch_lowrank_project(const void* x, bool is_fp32, const float* w1, 
     if (rows == 0) return hipSuccess;
     const bool aligned = ((uintptr_t)x & 15) == 0;
     if (!is_fp32 && C % 128 == 0 && aligned) {
-        hipLaunchKernelGGL(lowrank_project_mfma_kernel,
-                           dim3((unsigned)((rows + 16 * kProjTiles - 1) / (16 * kProjTiles))),
-                           dim3(256), 0, st, (const __half*)x, w1, rows, C, z);
+        // one 16-token tile per workgroup while that leaves fewer workgroups
+        // than two per CU (short sequences: latency), else two sharing W1
+        if (rows <= 16 * 512)
+            hipLaunchKernelGGL(lowrank_project_mfma_kernel<1>, dim3((unsigned)((rows + 15) / 16)),
+                               dim3(256), 0, st, (const __half*)x, w1, rows, C, z);
+        else
+            hipLaunchKernelGGL(lowrank_project_mfma_kernel<2>, dim3((unsigned)((rows + 31) / 32)),
+                               dim3(256), 0, st, (const __half*)x, w1, rows, C, z);
         return hipGetLastError();
     }
     const int vec = is_fp32 ? 4 : 8;
