@@ -27,15 +27,19 @@
 //      starting from S_in and store the outputs as they are produced.
 //
 // Exchanged values travel as 4-byte words: an fp32 value rounded to 16
-// mantissa bits whose low 8 bits carry a tag, written and read with
+// mantissa bits whose low 8 bits carry a tag (span summaries), or as 2-byte
+// fp16 words whose lowest mantissa bit carries the tag's parity (incoming
+// states, which the output pass uses in fp16), written and read with
 // device-scope (sc1) accesses. A reader polls the words themselves until every
 // tag equals the expected one, so a hand-over costs one memory round trip: no
 // flags, no fences, no atomics. Each exchange slot (sequence in the launch,
 // span) has its own epoch in the workspace; the words of a slot are rewritten
 // in full by every launch that uses it and its epoch is advanced once all of
 // that launch's readers know it, so the words in memory always carry the
-// previous tag and a workspace is cleared only once. The rounding perturbs an
-// exchanged value by at most 2^-16 of itself.
+// previous tag and a workspace is cleared only once. The rounding perturbs a
+// summary value by at most 2^-16 of itself and an incoming state by at most
+// 2^-10 (fp16 with its last bit taken; the final state is folded from the
+// summaries in fp32).
 //
 // One counter tracks a wave's loads and stores together, so a wave that waits
 // for a load also waits for every store it has in flight: the span summary is
@@ -82,6 +86,7 @@ constexpr unsigned int kMaxPolls = 1u << 22;
 constexpr int kMaxSpans = 64;        // spans per sequence
 constexpr int kScanD = 32 * 1024;    // exchange scratch: byte offset of the decays
 constexpr int kDevScope = 16;        // cache policy: device-scope (sc1) access
+constexpr int kSinSlotBytes = kD * kD * 2;   // incoming-state words of one span slot (2 B each)
 constexpr int kPollSleep = 2;        // s_sleep between incoming-state polls (64 clocks each)
 
 // ---------------------------------------------------------------------------
@@ -136,6 +141,23 @@ __device__ __forceinline__ unsigned int ll_word(float v, unsigned int tag)
 }
 __device__ __forceinline__ float ll_value(unsigned int x) { return __uint_as_float(x & 0xFFFFFF00u); }
 __device__ __forceinline__ bool ll_ok(unsigned int x, unsigned int tag) { return (x & 0xFFu) == tag; }
+
+// Incoming-state words are 2 bytes: the value in fp16 (the output pass uses
+// the incoming state in fp16) with its lowest mantissa bit replaced by the
+// parity of the tag. The parity suffices: every launch that uses a slot
+// rewrites all of its words and advances its epoch by one, so a stale word
+// always carries the previous launch's tag.
+__device__ __forceinline__ unsigned short sin_word(float v, unsigned int tag)
+{
+    const unsigned short x = __builtin_bit_cast(unsigned short, (_Float16)v);
+    return (unsigned short)((x & 0xFFFEu) | (tag & 1u));
+}
+__device__ __forceinline__ bool sin_ok(unsigned short x, unsigned int tag) { return ((x ^ tag) & 1u) == 0; }
+// (the tag bit is cleared, so that the value does not depend on the launch)
+__device__ __forceinline__ float sin_value(unsigned short x)
+{
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(x & 0xFFFEu));
+}
 
 // Buffer resource over n_bytes at base: accesses past the end read zeros and
 // are dropped on write.
@@ -207,7 +229,7 @@ struct FusedArgs {
     unsigned int* epoch;        // [seq in launch][n_spans] low 8 bits: tag of the slot's words
     unsigned int* err;          // set when a wait gives up
     unsigned int* agg;          // [seq in launch][agg_seq_words(n_spans)]  tagged, owner-major
-    unsigned int* sin;          // [seq in launch][n_spans][kD * kD]   tagged
+    unsigned int* sin;          // [seq in launch][n_spans] slots of kSinSlotBytes: 2-byte words
     u4* park;                   // [workgroup][span - 1][256 threads][4]: parked outputs (long kept spans)
     int L, H, grid_h, grid_w, dir;
     int n_chunks;               // per sequence
@@ -1023,7 +1045,8 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
         float* compB = reinterpret_cast<float*>(scr + kScanD + 3072);   // [256]
         // the initial state's slice, staged with the first poll
         const float* s0 = reinterpret_cast<const float*>(s0buf);
-        const __amdgpu_buffer_rsrc_t rs = rsrc(a.sin + seq_slot * (kD * kD), ns * (kD * kD * 4));
+        const __amdgpu_buffer_rsrc_t rs =
+            rsrc(reinterpret_cast<const unsigned char*>(a.sin) + seq_slot * kSinSlotBytes, ns * kSinSlotBytes);
         const __amdgpu_buffer_rsrc_t rf = final_rsrc(a, seq);
         // the decays of every (span, row) of the slice, tag-checked and decoded
         // once into LDS floats (dfl), so that the fold reads plain values
@@ -1115,17 +1138,18 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                     bool mine = d_ok;
                     const unsigned int* pu = ubuf + e;
                     const float* pd = dfl + (e >> 6);
-                    int voff = 4 * (e_first + e);
+                    int voff = 2 * (e_first + e);
 #pragma unroll 4
                     for (int m = 0; m < ns; ++m) {
                         const unsigned int xu = *pu, tg = sm.tags[m];
                         const float d = *pd;
-                        if (mine) st_dev1(rs, voff, ll_word(run, tg));
+                        if (mine)
+                            __builtin_amdgcn_raw_buffer_store_b16(sin_word(run, tg), rs, voff, 0, kDevScope);
                         mine = mine && ll_ok(xu, tg);
                         run = d * run + ll_value(xu);
                         pu += 1 << lo;
                         pd += 1 << lrows;
-                        voff += 4 * kD * kD;
+                        voff += kSinSlotBytes;
                     }
                     if (mine)
                         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(run), rf,
@@ -1167,16 +1191,16 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
             // range ends with the final state
             const unsigned int* pu = ubuf + (m_lo << lo) + ei;
             const float* pd = dfl + (m_lo << lrows) + (ei >> 6);
-            int voff = 4 * (m_lo * (kD * kD) + e_first + ei);
+            int voff = m_lo * kSinSlotBytes + 2 * (e_first + ei);
 #pragma unroll 4
             for (int m = m_lo; m < m_hi; ++m) {
                 const unsigned int xu = *pu;
                 const float d = *pd;
-                st_dev1(rs, voff, ll_word(run, sm.tags[m]));
+                __builtin_amdgcn_raw_buffer_store_b16(sin_word(run, sm.tags[m]), rs, voff, 0, kDevScope);
                 run = d * run + ll_value(xu);
                 pu += 1 << lo;
                 pd += 1 << lrows;
-                voff += 4 * kD * kD;
+                voff += kSinSlotBytes;
             }
             if (p == P - 1)
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(run), rf, 4 * (e_first + ei), 0, 0);
@@ -1189,23 +1213,24 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
     // has read it
     {
         const unsigned int tag = sm.tags[j];
-        const __amdgpu_buffer_rsrc_t rsn = rsrc(a.sin + (seq_slot + j) * (kD * kD), kD * kD * 4);
+        const __amdgpu_buffer_rsrc_t rsn =
+            rsrc(reinterpret_cast<const unsigned char*>(a.sin) + (seq_slot + j) * kSinSlotBytes, kSinSlotBytes);
         for (unsigned int polls = 0;; ++polls) {
             asm volatile("" ::: "memory");   // a fresh load every round
-            unsigned int x[4][4];
+            unsigned short x[4][4];
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    x[jt][e] = __builtin_amdgcn_raw_buffer_load_b32(
-                        rsn, 4 * ((16 * w + 4 * g + e) * kD + 16 * jt + r), 0, kDevScope);
+                    x[jt][e] = __builtin_amdgcn_raw_buffer_load_b16(
+                        rsn, 2 * ((16 * w + 4 * g + e) * kD + 16 * jt + r), 0, kDevScope);
             bool ok = true;
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    ok &= ll_ok(x[jt][e], tag);
-                    Sin[jt][e] = ll_value(x[jt][e]);
+                    ok &= sin_ok(x[jt][e], tag);
+                    Sin[jt][e] = sin_value(x[jt][e]);
                 }
             if (__all(ok)) break;
             if (polls > kMaxPolls) {
@@ -1805,8 +1830,8 @@ size_t fused_workspace_bytes(const Shape& s, const FusedPlan& p)
     (void)s;
     const size_t slots = (size_t)p.seq_batch * p.n_spans;
     return 256 + align256(slots * sizeof(unsigned int)) +
-           align256(((size_t)p.seq_batch * agg_seq_words(p.n_spans) + slots * kD * kD) *
-                    sizeof(unsigned int)) +
+           align256((size_t)p.seq_batch * agg_seq_words(p.n_spans) * sizeof(unsigned int) +
+                    slots * kSinSlotBytes) +
            park_bytes(p);
 }
 
