@@ -96,6 +96,17 @@ def test_generic_policy_parity(name, d):
         gla.gtr_gla_set_policy(gla.POLICY_AUTO)
 
 
+@pytest.mark.parametrize("name,plan", [("img640", (2, 1, 150)), ("img1024", (3, 2, 384)),
+                                       ("batched640", (3, 3, 432)), ("long2048", (3, 7, 444))])
+def test_default_plans(name, plan):
+    """The launch policy's choice for the benchmark workloads (kernel 2: one
+    chunk per workgroup while the grid fits at two per CU; kernel 3: the
+    shortest register-kept span whose grid is resident). The grids assume the
+    MI355X's 256 CUs."""
+    w = gla_synth.WORKLOADS[name]
+    assert gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, w.chunk, 0) == plan
+
+
 @pytest.mark.parametrize("span", [1, 2, 4, 8])
 @pytest.mark.parametrize("name", ["img1024", "ragged30"])
 def test_fused_spans(name, span):
