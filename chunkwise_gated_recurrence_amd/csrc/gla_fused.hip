@@ -63,6 +63,8 @@
 // chunk's log2-gate range, valid when that range is <= kGuard (every factor
 // then lies in [2^-8, 2^8]). A chunk with a wider range (very strong decay)
 // computes its scores exactly in fp32 instead.
+#include <type_traits>
+
 #include "gla_common.h"
 #include "gla_launch.h"
 
@@ -1132,7 +1134,13 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                 // passed their checks, so a stale pass stores only correct
                 // words (a later pass stores them again, unchanged)
                 const bool d_ok = sm.dstale == 0;
-                for (int ps = 0; ps < n_pass; ++ps) {
+                // When every span slot of the sequence expects the same tag
+                // (the steady state: the slots' epochs advance together), the
+                // loop takes it from a register instead of the tag table.
+                const unsigned int tag0 = sm.tags[0];
+                const bool uni = __all(lane >= ns || sm.tags[lane] == tag0);
+                auto fold1 = [&](auto uniform) {
+                  for (int ps = 0; ps < n_pass; ++ps) {
                     const int e = (ps << 8) + tid;
                     float run = a.init ? s0[e] : 0.f;
                     bool mine = d_ok;
@@ -1141,7 +1149,7 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                     int voff = 2 * (e_first + e);
 #pragma unroll 4
                     for (int m = 0; m < ns; ++m) {
-                        const unsigned int xu = *pu, tg = sm.tags[m];
+                        const unsigned int xu = *pu, tg = decltype(uniform)::value ? tag0 : sm.tags[m];
                         const float d = *pd;
                         if (mine)
                             __builtin_amdgcn_raw_buffer_store_b16(sin_word(run, tg), rs, voff, 0, kDevScope);
@@ -1155,7 +1163,12 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(run), rf,
                                                               4 * (e_first + e), 0, 0);
                     ok = ok && mine;
-                }
+                  }
+                };
+                if (uni)
+                    fold1(std::true_type{});
+                else
+                    fold1(std::false_type{});
             } else {
                 // my range's product of decays and fold from zero
                 float A = 1.f, run = 0.f;
