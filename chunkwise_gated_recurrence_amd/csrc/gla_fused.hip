@@ -1054,8 +1054,14 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
         // once into LDS floats (dfl), so that the fold reads plain values
         float* dfl = reinterpret_cast<float*>(scr + kScanD + 4096);   // [ns << lrows] <= 128
         const int nd = ns << lrows;
+        // When every span slot of the sequence expects the same tag (the
+        // steady state: the slots' epochs advance together), the folds take
+        // it from a register instead of reading the tag table per span.
+        const unsigned int tag0 = sm.tags[0];
+        const bool uni = __all(lane >= ns || sm.tags[lane] == tag0);
         // fold spans [m0, m1) of element e from `run`, checking the tags
-        auto fold = [&](int e, int m0, int m1, float& A, float& run, bool& ok) {
+        auto fold = [&](int e, int m0, int m1, float& A, float& run, bool& ok, auto uniform) {
+            constexpr bool UNI = decltype(uniform)::value;
             const int su = 1 << lo, sd = 1 << lrows;
             const unsigned int* pu = ubuf + (m0 << lo) + e;
             const float* pd = dfl + (m0 << lrows) + (e >> 6);
@@ -1068,7 +1074,7 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                 for (int k = 0; k < 4; ++k) {
                     xu[k] = pu[k * su];
                     d[k] = pd[k * sd];
-                    tg[k] = pt[k];
+                    tg[k] = UNI ? tag0 : pt[k];
                 }
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
@@ -1081,7 +1087,7 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                 pt += 4;
             }
             for (; m < m1; ++m) {
-                const unsigned int xu = *pu, tg = *pt;
+                const unsigned int xu = *pu, tg = UNI ? tag0 : *pt;
                 const float d = *pd;
                 ok &= ll_ok(xu, tg);
                 A *= d;
@@ -1134,11 +1140,6 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                 // passed their checks, so a stale pass stores only correct
                 // words (a later pass stores them again, unchanged)
                 const bool d_ok = sm.dstale == 0;
-                // When every span slot of the sequence expects the same tag
-                // (the steady state: the slots' epochs advance together), the
-                // loop takes it from a register instead of the tag table.
-                const unsigned int tag0 = sm.tags[0];
-                const bool uni = __all(lane >= ns || sm.tags[lane] == tag0);
                 auto fold1 = [&](auto uniform) {
                   for (int ps = 0; ps < n_pass; ++ps) {
                     const int e = (ps << 8) + tid;
@@ -1172,7 +1173,10 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
             } else {
                 // my range's product of decays and fold from zero
                 float A = 1.f, run = 0.f;
-                fold(ei, m_lo, m_hi, A, run, ok);
+                if (uni)
+                    fold(ei, m_lo, m_hi, A, run, ok, std::true_type{});
+                else
+                    fold(ei, m_lo, m_hi, A, run, ok, std::false_type{});
                 compA[tid] = A;
                 compB[tid] = run;
                 run0 = a.init ? s0[ei] : 0.f;
@@ -1202,19 +1206,26 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
             // every word has passed its tag check: each span's incoming
             // state goes straight from the fold to its slot, and the last
             // range ends with the final state
-            const unsigned int* pu = ubuf + (m_lo << lo) + ei;
-            const float* pd = dfl + (m_lo << lrows) + (ei >> 6);
-            int voff = m_lo * kSinSlotBytes + 2 * (e_first + ei);
+            auto pass2 = [&](auto uniform) {
+                const unsigned int* pu = ubuf + (m_lo << lo) + ei;
+                const float* pd = dfl + (m_lo << lrows) + (ei >> 6);
+                int voff = m_lo * kSinSlotBytes + 2 * (e_first + ei);
 #pragma unroll 4
-            for (int m = m_lo; m < m_hi; ++m) {
-                const unsigned int xu = *pu;
-                const float d = *pd;
-                __builtin_amdgcn_raw_buffer_store_b16(sin_word(run, sm.tags[m]), rs, voff, 0, kDevScope);
-                run = d * run + ll_value(xu);
-                pu += 1 << lo;
-                pd += 1 << lrows;
-                voff += kSinSlotBytes;
-            }
+                for (int m = m_lo; m < m_hi; ++m) {
+                    const unsigned int xu = *pu;
+                    const float d = *pd;
+                    const unsigned int tg = decltype(uniform)::value ? tag0 : sm.tags[m];
+                    __builtin_amdgcn_raw_buffer_store_b16(sin_word(run, tg), rs, voff, 0, kDevScope);
+                    run = d * run + ll_value(xu);
+                    pu += 1 << lo;
+                    pd += 1 << lrows;
+                    voff += kSinSlotBytes;
+                }
+            };
+            if (uni)
+                pass2(std::true_type{});
+            else
+                pass2(std::false_type{});
             if (p == P - 1)
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(run), rf, 4 * (e_first + ei), 0, 0);
         }
