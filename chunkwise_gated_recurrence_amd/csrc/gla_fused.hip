@@ -618,27 +618,37 @@ __device__ __forceinline__ void chunk_front(const FusedArgs& a, Smem& sm, const 
     }
     lds_barrier();  // (A2)
 
+    // every per-dim constant of the lane's dims at once (one LDS round trip)
     const bool exact = FULL && sm.fail;
+    float pre_c[2][8], ref_c[2][8];
+    h8 cq_c[2], ck_c[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const int d0 = 32 * hh + 8 * g;
-        float pre[8];
-        ld_f8(&sm.pre[w][d0], pre);
+        ld_f8(&sm.pre[w][d0], pre_c[hh]);
+        if (FULL) {
+            ld_f8(&sm.ref[d0], ref_c[hh]);
+            cq_c[hh] = *reinterpret_cast<const h8*>(&sm.cq16[d0]);
+            ck_c[hh] = *reinterpret_cast<const h8*>(&sm.ck16[d0]);
+        }
+    }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[hh][e] += pre[e];
+    for (int hh = 0; hh < 2; ++hh) {
+        const int d0 = 32 * hh + 8 * g;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[hh][e] += pre_c[hh][e];
         h8 kt8;
         if (FULL && !exact) {
             // E = 2^{b-r} and 1/E in fp32, the products in packed fp16
-            float rf[8], ef[8], ei[8];
-            ld_f8(&sm.ref[d0], rf);
+            float ef[8], ei[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float dlt = x[hh][e] - rf[e];
+                const float dlt = x[hh][e] - ref_c[hh][e];
                 ef[e] = ex2(dlt);
                 ei[e] = ex2(-dlt);
             }
-            const h8 cq = *reinterpret_cast<const h8*>(&sm.cq16[d0]);
-            const h8 ck = *reinterpret_cast<const h8*>(&sm.ck16[d0]);
+            const h8 cq = cq_c[hh];
+            const h8 ck = ck_c[hh];
             const h8 q8 = __builtin_bit_cast(h8, R.q[hh]);
             const h8 k8 = __builtin_bit_cast(h8, R.k[hh]);
             const h8 qh = q8 * pack8(ef);
