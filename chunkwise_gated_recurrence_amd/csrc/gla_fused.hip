@@ -844,10 +844,17 @@ __host__ __device__ inline long long agg_seq_words(int ns) { return (long long)n
 // every wave made the exchange's first polls return about 1 us later.
 constexpr int kU01 = 68;   // fp32 row stride of the handed-over rows (no bank conflicts)
 
+// u23: an LDS region of 32 rows x kU01 floats that no later read of the chunk
+// needs (or null): waves 2-3 then stage their rows too, and every row goes
+// out in 16-byte stores (fewer, wider stores than one word per lane). The
+// one-chunk kernel passes ST0 (with KtT as u01 after the AFTER_STATE
+// barrier): 11.24 -> 11.05 us at 640x640. In the register-kept kernel (its
+// staging tiles as u23) it measured 0.5-2 % slower, so that kernel keeps
+// the direct stores of waves 2-3's rows.
 template <bool AFTER_STATE>
 __device__ __forceinline__ void publish_summary(const FusedArgs& a, Smem& sm, const f4 (&S)[4],
                                                 long long slot, int j, unsigned int ep, int w,
-                                                int lane)
+                                                int lane, float* u23 = nullptr)
 {
     const int r = lane & 15, g = lane >> 4;
     const int tid = 64 * w + lane;
@@ -856,11 +863,13 @@ __device__ __forceinline__ void publish_summary(const FusedArgs& a, Smem& sm, co
     __builtin_amdgcn_s_waitcnt(0x0F70);
     if (AFTER_STATE) lds_barrier();
     float* u01 = reinterpret_cast<float*>(AFTER_STATE ? sm.KtT : sm.ST0);
-    if (w < 2) {
+    if (w < 2 || u23) {
+        float* dst = w < 2 ? u01 : u23;
+        const int rw = 16 * (w & 1);
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) u01[(16 * w + 4 * g + e) * kU01 + 16 * jt + r] = S[jt][e];
+            for (int e = 0; e < 4; ++e) dst[(rw + 4 * g + e) * kU01 + 16 * jt + r] = S[jt][e];
     }
     if (tid < kMaxSpans) sm.tags[tid] = (ep + 1u) & 0xFFu;
     lds_barrier();
@@ -876,18 +885,24 @@ __device__ __forceinline__ void publish_summary(const FusedArgs& a, Smem& sm, co
         auto row_word = [&](int i) {
             return (i >> lr) * ow + (j << lo) + ((i & ((1 << lr) - 1)) << 6);
         };
+        if (!u23) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int base = 4 * (row_word(16 * w + 4 * g + e) + r);
+            for (int e = 0; e < 4; ++e) {
+                const int base = 4 * (row_word(16 * w + 4 * g + e) + r);
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) st_dev1(rs, base + 64 * jt, ll_word(S[jt][e], tag));
+                for (int jt = 0; jt < 4; ++jt) st_dev1(rs, base + 64 * jt, ll_word(S[jt][e], tag));
+            }
         }
-        // rows 0-31 from LDS, 16 B per lane: row q >> 4, columns 4 (q & 15) .. +3
+        // rows from LDS (0-31, and 32-63 with u23), 16 B per lane: row q >> 4,
+        // columns 4 (q & 15) .. +3
+        const int nk = u23 ? 8 : 4;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 8; ++k) {
+            if (k >= nk) continue;
             const int q = tid - 128 + 128 * k;
             const int row = q >> 4, c4 = 4 * (q & 15);
-            const f4 x = *reinterpret_cast<const f4*>(u01 + row * kU01 + c4);
+            // k < 4: rows 0-31 (u01); k >= 4: rows 32-63 (u23)
+            const f4 x = *reinterpret_cast<const f4*>((k < 4 ? u01 : u23) + (row & 31) * kU01 + c4);
             u4 t;
 #pragma unroll
             for (int e = 0; e < 4; ++e) t[e] = ll_word(x[e], tag);
@@ -945,7 +960,7 @@ __device__ __forceinline__ void keep_pass1(const FusedArgs& a, Smem& sm, const C
     ChunkTmp T;
     h8 Qt[2];
     chunk_front<true>(a, sm, R, w, lane, 0, S, false, Qt, T);
-    publish_summary<false>(a, sm, S, slot, j, ep, w, lane);
+    publish_summary<true>(a, sm, S, slot, j, ep, w, lane, reinterpret_cast<float*>(sm.ST0));
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
         Qs[0][hh] = Qt[hh] * *reinterpret_cast<const h8*>(&sm.cp16[32 * hh + 8 * g]);
