@@ -1077,7 +1077,11 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
         const __amdgpu_buffer_rsrc_t rf = final_rsrc(a, seq);
         // the decays of every (span, row) of the slice, tag-checked and decoded
         // once into LDS floats (dfl), so that the fold reads plain values
-        float* dfl = reinterpret_cast<float*>(scr + kScanD + 4096);   // [ns << lrows] <= 128
+        // (everything the fold uses lies below ST0, the last chunk tile, so
+        // that the incoming state can be staged there while other waves of
+        // the workgroup still fold: the region ends by 33.3 KB, dfl at
+        // 33.5 KB, compA and compB up to 36 KB)
+        float* dfl = reinterpret_cast<float*>(scr + kScanD + 1536);   // [ns << lrows] <= 128
         const int nd = ns << lrows;
         // When every span slot of the sequence expects the same tag (the
         // steady state: the slots' epochs advance together), the folds take
@@ -1288,16 +1292,17 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
             }
             __builtin_amdgcn_s_sleep(kPollSleep);
         }
-        // Every owner has read this slot's epoch (it wrote S_in after reading
-        // the epochs), and so has every wave here: advance it. The barrier
-        // also frees the scratch (the chunk tiles) for the staging below and
-        // for the caller.
-        lds_barrier();
-        if (tid == 0) __hip_atomic_store(a.epoch + seq_slot + j, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // ST0 is outside the fold's scratch: stage right away
         if (stage_st0) {
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) st4(sm.ST0, 16 * jt + r, 16 * w + 4 * g, pack4(Sin[jt], 1.f));
         }
+        // Every owner has read this slot's epoch (it wrote S_in after reading
+        // the epochs), and so has every wave here: advance it. The barrier
+        // also makes the staged state (and anything the caller wrote to LDS
+        // before the exchange) visible, and frees the chunk tiles.
+        lds_barrier();
+        if (tid == 0) __hip_atomic_store(a.epoch + seq_slot + j, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -1403,13 +1408,12 @@ gla_fused_kernel(FusedArgs a_arg)
     if (KEEP && SPAN == 1) load_gate(a, b, h, c_first * kC, w, lane, zg);
     // the incoming state is nonzero past the first span, or with an initial state
     const bool has_in = j > 0 || a.init != nullptr;
+    if (tid < kD) sm.nw[tid] = nwr;   // the exchange's last barrier orders it
     f4 Sin[4];
     exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin, KEEP && has_in);
 
     // ---- 3. outputs -----------------------------------------------------------
-    if (tid < kD) sm.nw[tid] = nwr;
     if (KEEP) {
-        lds_barrier();   // the incoming state is in ST0
         if constexpr (SPAN == 1) {
             f4 O[4];
             K[0].get(O);
@@ -1655,11 +1659,10 @@ gla_fused_rk_kernel(FusedArgs a_arg)
     // ---- 2. boundary exchange --------------------------------------------------
     const bool has_in = j > 0 || a.init != nullptr;
     f4 Sin[4];
+    if (tid < kD) sm.nw[tid] = nwr;   // the exchange's last barrier orders it
     exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin, has_in);
 
-    // ---- 3. outputs: O_c += Qs_c S_in -------------------------------------------
-    if (tid < kD) sm.nw[tid] = nwr;
-    lds_barrier();   // the incoming state is in ST0
+    // ---- 3. outputs: O_c += Qs_c S_in (the state is in ST0) -----------------------
     // the gate of the next chunk loads while this one finishes
     u4 zc[2], zn[2];
     if (a.gate) load_gate(a, b, h, c_first * kC, w, lane, zc);
