@@ -39,6 +39,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 512 << 20     # 2x the Infinity Cache
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 DIRS = (0, 1, 2, 3)
+DIR_NAMES = ("l2r", "r2l", "t2b", "b2t")
 
 
 def lowrank_features(w) -> int:
@@ -120,17 +121,18 @@ def measured_traffic(workload: str):
         return None
 
 
-def rotation_groups(per_call: int, steps: int, rotate: bool) -> int:
-    """Input sets per scan order: enough that the sets span >= ROTATE_BYTES, and a
-    divisor of `steps` (so that whole replays of one graph over every set time exactly
-    `steps` steps) when `steps` allows that (else `steps` itself)."""
+def rotation_groups(per_call: int, rotate: bool) -> int:
+    """Input sets per scan order: enough that the sets of the four scan orders
+    together span >= ROTATE_BYTES (2x the Infinity Cache), whatever the step count."""
     if not rotate:
         return 1
-    need = math.ceil(ROTATE_BYTES / (per_call * len(DIRS)))
-    for g in range(need, steps + 1):
-        if steps % g == 0:
-            return g
-    return max(1, steps)
+    return max(1, math.ceil(ROTATE_BYTES / (per_call * len(DIRS))))
+
+
+def replay_plan(steps: int, n_groups: int):
+    """(full replays of the n_groups-step graph, steps of the remainder graph):
+    exactly `steps` steps in total."""
+    return steps // n_groups, steps % n_groups
 
 
 def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = True,
@@ -153,7 +155,7 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
 
     arrays = gla_synth.generate(w)
     per_call = alg_bytes(w, gate, init, lowrank)
-    nsets = len(DIRS) * rotation_groups(per_call, steps, rotate)
+    nsets = len(DIRS) * rotation_groups(per_call, rotate)
     dev = torch.device("cuda:0")
     base = [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in arrays]
     rng = np.random.default_rng(w.seed + 1000)
@@ -207,57 +209,102 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
         call(d, d)
     torch.cuda.synchronize()
     if use_graph:
-        # one graph holds n_groups consecutive steps over every input set, as a model's
-        # forward graph holds its blocks back to back; a replay runs n_groups steps
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for g in range(n_groups):
-                for d in DIRS:
-                    call(len(DIRS) * g + d, d)
+        # One graph holds n_groups consecutive steps over every input set, as a model's
+        # forward graph holds its blocks back to back; a second graph holds the first
+        # `rem` groups, so that replays of the two run exactly the requested steps.
+        def capture(groups):
+            g_ = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_):
+                for g in range(groups):
+                    for d in DIRS:
+                        call(len(DIRS) * g + d, d)
+            return g_
+        graph = capture(n_groups)
+        rem_graphs = {}
         torch.cuda.synchronize()
 
-        def run_steps(first, count):
-            assert first % n_groups == 0 and count % n_groups == 0
-            for _ in range(count // n_groups):
+        def run_steps(count):
+            full, rem = replay_plan(count, n_groups)
+            for _ in range(full):
                 graph.replay()
+            if rem:
+                if rem not in rem_graphs:
+                    rem_graphs[rem] = capture(rem)
+                rem_graphs[rem].replay()
+        # capture the remainder graphs outside the timed region
+        for c in (warmup, steps):
+            rem = replay_plan(c, n_groups)[1]
+            if rem and rem not in rem_graphs:
+                rem_graphs[rem] = capture(rem)
+        torch.cuda.synchronize()
     else:
-        def run_steps(first, count):
-            for n in range(first, first + count):
+        def run_steps(count):
+            for n in range(count):
                 for d in DIRS:
                     call(len(DIRS) * (n % n_groups) + d, d)
 
-    warm = (warmup + n_groups - 1) // n_groups * n_groups if use_graph else warmup
-    run_steps(0, warm)
+    run_steps(warmup)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    run_steps(warm, steps)
+    run_steps(steps)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     ncalls = steps * len(DIRS)
     dir_us = None
+    dir_stats = None
+    errors = None
     if per_dir and use_graph:
         # each scan order on its own: graphs of one direction's calls over the rotating sets
         dir_us = {}
         reps = max(5, steps // 8)
         for d in DIRS:
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
+            graph_d = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph_d):
                 for i in range(nsets):
                     call(i, d)
-            graph.replay()
+            graph_d.replay()
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(reps):
-                graph.replay()
+                graph_d.replay()
             e1.record(stream)
             torch.cuda.synchronize()
-            dir_us[("l2r", "r2l", "t2b", "b2t")[d]] = 1e3 * e0.elapsed_time(e1) / (reps * nsets)
+            dir_us[DIR_NAMES[d]] = 1e3 * e0.elapsed_time(e1) / (reps * nsets)
+    if per_dir:
+        # per-call distribution: direct calls, each bracketed by two events on the stream
+        # the kernel runs on (inputs rotating as above); p10 / median / p90 per direction
+        dir_stats = {}
+        n_per = 100 if w.L * w.B <= 4096 else 50
+        for d in DIRS:
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n_per)]
+            for i, (a, b) in enumerate(evs):
+                a.record(stream)
+                call(len(DIRS) * (i % n_groups) + d, d)
+                b.record(stream)
+            torch.cuda.synchronize()
+            us = np.sort([1e3 * a.elapsed_time(b) for a, b in evs])
+            dir_stats[DIR_NAMES[d]] = {"p10_us": float(np.percentile(us, 10)),
+                                       "median_us": float(np.median(us)),
+                                       "p90_us": float(np.percentile(us, 90)), "calls": n_per}
+        if not (gate or init or lowrank):
+            # err_o / err_S of one call per direction on input set 0 against the fp64 oracle
+            import oracle
+            errors = {}
+            ins, out, fs = sets[0]
+            for d in DIRS:
+                call(0, d)
+                torch.cuda.synchronize()
+                o_ref, s_ref = oracle.recurrent(*arrays, w.grid_h, w.grid_w, DIR_NAMES[d])
+                errors[DIR_NAMES[d]] = {
+                    "err_o": float(oracle.rel_err(out.float().cpu().numpy(), o_ref)),
+                    "err_S": float(oracle.rel_err(fs.cpu().numpy(), s_ref))}
     kern, span, grid = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, w.chunk,
                                         int(is_fp32), lowrank)
     return {
@@ -272,6 +319,9 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
         "span": span,
         "grid": grid,
         "per_dir_us": dir_us,
+        "per_dir_call_us": dir_stats,
+        "errors": errors,
+        "rotated_bytes": nsets * per_call,
     }
 
 
@@ -299,7 +349,7 @@ def run_sswiglu(name: str, steps: int, warmup: int, rotate: bool = True):
     base = [None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
             for a in gla_synth.generate_sswiglu(B, gh, gw, C, Hd, seed=21)]
     per_call = (2 * B * L * C + 3 * Hd * C) * 2 + Hd * 40
-    nsets = len(DIRS) * rotation_groups(per_call, steps, rotate)
+    nsets = len(DIRS) * rotation_groups(per_call, rotate)
     sets = []
     for i in range(nsets):
         ins = base if i == 0 else [t.clone() for t in base]
@@ -349,59 +399,79 @@ def run_ceiling(w, steps: int, warmup: int):
     """Practical ceiling: a plain streaming kernel (libgtrgla_ceiling.so) that reads four
     fp16 tensors and writes one, each of the workload's [B, L, H, 64] size, i.e. the
     operator's q, k, v, log_gamma and out bytes, timed like the operator (four calls per
-    step, graph replay, sets rotated over >= 512 MiB). Returns microseconds per call."""
+    step, graph replay, sets rotated over >= 512 MiB). Each thread keeps 4 x unroll 16-byte
+    loads in flight; the fastest of a few unroll / grid choices is reported. Returns
+    (microseconds per call, the configuration)."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "chunkwise_gated_recurrence_amd", "libgtrgla_ceiling.so")
     lib = ctypes.CDLL(path)
     lib.gtr_stream_ceiling.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_int,
-                                                                ctypes.c_void_p]
+                                                                ctypes.c_int, ctypes.c_void_p]
     lib.gtr_stream_ceiling.restype = ctypes.c_int
     n = w.B * w.L * w.H * w.d_v
     per_call = 5 * n * 2
-    n_groups = rotation_groups(per_call, steps, True)
+    n_groups = rotation_groups(per_call, True)
     nsets = len(DIRS) * n_groups
     dev = torch.device("cuda:0")
     sets = [[torch.full((n,), 0.01 * (i + 1), dtype=torch.float16, device=dev) for i in range(5)]
             for _ in range(nsets)]
-    blocks = max(1, min((n // 8 + 255) // 256, 2048))
-
-    def call(i):
-        a, b, c, d, o = sets[i % nsets]
-        r = lib.gtr_stream_ceiling(a.data_ptr(), b.data_ptr(), c.data_ptr(), d.data_ptr(),
-                                   o.data_ptr(), n, blocks, torch.cuda.current_stream().cuda_stream)
-        if r != 0:
-            raise RuntimeError(f"gtr_stream_ceiling failed ({r})")
-
-    for i in range(len(DIRS)):
-        call(i)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(nsets):
-            call(i)
-    for _ in range(max(1, warmup // n_groups)):
-        graph.replay()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps // n_groups):
-        graph.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    return 1e3 * t0.elapsed_time(t1) / ((steps // n_groups) * nsets)
+    best = None
+    for unroll in (1, 2, 4):
+        for blocks in (512, 1024, 2048, 4096):
+            def call(i):
+                a, b, c, d, o = sets[i % nsets]
+                r = lib.gtr_stream_ceiling(a.data_ptr(), b.data_ptr(), c.data_ptr(), d.data_ptr(),
+                                           o.data_ptr(), n, blocks, unroll, stream.cuda_stream)
+                if r != 0:
+                    raise RuntimeError(f"gtr_stream_ceiling failed ({r})")
+
+            for i in range(len(DIRS)):
+                call(i)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(nsets):
+                    call(i)
+            reps = max(1, steps // (4 * n_groups))
+            for _ in range(max(1, warmup // n_groups)):
+                graph.replay()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            us = 1e3 * t0.elapsed_time(t1) / (reps * nsets)
+            if best is None or us < best[0]:
+                best = (us, {"unroll": unroll, "blocks": blocks})
+            del graph
+    return best
 
 
-def cpu_baseline(w, budget_s: float):
-    """The fp64 oracle as it stands, on this host, for as many single-direction
-    calls of the workload as fit in about `budget_s` seconds (at least one)."""
-    import gla_synth
+def host_cpu() -> dict:
+    """The host the oracle runs on: CPU model, logical CPUs, CPUs this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": affinity}
+
+
+def _time_oracle(w, arrays, threads: int, budget_s: float):
     import oracle
-
-    arrays = gla_synth.generate(w)
-    threads = min(oracle.default_threads(), w.B * w.H)
     calls = 0
     t0 = time.perf_counter()
     while True:
@@ -410,6 +480,22 @@ def cpu_baseline(w, budget_s: float):
         el = time.perf_counter() - t0
         if el >= budget_s or el / calls * (calls + 1) > 2.5 * budget_s:
             break
+    return calls, el
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle as it stands, on this host, for as many single-direction
+    calls of the workload as fit in about `budget_s` seconds (at least one), with
+    one thread per (batch, head) sequence up to the CPUs available; then again on
+    one thread for about a third of that budget."""
+    import gla_synth
+    import oracle
+
+    arrays = gla_synth.generate(w)
+    host = host_cpu()
+    threads = min(oracle.default_threads(), w.B * w.H)
+    calls, el = _time_oracle(w, arrays, threads, budget_s)
+    calls1, el1 = _time_oracle(w, arrays, 1, budget_s / 3)
     return {
         "value": calls * w.B * w.L / el,
         "unit": "tokens/s",
@@ -417,7 +503,12 @@ def cpu_baseline(w, budget_s: float):
         "kind": "oracle",
         "sample": f"{calls} single-direction calls of {w.name} "
                   f"(B={w.B}, {w.grid_h}x{w.grid_w}, H={w.H}, d_k={w.d_k}, d_v={w.d_v}) "
-                  f"in {el:.1f} s, fp64 token-by-token recurrence, one thread per (batch, head)",
+                  f"in {el:.1f} s, fp64 token-by-token recurrence, one thread per (batch, head) "
+                  f"sequence ({threads} threads)",
+        "threads": threads,
+        "host": host,
+        "single_thread": {"value": calls1 * w.B * w.L / el1, "unit": "tokens/s", "cores": 1,
+                          "sample": f"{calls1} calls in {el1:.1f} s on one thread"},
     }
 
 
@@ -475,9 +566,9 @@ def main() -> int:
         base_name, variant = split_name(name)
         ws = gla_synth.WORKLOADS[base_name]
         rs = run_workload(ws, max(20, args.steps // 4), args.warmup, rotate=not args.warm,
-                          use_graph=graph, **variant)
+                          use_graph=graph, per_dir=not any(variant.values()), **variant)
         gbs = rs["alg_bytes_per_call"] / (rs["call_us_mean"] * 1e-6) / 1e9
-        ceil_us = run_ceiling(ws, max(20, args.steps // 4), args.warmup) if not any(
+        ceil_us = run_ceiling(ws, max(20, args.steps // 4), args.warmup)[0] if not any(
             variant.values()) else None
         secondary.append({
             "workload": name, "tokens_per_s": rs["tokens_per_s"], "ms_per_step": rs["ms_per_step"],
@@ -486,16 +577,18 @@ def main() -> int:
             "mfma_frac": mfma_flops(ws) / (rs["call_us_mean"] * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
             "kernel": rs["kernel"], "span": rs["span"], "grid": rs["grid"],
             "traffic": measured_traffic(name),
+            "call_us_per_dir": rs["per_dir_call_us"], "errors_vs_oracle": rs["errors"],
         })
 
     mixer = [run_sswiglu(name, max(20, args.steps // 4), args.warmup, rotate=not args.warm)
              for name in args.sswiglu.split(",") if name]
 
-    ceil_us = run_ceiling(w, max(20, args.steps // 4), args.warmup)
+    ceil_us, ceil_cfg = run_ceiling(w, max(20, args.steps // 4), args.warmup)
     ceiling = {
         "kind": "plain streaming kernel: read 4 fp16 tensors, write 1 (the operator's q, k, v, "
-                "log_gamma, out bytes), same timing",
+                "log_gamma, out bytes), same timing; fastest of unroll x grid choices",
         "us_per_call": ceil_us,
+        "config": ceil_cfg,
         "GBs": 5 * w.B * w.L * w.H * w.d_v * 2 / (ceil_us * 1e-6) / 1e9,
         "operator_over_ceiling": r["call_us_mean"] / ceil_us,
     }
@@ -511,7 +604,8 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16" if w.dtype == "fp16" else "f32",
-        "data": ("synthetic (seeded gla_synth inputs, rotated over >=512 MiB of HBM buffers)"
+        "data": (f"synthetic (seeded gla_synth inputs, rotated over {r['rotated_bytes'] / 2**20:.0f} "
+                 f"MiB of HBM buffers, >= 512 MiB)"
                  if not args.warm else "synthetic (seeded gla_synth inputs, one warm set)"),
         "config": {
             "workload": w.name, "B": w.B, "grid": f"{w.grid_h}x{w.grid_w}", "L": w.L, "H": w.H,
@@ -532,8 +626,10 @@ def main() -> int:
             "alg_bytes_per_launch": r["alg_bytes_per_call"],
             "launch_us_mean": r["call_us_mean"],
             "launch_us_per_dir": r["per_dir_us"],
+            "call_us_per_dir": r["per_dir_call_us"],
             "mfma_frac": mfma_flops(w) / (r["call_us_mean"] * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
         },
+        "errors_vs_oracle": r["errors"],
         "ceiling": ceiling,
         "secondary": secondary,
         "spatial_swiglu": mixer,

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libgtrgla.so")
 
 # status codes (gtr_gla_status)
 OK, ERR_NULL, ERR_SHAPE, ERR_DIR, ERR_CHUNK, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, \
-    ERR_ALIAS, ERR_POLICY, ERR_VALUE = range(11)
+    ERR_ALIAS, ERR_POLICY, ERR_VALUE, ERR_EXCHANGE, ERR_WS_STATE = range(13)
 # scan orders (gtr_gla_dir)
 L2R, R2L, T2B, B2T = 0, 1, 2, 3
 DIRS = {"l2r": L2R, "r2l": R2L, "t2b": T2B, "b2t": B2T}
@@ -35,7 +35,7 @@ EXPORTED = (
     "gtr_gla_fwd_ws", "gtr_gla_fwd_f32_ws", "gtr_gla_fwd_ex", "gtr_gla_fwd_lowrank",
     "gtr_gla_lowrank_workspace_bytes", "gtr_gla_set_policy", "gtr_gla_get_policy",
     "gtr_gla_plan", "gtr_gla_plan_lowrank", "gtr_gla_status_str", "gtr_sswiglu_fwd",
-    "gtr_sswiglu_workspace_bytes",
+    "gtr_sswiglu_workspace_bytes", "gtr_gla_workspace_status", "gtr_gla_set_exchange_wait",
 )
 
 
@@ -91,6 +91,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gtr_sswiglu_workspace_bytes.restype = Z
     lib.gtr_gla_status_str.argtypes = [I]
     lib.gtr_gla_status_str.restype = ctypes.c_char_p
+    lib.gtr_gla_workspace_status.argtypes = [P, Z, P]
+    lib.gtr_gla_workspace_status.restype = I
+    lib.gtr_gla_set_exchange_wait.argtypes = [ctypes.c_uint, I]
+    lib.gtr_gla_set_exchange_wait.restype = I
     _lib = lib
     return lib
 
@@ -267,6 +271,22 @@ def gtr_gla_plan(B, H, grid_h, grid_w, d_k, d_v, chunk, is_fp32,
            ctypes.byref(span), ctypes.byref(grid))
     _raise(r, "gtr_gla_plan_lowrank" if lowrank else "gtr_gla_plan")
     return kern.value, span.value, grid.value
+
+
+def gtr_gla_workspace_status(workspace=None, workspace_bytes: int = 0, stream=None) -> int:
+    """Wait for the stream, read and clear a workspace's error word (None: the library's
+    own workspaces for this stream), re-initialising a flagged workspace. Returns the
+    status (OK, ERR_EXCHANGE or ERR_WS_STATE) rather than raising on those two."""
+    r = load_library().gtr_gla_workspace_status(_ptr(workspace), workspace_bytes,
+                                                _stream(stream))
+    if r not in (OK, ERR_EXCHANGE, ERR_WS_STATE):
+        _raise(r, "gtr_gla_workspace_status")
+    return r
+
+
+def gtr_gla_set_exchange_wait(wait_us: int, fault: int = 0) -> None:
+    _raise(load_library().gtr_gla_set_exchange_wait(int(wait_us), int(fault)),
+           "gtr_gla_set_exchange_wait")
 
 
 def gtr_gla_status_str(status: int) -> str:

@@ -63,10 +63,13 @@
 // chunk's log2-gate range, valid when that range is <= kGuard (every factor
 // then lies in [2^-8, 2^8]). A chunk with a wider range (very strong decay)
 // computes its scores exactly in fp32 instead.
+#include <atomic>
+#include <cstdlib>
 #include <type_traits>
 
 #include "gla_common.h"
 #include "gla_launch.h"
+#include "gla_ws.h"
 
 namespace gtrgla {
 
@@ -84,7 +87,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kGuard = 16.0f;   // max log2 range of a chunk for factorised scores
 constexpr int kTile = kC * 72;    // halves per LDS tile (rows padded to 72)
 constexpr int kAggWords = kD * kD + kD;   // U and D words of one span summary
-constexpr unsigned int kMaxPolls = 1u << 22;
 constexpr int kMaxSpans = 64;        // spans per sequence
 constexpr int kScanD = 32 * 1024;    // exchange scratch: byte offset of the decays
 constexpr int kDevScope = 16;        // cache policy: device-scope (sc1) access
@@ -229,7 +231,7 @@ struct FusedArgs {
     __half* out;
     float* final_state;
     unsigned int* epoch;        // [seq in launch][n_spans] low 8 bits: tag of the slot's words
-    unsigned int* err;          // set when a wait gives up
+    unsigned int* hdr;          // workspace header (gla_ws.h): error word, magic, layout
     unsigned int* agg;          // [seq in launch][agg_seq_words(n_spans)]  tagged, owner-major
     unsigned int* sin;          // [seq in launch][n_spans] slots of kSinSlotBytes: 2-byte words
     u4* park;                   // [workgroup][span - 1][256 threads][4]: parked outputs (long kept spans)
@@ -252,6 +254,9 @@ struct FusedArgs {
     const float* gbias;         // [H * dk]
     float inv_tau;
     int gtab_off;               // byte offset of the low-rank gate tables in dynamic LDS
+    unsigned int layout;        // exchange layout word of this launch (header word 2)
+    int fault;                  // test hook: nonzero, span 0 of every sequence publishes nothing
+    unsigned long long wait_ticks;   // longest wait of one exchange poll loop (100 MHz ticks)
 };
 
 // Dynamic LDS of every fused kernel: its Smem (or SmemRK), then, for the
@@ -314,6 +319,10 @@ struct Smem {
     int fail;
     int stale;
     int dstale;   // exchange: a decay word was stale in this poll
+    int expired;  // exchange: the owners' wait has passed its deadline
+    int poison;   // exchange: this workgroup's incoming state is missing or NaN
+    int wsbad;    // the workspace header does not allow this launch
+    unsigned int hdr[4];   // the workspace header, staged by wave 0 at the start
 };
 
 
@@ -784,7 +793,8 @@ __device__ __forceinline__ void load_gate(const FusedArgs& a, int b, int h, int 
 // o / sqrt(mean(o^2) + eps) * w * SiLU(z), z from load_gate (the row's mean
 // square is summed over the four lanes that hold it).
 __device__ __forceinline__ void store_out(Smem& sm, const FusedArgs& a, int b, int h, int t0, int w,
-                                          int lane, const f4 (&O)[4], const u4 (&z)[2])
+                                          int lane, const f4 (&O)[4], const u4 (&z)[2],
+                                          bool poison = false)
 {
     const int r = lane & 15, g = lane >> 4;
     const int t = 16 * w + r;
@@ -799,6 +809,7 @@ __device__ __forceinline__ void store_out(Smem& sm, const FusedArgs& a, int b, i
         ss += __shfl_xor(ss, 32, 64);
         f = a.scale * __builtin_amdgcn_rsqf(a.scale * a.scale * ss * (1.f / kD) + a.eps);
     }
+    if (poison) f = __builtin_nanf("");   // the failure path: every output NaN
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) st4(sm.Sc, t, 16 * jt + 4 * g, pack4(O[jt], f));
     __builtin_amdgcn_wave_barrier();
@@ -822,6 +833,28 @@ __device__ __forceinline__ void store_out(Smem& sm, const FusedArgs& a, int b, i
     }
 }
 
+// ---- workspace header (gla_ws.h)
+// The header, staged in LDS by wave 0 at the start (a 4-byte DMA per lane of
+// lanes 0-3, device scope): no registers are held for it, and wave 0's wait
+// for its chunk loads (issued after it) also covers it.
+__device__ __forceinline__ void stage_ws_header(const FusedArgs& a, unsigned int* hdr_lds, int w,
+                                                int lane)
+{
+    if (w == 0 && lane < 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(a.hdr, kWsHeaderBytes),
+                                                 (__attribute__((address_space(3))) void*)hdr_lds,
+                                                 4, 4 * lane, 0, 0, kDevScope);
+}
+// Whether this launch may use the workspace's exchange words: no error since
+// the last status check, and the region either zeroed by the library or last
+// used by fused launches of this very layout.
+__device__ __forceinline__ bool ws_header_ok(const FusedArgs& a, const unsigned int* hv)
+{
+    const unsigned int magic = hv[kWsMagicWord];
+    return hv[kWsErrWord] == 0 &&
+           (magic == kWsClean ||
+            (magic == kWsFused && hv[kWsLayoutWord] == a.layout && hv[kWsLayoutCheck] == ~a.layout));
+}
 // Summary words of one sequence, owner-major: for each owner o (slice of
 // 2^lo state elements) a contiguous region [ns][slice] of U words, then
 // [ns][slice / 64] D words (the decays of the slice's state rows), padded to
@@ -872,8 +905,12 @@ __device__ __forceinline__ void publish_summary(const FusedArgs& a, Smem& sm, co
             for (int e = 0; e < 4; ++e) dst[(rw + 4 * g + e) * kU01 + 16 * jt + r] = S[jt][e];
     }
     if (tid < kMaxSpans) sm.tags[tid] = (ep + 1u) & 0xFFu;
+    // wave 0 has waited for its loads, the staged header among them
+    if (w == 0 && lane == 0 && !ws_header_ok(a, sm.hdr)) sm.wsbad = 1;
     lds_barrier();
-    if (w >= 2) {
+    // an untrusted workspace: nothing is published (the caller takes the
+    // failure path); the fault hook silences span 0 of every sequence
+    if (w >= 2 && !sm.wsbad && !(a.fault && j == 0)) {
         const unsigned int tag = sm.tags[j];
         const int ns = a.n_spans, lo = a.slice_log2;
         const int ow = owner_region_words(ns, lo);
@@ -1035,12 +1072,58 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t final_rsrc(const FusedArgs& a,
                 a.final_state ? a.dk * kD * 4 : 0);
 }
 
-__device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local_seq, int seq, int j,
+// ---- workspace header (gla_ws.h) and the failure paths ------------------------
+// After a successful exchange, workgroup 0 records the layout in a workspace
+// that was still clean. Every workgroup of the launch has read the header by
+// then, or reads either value, which both admit this layout.
+__device__ __forceinline__ void mark_ws_header(const FusedArgs& a, const unsigned int* hv, int tid)
+{
+    if (blockIdx.x == 0 && tid == 0 && hv[kWsMagicWord] == kWsClean) {
+        const __amdgpu_buffer_rsrc_t rh = rsrc(a.hdr, kWsHeaderBytes);
+        __builtin_amdgcn_raw_buffer_store_b32(a.layout, rh, 4 * kWsLayoutWord, 0, kDevScope);
+        __builtin_amdgcn_raw_buffer_store_b32(~a.layout, rh, 4 * kWsLayoutCheck, 0, kDevScope);
+        __builtin_amdgcn_raw_buffer_store_b32(kWsFused, rh, 4 * kWsMagicWord, 0, kDevScope);
+    }
+}
+// A launch on an untrusted workspace publishes nothing and waits for nothing:
+// it flags the header and writes NaN to every output row of its span and (span
+// 0) to the sequence's final state.
+__device__ void fail_untrusted(const FusedArgs& a, int b, int h, int seq, int j, int c_first,
+                               int n_c, int w, int lane)
+{
+    const int tid = 64 * w + lane;
+    if (tid == 0) atomicOr(a.hdr + kWsErrWord, kWsErrState);
+    const u4 nan4 = {0x7E007E00u, 0x7E007E00u, 0x7E007E00u, 0x7E007E00u};
+    for (int c = 0; c < n_c; ++c) {
+        const long long off = row_offset(a, b, h, (c_first + c) * kC + 16 * w + (lane & 15));
+        if (off >= 0) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                *reinterpret_cast<u4*>(a.out + off + 8 * (lane >> 4) + 32 * hh) = nan4;
+        }
+    }
+    if (j == 0) {
+        const __amdgpu_buffer_rsrc_t rf = final_rsrc(a, seq);
+        for (int e = tid; e < kD * kD; e += kThreads)
+            __builtin_amdgcn_raw_buffer_store_b32(0x7FC00000u, rf, 4 * e, 0, 0);
+    }
+}
+
+// Every wait of the exchange is bounded by a deadline on the chip's 100 MHz
+// real-time counter (a.wait_ticks per poll loop). A wait that passes it gives
+// up: the error word of the workspace header records it, an owner hands NaN
+// incoming states (with the expected tags, so that its readers stop waiting)
+// and a NaN final state to its slice, and a reader that gives up, or receives
+// NaN, makes its workgroup write NaN outputs. Returns that poison flag.
+__device__ __forceinline__ unsigned long long now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+__device__ __forceinline__ bool exchange(const FusedArgs& a, Smem& sm, int local_seq, int seq, int j,
                                          long long seq_slot, int w, int lane, f4 (&Sin)[4],
                                          bool stage_st0)
 {
     const int tid = 64 * w + lane;
     const int r = lane & 15, g = lane >> 4;
+    if (tid == 0) sm.poison = 0;
     lds_barrier();   // every wave is done with the chunk tiles
     // The chunk tiles are free now: 45 KB of LDS scratch for the exchange.
     unsigned char* scr = reinterpret_cast<unsigned char*>(sm.Kh);
@@ -1127,6 +1210,8 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
             }
         };
         float run0 = 0.f;   // ranged fold: the initial state of my element
+        const unsigned long long t_start = now_ticks();
+        bool gave_up = false;
         for (unsigned int polls = 0;; ++polls) {
             {   // every wave loads a share of the region
                 for (int k0 = 64 * w; k0 < nl; k0 += 256) {
@@ -1211,17 +1296,30 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                 run0 = a.init ? s0[ei] : 0.f;
             }
             if (!__all(ok) && lane == 0) sm.stale = 1;
+            if (tid == 0) sm.expired = (now_ticks() - t_start) > a.wait_ticks ? 1 : 0;
             lds_barrier();
             const bool stale = sm.stale;
             if (!stale) break;
-            if (polls > kMaxPolls) {
-                if (tid == 0) atomicOr(a.err, 1u);
+            if (sm.expired) {   // (read by every thread before tid 0 rewrites it)
+                gave_up = true;
                 break;
             }
-            lds_barrier();   // every thread has read the flag before it is reset
+            lds_barrier();   // every thread has read the flags before they are reset
             __builtin_amdgcn_s_sleep(2);
         }
-        if (P > 1) {
+        if (gave_up) {
+            // NaN incoming states for every span of the slice, with the tags
+            // their readers expect, and a NaN final state
+            if (tid == 0) atomicOr(a.hdr + kWsErrWord, kWsErrExchange);
+            const unsigned short nanw = 0x7E00u;
+            for (int e = tid; e < (1 << lo); e += kThreads) {
+                int voff = 2 * (e_first + e);
+                for (int m = 0; m < ns; ++m, voff += kSinSlotBytes)
+                    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(nanw | (sm.tags[m] & 1u)),
+                                                          rs, voff, 0, kDevScope);
+                __builtin_amdgcn_raw_buffer_store_b32(0x7FC00000u, rf, 4 * (e_first + e), 0, 0);
+            }
+        } else if (P > 1) {
             // the ranges before mine (at most three), from the initial state;
             // then my range again, writing the incoming states
             float run = run0;
@@ -1268,7 +1366,9 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
         const unsigned int tag = sm.tags[j];
         const __amdgpu_buffer_rsrc_t rsn =
             rsrc(reinterpret_cast<const unsigned char*>(a.sin) + (seq_slot + j) * kSinSlotBytes, kSinSlotBytes);
-        for (unsigned int polls = 0;; ++polls) {
+        const unsigned long long t_start = now_ticks();
+        bool bad = false;
+        for (;;) {
             asm volatile("" ::: "memory");   // a fresh load every round
             unsigned short x[4][4];
 #pragma unroll
@@ -1286,12 +1386,19 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
                     Sin[jt][e] = sin_value(x[jt][e]);
                 }
             if (__all(ok)) break;
-            if (polls > kMaxPolls) {
-                if (lane == 0) atomicOr(a.err, 1u);
+            if (now_ticks() - t_start > a.wait_ticks) {   // wave-uniform
+                if (lane == 0) atomicOr(a.hdr + kWsErrWord, kWsErrExchange);
+                bad = true;
                 break;
             }
             __builtin_amdgcn_s_sleep(kPollSleep);
         }
+        // a NaN incoming state (an owner that gave up) poisons the workgroup too
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bad |= __builtin_isnan(Sin[jt][e]);
+        if (__any(bad) && lane == 0) sm.poison = 1;
         // ST0 is outside the fold's scratch: stage right away
         if (stage_st0) {
 #pragma unroll
@@ -1304,6 +1411,7 @@ __device__ __forceinline__ void exchange(const FusedArgs& a, Smem& sm, int local
         lds_barrier();
         if (tid == 0) __hip_atomic_store(a.epoch + seq_slot + j, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    return sm.poison != 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1352,11 +1460,13 @@ gla_fused_kernel(FusedArgs a_arg)
     const long long seq_slot = (long long)local_seq * a.n_spans;
     const unsigned int ep = __builtin_amdgcn_raw_buffer_load_b32(
         rsrc(a.epoch + seq_slot, 4 * a.n_spans), 4 * tid, 0, kDevScope);
+    stage_ws_header(a, sm.hdr, w, lane);   // checked at the publish
     // RMSNorm weight of the output epilogue (an empty resource without a gate)
     const float nwr = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
         rsrc(a.norm_w, a.gate ? 4 * kD : 0), 4 * (tid & (kD - 1)), 0, 0));
     ChunkRegs cur;
     load_chunk<KEEP>(a, b, h, c_first * kC, w, lane, cur);
+    if (tid == 0) sm.wsbad = 0;   // ordered by the local pass's first barrier
     if (tid < kD) {
         sm.P[0][tid] = 0.f;
         sm.Pend[tid] = 0.f;
@@ -1397,6 +1507,10 @@ gla_fused_kernel(FusedArgs a_arg)
         }
         publish_summary<false>(a, sm, S, seq_slot + j, j, ep, w, lane);
     }
+    if (sm.wsbad) {   // set before the publish's barrier
+        fail_untrusted(a, b, h, seq, j, c_first, n_c, w, lane);
+        return;
+    }
 
     // ---- 2. boundary scan across the sequence's spans -------------------------
     // The first `owners` workgroups (a power of two <= n_spans) each own a
@@ -1410,7 +1524,8 @@ gla_fused_kernel(FusedArgs a_arg)
     const bool has_in = j > 0 || a.init != nullptr;
     if (tid < kD) sm.nw[tid] = nwr;   // the exchange's last barrier orders it
     f4 Sin[4];
-    exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin, KEEP && has_in);
+    const bool poison = exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin, KEEP && has_in);
+    if (!poison) mark_ws_header(a, sm.hdr, tid);
 
     // ---- 3. outputs -----------------------------------------------------------
     if (KEEP) {
@@ -1424,7 +1539,7 @@ gla_fused_kernel(FusedArgs a_arg)
                     for (int jt = 0; jt < 4; ++jt)
                         O[jt] = mfma(ld8(sm.ST0, 16 * jt + r, 32 * hh + 8 * g), Qs[0][hh], O[jt]);
             }
-            store_out(sm, a, b, h, c_first * kC, w, lane, O, zg);
+            store_out(sm, a, b, h, c_first * kC, w, lane, O, zg, poison);
         } else {
             // parked chunks: the next chunk's slot loads while this one finishes
             u4 pk[4], pn[4];
@@ -1454,7 +1569,7 @@ gla_fused_kernel(FusedArgs a_arg)
                         for (int jt = 0; jt < 4; ++jt)
                             O[jt] = mfma(ld8(sm.ST0, 16 * jt + r, 32 * hh + 8 * g), qs[hh], O[jt]);
                 }
-                store_out(sm, a, b, h, (c_first + c) * kC, w, lane, O, z);
+                store_out(sm, a, b, h, (c_first + c) * kC, w, lane, O, z, poison);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) pk[k] = pn[k];
             }
@@ -1483,7 +1598,7 @@ gla_fused_kernel(FusedArgs a_arg)
             chunk_front<true>(a, sm, cur, w, ln, kMaxKeep, S, c > 0, qt, T);
             load_chunk<true>(a, b, h, c + 1 < n_c ? (c_first + c + 1) * kC : a.L, w, ln, cur);
             chunk_back(sm, a, b, h, (c_first + c) * kC, w, ln, has_in || (c > 0), Oc, qt, T);
-            store_out(sm, a, b, h, (c_first + c) * kC, w, ln, Oc, z);
+            store_out(sm, a, b, h, (c_first + c) * kC, w, ln, Oc, z, poison);
         }
     }
 }
@@ -1578,6 +1693,8 @@ gla_fused_rk_kernel(FusedArgs a_arg)
         rsrc(a.epoch + seq_slot, 4 * a.n_spans), 4 * tid, 0, kDevScope);
     const float nwr = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
         rsrc(a.norm_w, a.gate ? 4 * kD : 0), 4 * (tid & (kD - 1)), 0, 0));
+    stage_ws_header(a, sm.hdr, w, lane);   // checked at the publish
+    if (tid == 0) sm.wsbad = 0;            // ordered by the first chunk's barrier
     dma_gkv(a, sk, b, h, c_first * kC, w, lane);
     if (a.z) dma_z(a, sk, b, c_first * kC, w, lane);
     u4 qn[2];
@@ -1656,11 +1773,17 @@ gla_fused_rk_kernel(FusedArgs a_arg)
             }
     }
 
+    if (sm.wsbad) {   // set before the publish's barrier
+        fail_untrusted(a, b, h, seq, j, c_first, n_c, w, lane);
+        return;
+    }
+
     // ---- 2. boundary exchange --------------------------------------------------
     const bool has_in = j > 0 || a.init != nullptr;
     f4 Sin[4];
     if (tid < kD) sm.nw[tid] = nwr;   // the exchange's last barrier orders it
-    exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin, has_in);
+    const bool poison = exchange(a, sm, local_seq, seq, j, seq_slot, w, lane, Sin, has_in);
+    if (!poison) mark_ws_header(a, sm.hdr, tid);
 
     // ---- 3. outputs: O_c += Qs_c S_in (the state is in ST0) -----------------------
     // the gate of the next chunk loads while this one finishes
@@ -1686,7 +1809,7 @@ gla_fused_rk_kernel(FusedArgs a_arg)
                     for (int jt = 0; jt < 4; ++jt)
                         O[jt] = mfma(ld8(sm.ST0, 16 * jt + r, 32 * hh + 8 * g), KQ[ki][hh], O[jt]);
             }
-            store_out(sm, a, b, h, (c_first + c) * kC, w, lane, O, zc);
+            store_out(sm, a, b, h, (c_first + c) * kC, w, lane, O, zc, poison);
         }
         zc[0] = zn[0];
         zc[1] = zn[1];
@@ -1702,6 +1825,62 @@ __global__ void fill_zero_kernel(unsigned char* p, size_t n)
          i += (size_t)gridDim.x * blockDim.x)
         reinterpret_cast<u4*>(p)[i] = u4{0u, 0u, 0u, 0u};
     if (blockIdx.x == 0 && threadIdx.x < n - 16 * n16) p[16 * n16 + threadIdx.x] = 0;
+}
+
+// Workspace initialisation: zero everything past the header, then a clean
+// header (error word 0, magic kWsClean).
+__global__ void init_ws_kernel(unsigned char* p, size_t n)
+{
+    const size_t n16 = n / 16;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x + kWsHeaderBytes / 16; i < n16;
+         i += (size_t)gridDim.x * blockDim.x)
+        reinterpret_cast<u4*>(p)[i] = u4{0u, 0u, 0u, 0u};
+    if (blockIdx.x == 0 && threadIdx.x < n - 16 * n16) p[16 * n16 + threadIdx.x] = 0;
+    if (blockIdx.x == 0 && threadIdx.x < kWsHeaderBytes / 4)
+        reinterpret_cast<unsigned int*>(p)[threadIdx.x] = threadIdx.x == kWsMagicWord ? kWsClean : 0u;
+}
+
+hipError_t init_workspace(void* p, size_t bytes, hipStream_t st)
+{
+    if (bytes < (size_t)kWsHeaderBytes) return hipErrorInvalidValue;
+    if (((uintptr_t)p & 15) != 0) return hipErrorInvalidValue;
+    const size_t n16 = bytes / 16;
+    int blocks = (int)((n16 + 255) / 256);
+    if (blocks < 1) blocks = 1;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(init_ws_kernel, dim3(blocks), dim3(256), 0, st, (unsigned char*)p, bytes);
+    return hipGetLastError();
+}
+
+// Exchange wait limit and the give-up test hook (process-wide).
+static std::atomic<unsigned int> g_wait_us{20000};
+static std::atomic<int> g_fault{0};
+void set_exchange_wait(unsigned int wait_us, int fault)
+{
+    g_wait_us.store(wait_us, std::memory_order_relaxed);
+    g_fault.store(fault, std::memory_order_relaxed);
+}
+unsigned int exchange_wait_us() { return g_wait_us.load(std::memory_order_relaxed); }
+
+// Ticks per microsecond of the counter the kernels read (s_memrealtime).
+static unsigned long long wall_ticks_per_ms()
+{
+    static int cached = 0;
+    if (cached == 0) {
+        int dev = 0, khz = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+            khz < 1)
+            khz = 100000;   // 100 MHz
+        cached = khz;
+    }
+    return (unsigned long long)cached;
+}
+
+unsigned int fused_layout_word(const FusedPlan& p)
+{
+    // one exchange slot layout per (spans per sequence, sequences per launch)
+    return 0x80000000u | ((unsigned int)p.seq_batch << 8) | (unsigned int)p.n_spans;
 }
 
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st)
@@ -1798,18 +1977,34 @@ static int resident_per_cu(int span, bool keep, bool rk, int var)
     return c;
 }
 
+// Test hook: GTR_GLA_MAX_RESIDENT=n caps the workgroups the plan takes as
+// resident at once (so that a small shape needs several launches).
+static long long resident_cap_from_env()
+{
+    if (const char* env = std::getenv("GTR_GLA_MAX_RESIDENT")) {
+        const long long v = std::atoll(env);
+        if (v > 0) return v;
+    }
+    return 0;
+}
+
 FusedPlan fused_plan(const Shape& s, int span_override, int rk_override, int var)
 {
     FusedPlan p;
     p.var = var;
     const int n_seq = s.B * s.H;
     const int nc = s.n_chunks;
+    const long long cap_env = resident_cap_from_env();
+    auto capacity = [&](int span, bool keep, bool rk) {
+        const long long cap = (long long)resident_per_cu(span, keep, rk, var) * device_cus();
+        return cap_env > 0 && cap_env < cap ? cap_env : cap;
+    };
     auto fill = [&](int span, bool keep, bool rk = false) {
         p.span = span;
         p.keep = keep || rk;
         p.rk = rk;
         p.n_spans = (nc + span - 1) / span;
-        const long long cap = (long long)resident_per_cu(span, keep, rk, var) * device_cus();
+        const long long cap = capacity(span, keep, rk);
         // sequences per launch, so that every workgroup of a launch is resident
         long long per = cap / p.n_spans;
         if (per < 1) per = 1;
@@ -1820,10 +2015,7 @@ FusedPlan fused_plan(const Shape& s, int span_override, int rk_override, int var
         while ((2 << lg) <= p.n_spans) ++lg;
         p.slice_log2 = 12 - lg;
     };
-    auto one_seq_fits = [&]() {
-        return (long long)p.n_spans <=
-               (long long)resident_per_cu(p.span, p.keep, p.rk, var) * device_cus();
-    };
+    auto one_seq_fits = [&]() { return (long long)p.n_spans <= capacity(p.span, p.keep, p.rk); };
     if (span_override > 0) {
         if (rk_override > 0 && rk_span_ok(span_override)) {
             fill(span_override, false, true);
@@ -1856,7 +2048,7 @@ FusedPlan fused_plan(const Shape& s, int span_override, int rk_override, int var
         if (whole()) return p;
     }
     // else streamed spans
-    const long long cap = (long long)resident_per_cu(1, false, false, var) * device_cus();
+    const long long cap = capacity(1, false, false);
     long long per_seq = cap / n_seq;
     if (per_seq < 1) per_seq = 1;
     if (per_seq > kMaxSpans) per_seq = kMaxSpans;
@@ -1912,7 +2104,11 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
     a.final_state = final_state;
     unsigned char* base = (unsigned char*)ws;
     const size_t slots = (size_t)p.seq_batch * p.n_spans;
-    a.err = (unsigned int*)base;
+    a.hdr = (unsigned int*)base;
+    a.layout = fused_layout_word(p);
+    a.fault = g_fault.load(std::memory_order_relaxed);
+    a.wait_ticks = (unsigned long long)g_wait_us.load(std::memory_order_relaxed) *
+                   wall_ticks_per_ms() / 1000ull;
     a.epoch = (unsigned int*)(base + 256);
     a.agg = (unsigned int*)(base + 256 + align256(slots * sizeof(unsigned int)));
     a.sin = a.agg + (size_t)p.seq_batch * agg_seq_words(p.n_spans);

@@ -15,6 +15,7 @@
 // exponent of a gate sum can overflow, whatever the gates.
 #include "gla_common.h"
 #include "gla_launch.h"
+#include "gla_ws.h"
 
 namespace gtrgla {
 
@@ -194,8 +195,12 @@ generic_gate_kernel(T* __restrict__ out, const T* __restrict__ gate, const float
 size_t generic_workspace_bytes(const Shape& s)
 {
     const size_t nb = (size_t)s.B * s.H * s.n_chunks;
-    return nb * ((size_t)s.d_k * s.d_v + s.d_k) * sizeof(float);
+    return kWsHeaderBytes + nb * ((size_t)s.d_k * s.d_v + s.d_k) * sizeof(float);
 }
+
+// The generic kernels overwrite what a fused launch left past the header:
+// mark the header so that no fused launch trusts those words.
+__global__ void mark_dirty_kernel(unsigned int* hdr) { hdr[kWsMagicWord] = kWsDirty; }
 
 template <typename T, int DKMAX>
 static hipError_t launch_generic_t(const T* q, const T* k, const T* v, const T* lg, const Shape& s,
@@ -203,7 +208,8 @@ static hipError_t launch_generic_t(const T* q, const T* k, const T* v, const T* 
                                    hipStream_t st)
 {
     const size_t nb = (size_t)s.B * s.H * s.n_chunks;
-    float* wsU = static_cast<float*>(ws);
+    hipLaunchKernelGGL(mark_dirty_kernel, dim3(1), dim3(1), 0, st, static_cast<unsigned int*>(ws));
+    float* wsU = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + kWsHeaderBytes);
     float* wsD = wsU + nb * s.d_k * (size_t)s.d_v;
     const int threads = ((s.d_v > 64 ? s.d_v : 64) + 63) / 64 * 64;
     const unsigned grid = (unsigned)nb;

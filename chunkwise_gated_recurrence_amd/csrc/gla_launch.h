@@ -10,6 +10,8 @@ namespace gtrgla {
 
 // Generic three-phase path (gla_generic.hip).
 size_t generic_workspace_bytes(const Shape& s);
+// The generic kernels use the workspace past its header and mark the header
+// dirty (a fused launch that finds it so does not trust the exchange words).
 hipError_t launch_generic(const void* q, const void* k, const void* v, const void* lg,
                           bool is_fp32, const Shape& s, const Extras& x, void* out,
                           float* final_state, void* ws, hipStream_t st);
@@ -37,6 +39,16 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
 
 // Zero fill by a kernel (graph-capturable); p must be 16-byte aligned.
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
+// Workspace (re)initialisation by one kernel (graph-capturable): zero the whole
+// region and write a clean header (gla_ws.h). bytes >= kWsHeaderBytes.
+hipError_t init_workspace(void* p, size_t bytes, hipStream_t st);
+
+// The in-kernel exchange's wait limit (microseconds per poll loop) and the test
+// hook that silences span 0 of every sequence; read at each fused launch.
+void set_exchange_wait(unsigned int wait_us, int fault);
+unsigned int exchange_wait_us();
+// Exchange layout word of a plan (the header's word 2).
+unsigned int fused_layout_word(const FusedPlan& p);
 
 // Low-rank gate (gla_gate.hip): z = x W1 per token, [rows, 16] fp32 in
 // natural rank order; and log_gamma [rows, K] (K = H dk,

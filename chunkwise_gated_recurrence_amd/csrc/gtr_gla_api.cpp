@@ -14,6 +14,9 @@
 #include <utility>
 
 #include "gla_launch.h"
+#include "gla_ws.h"
+#include <cstdio>
+#include <vector>
 
 namespace {
 
@@ -192,7 +195,7 @@ struct WsLayout {
         return seq_batch < o.seq_batch;
     }
 };
-const WsLayout kWsClean = {0, 0, 0};
+const WsLayout kWsLayoutClean = {0, 0, 0};
 std::mutex g_state_mu;
 std::map<uintptr_t, WsLayout> g_ws_state;
 
@@ -206,7 +209,7 @@ bool workspace_ready_for(const void* ws, const WsLayout& l)
 {
     std::lock_guard<std::mutex> lk(g_state_mu);
     auto it = g_ws_state.find((uintptr_t)ws);
-    return it != g_ws_state.end() && (it->second == kWsClean || it->second == l);
+    return it != g_ws_state.end() && (it->second == kWsLayoutClean || it->second == l);
 }
 
 // Library-owned workspaces for the non-_ws entry points, one per (device,
@@ -237,9 +240,9 @@ int cached_workspace(size_t need, hipStream_t st, const WsLayout& layout, void**
             c.ptr = nullptr;
             return GTR_GLA_ERR_HIP;
         }
-        if (gtrgla::fill_zero(c.ptr, bytes, st) != hipSuccess) return GTR_GLA_ERR_HIP;
+        if (gtrgla::init_workspace(c.ptr, bytes, st) != hipSuccess) return GTR_GLA_ERR_HIP;
         c.bytes = bytes;
-        mark_workspace(c.ptr, kWsClean);
+        mark_workspace(c.ptr, kWsLayoutClean);
     }
     *out = c.ptr;
     return GTR_GLA_OK;
@@ -273,6 +276,40 @@ int validate_lowrank(const LowRank& g, const void* out, const float* fs, const S
     return GTR_GLA_OK;
 }
 
+// GTR_GLA_LOG=1: one line per call on stderr with the chosen kernel and launch geometry.
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char* env = std::getenv("GTR_GLA_LOG");
+        return env && env[0] && env[0] != '0';
+    }();
+    return on;
+}
+
+void log_call(const Shape& s, bool is_fp32, const Choice& c, int var, bool own_ws)
+{
+    if (c.kernel == kFused) {
+        const FusedPlan& p = c.plan;
+        const int n_seq = s.B * s.H;
+        std::fprintf(stderr,
+                     "gtr_gla: B=%d H=%d grid=%dx%d L=%d d_k=%d d_v=%d dir=%d chunk=%d %s "
+                     "policy=%d kernel=fused%s variant=%d span=%d n_spans=%d seq_batch=%d "
+                     "launches=%d grid_wg=%d slice_log2=%d workspace=%zu (%s) wait_us=%u\n",
+                     s.B, s.H, s.grid_h, s.grid_w, s.L, s.d_k, s.d_v, s.dir, s.chunk,
+                     is_fp32 ? "fp32" : "fp16", current_policy(),
+                     p.rk ? "-rk" : (p.keep ? "-keep" : "-streamed"), var, p.span, p.n_spans,
+                     p.seq_batch, (n_seq + p.seq_batch - 1) / p.seq_batch, p.grid, p.slice_log2,
+                     c.ws_bytes, own_ws ? "library" : "caller", gtrgla::exchange_wait_us());
+    } else {
+        std::fprintf(stderr,
+                     "gtr_gla: B=%d H=%d grid=%dx%d L=%d d_k=%d d_v=%d dir=%d chunk=%d %s "
+                     "policy=%d kernel=generic chunk_tiles=%d workspace=%zu (%s)\n",
+                     s.B, s.H, s.grid_h, s.grid_w, s.L, s.d_k, s.d_v, s.dir, s.chunk,
+                     is_fp32 ? "fp32" : "fp16", current_policy(), s.B * s.H * s.n_chunks,
+                     c.ws_bytes, own_ws ? "library" : "caller");
+    }
+}
+
 int run(const void* q, const void* k, const void* v, const void* lg, int B, int H, int gh, int gw,
         int dk, int dv, int dir, int chunk, void* out, float* fs, bool is_fp32, void* ws,
         size_t ws_bytes, bool own_ws, hipStream_t st, const Extras& x0 = Extras{},
@@ -291,7 +328,9 @@ int run(const void* q, const void* k, const void* v, const void* lg, int B, int 
         if (r != GTR_GLA_OK) return r;
     }
     Extras x = x0;
-    const Choice c = choose(s, is_fp32, current_policy(), lr ? 2 : (x0.init || x0.gate) ? 1 : 0);
+    const int var = lr ? 2 : (x0.init || x0.gate) ? 1 : 0;
+    const Choice c = choose(s, is_fp32, current_policy(), var);
+    if (log_enabled()) log_call(s, is_fp32, c, var, own_ws);
     const WsLayout layout = c.kernel == kFused ? WsLayout{kFused, c.plan.n_spans, c.plan.seq_batch}
                                                : WsLayout{kGeneric, 0, 0};
     if (own_ws) {
@@ -317,7 +356,7 @@ int run(const void* q, const void* k, const void* v, const void* lg, int B, int 
         }
     }
     if (e == hipSuccess && c.kernel == kFused) {
-        if (!workspace_ready_for(ws, layout)) e = gtrgla::fill_zero(ws, c.base_bytes, st);
+        if (!workspace_ready_for(ws, layout)) e = gtrgla::init_workspace(ws, c.base_bytes, st);
         if (e == hipSuccess) e = gtrgla::launch_fused(q, k, v, lg, s, x, c.plan, out, fs, ws, st);
     } else if (e == hipSuccess) {
         e = gtrgla::launch_generic(q, k, v, lg, is_fp32, s, x, out, fs, ws, st);
@@ -361,8 +400,9 @@ int gtr_gla_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t 
 {
     if (!workspace) return GTR_GLA_ERR_NULL;
     if (workspace_bytes == 0) return GTR_GLA_ERR_WORKSPACE;
-    if (gtrgla::fill_zero(workspace, workspace_bytes, stream) != hipSuccess) return GTR_GLA_ERR_HIP;
-    mark_workspace(workspace, kWsClean);
+    if (workspace_bytes < (size_t)gtrgla::kWsHeaderBytes) return GTR_GLA_ERR_WORKSPACE;
+    if (gtrgla::init_workspace(workspace, workspace_bytes, stream) != hipSuccess) return GTR_GLA_ERR_HIP;
+    mark_workspace(workspace, kWsLayoutClean);
     return GTR_GLA_OK;
 }
 
@@ -485,9 +525,70 @@ const char* gtr_gla_status_str(int status)
     case GTR_GLA_ERR_HIP: return "HIP runtime error";
     case GTR_GLA_ERR_ALIAS: return "an output overlaps an input or the other output";
     case GTR_GLA_ERR_POLICY: return "unknown policy";
-    case GTR_GLA_ERR_VALUE: return "invalid scalar argument (norm_eps must be finite and >= 0, inv_tau finite and > 0)";
+    case GTR_GLA_ERR_VALUE: return "invalid scalar argument (norm_eps must be finite and >= 0, inv_tau finite and > 0, exchange wait 1 us .. 10 s)";
+    case GTR_GLA_ERR_EXCHANGE: return "a call's boundary exchange gave up waiting (its outputs are NaN); the workspace was re-initialised";
+    case GTR_GLA_ERR_WS_STATE: return "a call found its workspace neither initialised nor of its layout (its outputs are NaN); the workspace was re-initialised";
     default: return "unknown status";
     }
+}
+
+}  // extern "C"
+
+namespace {
+// Read and clear the error word of one workspace; re-initialise it when set.
+int check_workspace(void* ws, size_t bytes, hipStream_t st, unsigned int* err_out)
+{
+    unsigned int err = 0;
+    if (hipMemcpyAsync(&err, ws, sizeof(err), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return GTR_GLA_ERR_HIP;
+    if (err != 0) {
+        if (gtrgla::init_workspace(ws, bytes, st) != hipSuccess || hipStreamSynchronize(st) != hipSuccess)
+            return GTR_GLA_ERR_HIP;
+        mark_workspace(ws, kWsLayoutClean);
+    }
+    *err_out |= err;
+    return GTR_GLA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int gtr_gla_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    unsigned int err = 0;
+    if (workspace) {
+        if (workspace_bytes < (size_t)gtrgla::kWsHeaderBytes) return GTR_GLA_ERR_WORKSPACE;
+        const int r = check_workspace(workspace, workspace_bytes, stream, &err);
+        if (r != GTR_GLA_OK) return r;
+    } else {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return GTR_GLA_ERR_HIP;
+        std::vector<std::pair<void*, size_t>> mine;
+        {
+            std::lock_guard<std::mutex> lk(g_ws_mu);
+            for (auto& kv : g_ws)
+                if (kv.first.first.first == dev && kv.first.first.second == (uintptr_t)stream &&
+                    kv.second.ptr)
+                    mine.emplace_back(kv.second.ptr, kv.second.bytes);
+        }
+        for (auto& m : mine) {
+            const int r = check_workspace(m.first, m.second, stream, &err);
+            if (r != GTR_GLA_OK) return r;
+        }
+    }
+    // an untrusted workspace first: its error word may hold anything else
+    if (err & gtrgla::kWsErrState) return GTR_GLA_ERR_WS_STATE;
+    if (err & gtrgla::kWsErrExchange) return GTR_GLA_ERR_EXCHANGE;
+    if (err) return GTR_GLA_ERR_WS_STATE;
+    return GTR_GLA_OK;
+}
+
+int gtr_gla_set_exchange_wait(unsigned int wait_us, int fault)
+{
+    if (wait_us < 1 || wait_us > 10000000u) return GTR_GLA_ERR_VALUE;
+    gtrgla::set_exchange_wait(wait_us, fault);
+    return GTR_GLA_OK;
 }
 
 }  // extern "C"

@@ -66,8 +66,15 @@ typedef enum {
     GTR_GLA_ERR_HIP = 7,         /* the HIP runtime reported an error               */
     GTR_GLA_ERR_ALIAS = 8,       /* an output overlaps an input or the other output  */
     GTR_GLA_ERR_POLICY = 9,      /* unknown policy value                             */
-    GTR_GLA_ERR_VALUE = 10       /* invalid scalar argument (norm_eps not finite or < 0,
-                                    inv_tau not finite or <= 0)                     */
+    GTR_GLA_ERR_VALUE = 10,      /* invalid scalar argument (norm_eps not finite or < 0,
+                                    inv_tau not finite or <= 0, exchange wait out of
+                                    range)                                          */
+    GTR_GLA_ERR_EXCHANGE = 11,   /* (gtr_gla_workspace_status only) a fused call's
+                                    boundary exchange gave up waiting: that call wrote
+                                    NaN outputs and final state                      */
+    GTR_GLA_ERR_WS_STATE = 12    /* (gtr_gla_workspace_status only) a fused call found
+                                    its workspace neither initialised nor last used by
+                                    calls of its layout: it wrote NaN outputs          */
 } gtr_gla_status;
 
 /* Launch policies (the pages' length-aware scheduling: short sequences take
@@ -88,8 +95,17 @@ typedef enum {
  * accumulation, fp32 state and fp32 final_state.
  * Uses a workspace that the library allocates on the first call for each
  * (device, stream) pair and grows when a larger shape arrives; call it once
- * outside stream capture for a shape before capturing it. Calls on different
- * streams use different workspaces and may overlap.
+ * outside stream capture for a shape before capturing it.
+ *
+ * Concurrency of the fused kernels. A fused launch hands boundary states
+ * between its workgroups inside the kernel, so it needs all of them resident
+ * on the GPU at once; the launch policy sizes its grid to the whole chip. Run
+ * fused calls one at a time per GPU (one stream, or streams ordered by
+ * events), and not beside other kernels that occupy compute units for long.
+ * If some workgroups cannot become resident, every wait in the exchange gives
+ * up after its deadline (gtr_gla_set_exchange_wait, 20 ms by default): the
+ * call then writes NaN outputs and final state instead of hanging or returning
+ * wrong numbers, and gtr_gla_workspace_status reports it.
  */
 int gtr_gla_fwd(const void* q, const void* k, const void* v, const void* log_gamma,
                 int B, int H, int grid_h, int grid_w, int d_k, int d_v,
@@ -106,9 +122,13 @@ int gtr_gla_fwd_f32(const float* q, const float* k, const float* v, const float*
  * 0539edu.com page, appendix E.3.1).
  * gtr_gla_workspace_bytes returns the size needed by the _ws entry points for
  * this shape and precision under the current policy, or 0 for invalid sizes.
- * A workspace must be cleared once by gtr_gla_workspace_init before its first
- * use; the kernels leave it ready for the next call. One workspace must not
- * be used by two calls that may run at the same time.
+ * A workspace must be initialised once by gtr_gla_workspace_init before its
+ * first use; the kernels leave it ready for the next call of the same layout,
+ * and an eager call of another layout re-initialises it first. A fused kernel
+ * that finds it in any other state writes NaN outputs (see
+ * gtr_gla_workspace_status). One workspace must not be used by two calls that
+ * may run at the same time. GTR_GLA_LOG=1 in the environment prints each
+ * call's kernel, plan and launch geometry on stderr.
  * The _ws entry points allocate nothing and may be captured in a HIP graph.
  */
 /*
@@ -181,6 +201,32 @@ int gtr_gla_fwd_f32_ws(const float* q, const float* k, const float* v, const flo
                        int B, int H, int grid_h, int grid_w, int d_k, int d_v,
                        int dir, int chunk, float* out, float* final_state,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gtr_gla_workspace_status -- outside the hot path: waits for `stream`, reads
+ * and clears the error word of a workspace (NULL: every workspace the library
+ * owns for the current device and this stream), and re-initialises a workspace
+ * whose word was set, so that the next call starts clean. Returns GTR_GLA_OK,
+ * GTR_GLA_ERR_EXCHANGE (some fused call on it since the last check gave up in
+ * its exchange; that call's outputs are NaN), GTR_GLA_ERR_WS_STATE (some fused
+ * call found the workspace uninitialised, written by something else, or last
+ * used by calls of another layout, e.g. a captured graph replayed after an
+ * eager call of another shape on the same workspace; its outputs are NaN), or
+ * GTR_GLA_ERR_HIP / GTR_GLA_ERR_WORKSPACE (workspace_bytes < 256).
+ * A workspace is never trusted blindly: its first 256 bytes are a header
+ * (error word, layout) that every fused launch checks before it uses the rest.
+ */
+int gtr_gla_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gtr_gla_set_exchange_wait -- process-wide, read at each fused launch: the
+ * longest time, in microseconds (1 .. 10^7; default 20000), that one wait of a
+ * fused kernel's boundary exchange may take before the call gives up (see
+ * gtr_gla_fwd). `fault` is a test hook of the give-up path and must be 0 in
+ * use: nonzero makes the first span of every sequence publish nothing, so
+ * that every fused call gives up after `wait_us`.
+ */
+int gtr_gla_set_exchange_wait(unsigned int wait_us, int fault);
 
 /*
  * Policy control, for A/B measurement and tests. The setting is process-wide

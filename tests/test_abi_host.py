@@ -89,10 +89,11 @@ def test_aliasing_outputs(lib):
 
 
 def test_workspace_checks(lib):
-    # fp32 always takes the generic kernels: U/S (d_k*d_v) and d (d_k) per chunk
+    # fp32 always takes the generic kernels: the 256-byte header, then U/S (d_k*d_v)
+    # and d (d_k) per chunk
     n = lib.gtr_gla_workspace_bytes(2, 3, 10, 13, 32, 16, 64, 1)
     chunks = 2 * 3 * ((10 * 13 + 63) // 64)
-    assert n == chunks * (32 * 16 + 32) * 4
+    assert n == 256 + chunks * (32 * 16 + 32) * 4
     assert lib.gtr_gla_workspace_bytes(0, 3, 10, 13, 32, 16, 64, 1) == 0
     assert lib.gtr_gla_workspace_bytes(2, 3, 10, 13, 32, 16, 48, 1) == 0
     assert _fwd(lib, PTRS, B=2, H=3, gh=10, gw=13, dk=32, dv=16, f32=True, ws=None, nws=1) == \
@@ -234,3 +235,16 @@ def test_sswiglu_checks():
     assert _ss(lib, B=2, ws=BASE + 8 * SEP, nws=n - 1) == gla.ERR_WORKSPACE
     assert _ss(lib, B=2, ws=BASE + 6 * SEP + 16, nws=n) == gla.ERR_ALIAS
     assert _ss(lib, B=2, ws=BASE + 16, nws=n) == gla.ERR_ALIAS
+
+
+def test_status_and_exchange_wait_validation(lib):
+    """The status query and the exchange-wait hook check their arguments before
+    any HIP call; the new status codes have descriptions."""
+    assert lib.gtr_gla_workspace_status(BASE, 255, None) == gla.ERR_WORKSPACE
+    assert lib.gtr_gla_workspace_status(BASE, 0, None) == gla.ERR_WORKSPACE
+    assert lib.gtr_gla_set_exchange_wait(0, 0) == gla.ERR_VALUE
+    assert lib.gtr_gla_set_exchange_wait(10 ** 7 + 1, 0) == gla.ERR_VALUE
+    assert lib.gtr_gla_set_exchange_wait(20000, 0) == gla.OK
+    for st in (gla.ERR_EXCHANGE, gla.ERR_WS_STATE):
+        text = gla.gtr_gla_status_str(st)
+        assert text and "unknown" not in text and "NaN" in text

@@ -37,3 +37,27 @@ def test_traffic_summary_only_for_matching_code(tmp_path, monkeypatch):
     (tmp_path / "traffic_w.txt").write_text("bytes_per_launch: 1234\nkernel_hash: 0000\n")
     assert bench.measured_traffic("w") is None
     assert bench.measured_traffic("missing") is None
+
+
+def test_rotation_spans_512_mib_for_any_step_count():
+    import gla_synth
+    for name in ("img640", "img1024", "batched640", "long2048"):
+        w = gla_synth.WORKLOADS[name]
+        per_call = bench.alg_bytes(w)
+        groups = bench.rotation_groups(per_call, True)
+        assert groups * len(bench.DIRS) * per_call >= bench.ROTATE_BYTES, name
+        assert (groups - 1) * len(bench.DIRS) * per_call < bench.ROTATE_BYTES, name
+    assert bench.rotation_groups(10 ** 6, False) == 1
+
+
+def test_replay_plan_runs_exactly_the_requested_steps():
+    for n_groups in (1, 3, 22, 87):
+        for steps in (0, 1, 5, 20, 21, 200, 201):
+            full, rem = bench.replay_plan(steps, n_groups)
+            assert full * n_groups + rem == steps and 0 <= rem < n_groups
+
+
+def test_host_cpu_fields():
+    h = bench.host_cpu()
+    assert h["nproc"] >= 1 and 1 <= h["affinity"] <= h["nproc"]
+    assert h["cpu_model"] is None or isinstance(h["cpu_model"], str)

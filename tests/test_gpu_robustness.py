@@ -1,0 +1,216 @@
+"""Failure paths and launch-loop coverage of the fused kernels on the GPU.
+
+* The in-kernel boundary exchange gives up within its deadline when a span's
+  summary never arrives (forced from the host: the exchange's test hook makes
+  span 0 of every sequence publish nothing). Every kernel still exits; the
+  call writes NaN outputs and final state; gtr_gla_workspace_status reports
+  GTR_GLA_ERR_EXCHANGE and re-initialises the workspace; the next call matches
+  the oracle. Covered for one-chunk spans, register-kept spans, and a ranged
+  fold (two span ranges per owner element), and for the library's own
+  workspace.
+* A workspace the kernel cannot trust (its bytes overwritten after use, or
+  last used by a call of another layout while a captured graph still expects
+  the old one) gives NaN outputs and GTR_GLA_ERR_WS_STATE instead of silently
+  wrong numbers; after the status call the same call is correct again.
+* The multi-launch loop (more sequences than fit on the chip at once) matches
+  the oracle: a test-only cap on resident workgroups forces several launches.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import gla_synth
+import oracle
+
+torch = pytest.importorskip("torch")
+import chunkwise_gated_recurrence_amd as gla  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+SMALL = gla_synth.WORKLOADS["img640"].with_(name="robust", B=1, H=2, grid_h=24, grid_w=20, seed=91)
+
+
+@pytest.fixture(autouse=True)
+def clean_state():
+    assert torch.cuda.is_available(), "the gpu tests need an MI355X"
+    saved = {k: os.environ.pop(k, None) for k in ("GTR_GLA_SPAN", "GTR_GLA_RK",
+                                                  "GTR_GLA_MAX_RESIDENT")}
+    gla.gtr_gla_set_policy(gla.POLICY_AUTO)
+    gla.gtr_gla_set_exchange_wait(20000, 0)
+    yield
+    gla.gtr_gla_set_exchange_wait(20000, 0)
+    gla.gtr_gla_set_policy(gla.POLICY_AUTO)
+    for k, v in saved.items():
+        os.environ.pop(k, None)
+        if v is not None:
+            os.environ[k] = v
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def outputs(w):
+    o = torch.zeros((w.B, w.L, w.H, w.d_v), dtype=torch.float16, device="cuda")
+    s = torch.zeros((w.B, w.H, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    return o, s
+
+
+def ws_call(x, w, d, ws, o, s):
+    gla.gtr_gla_fwd_ws(*x, w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, d, 64, o, s, ws,
+                       ws.numel())
+
+
+def check_oracle(arrays, w, d, o, s):
+    o_ref, s_ref = oracle.recurrent(*arrays, w.grid_h, w.grid_w, d)
+    eo = oracle.rel_err(o.cpu().numpy().astype(np.float64), o_ref)
+    es = oracle.rel_err(s.cpu().numpy(), s_ref)
+    assert eo <= TOL and es <= TOL, (eo, es)
+
+
+def all_nan(t):
+    return bool(torch.isnan(t.float()).all())
+
+
+GIVE_UP_CASES = {
+    # name: (workload, GTR_GLA_SPAN, GTR_GLA_RK, expected kernel of gtr_gla_plan)
+    "one_chunk": (SMALL, "1", None, 2),
+    "register_kept": (SMALL, "2", "1", 3),
+    "ranged_fold": (SMALL.with_(name="ranged", grid_h=64, grid_w=32), "1", None, 2),
+}
+
+
+@pytest.mark.parametrize("case", sorted(GIVE_UP_CASES))
+def test_exchange_gives_up_loudly_and_recovers(case):
+    w, span, rk, kernel = GIVE_UP_CASES[case]
+    os.environ["GTR_GLA_SPAN"] = span
+    if rk:
+        os.environ["GTR_GLA_RK"] = rk
+    assert gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 64, 0)[0] == kernel
+    arrays = gla_synth.generate(w)
+    x = [dev(a) for a in arrays]
+    nbytes = gla.gtr_gla_workspace_bytes(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 64, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    gla.gtr_gla_workspace_init(ws, nbytes)
+    o, s = outputs(w)
+    print(f"[case] forced give-up {case}", flush=True)
+    gla.gtr_gla_set_exchange_wait(2000, 1)
+    ws_call(x, w, 1, ws, o, s)
+    torch.cuda.synchronize()
+    assert all_nan(o) and all_nan(s)
+    assert gla.gtr_gla_workspace_status(ws, nbytes) == gla.ERR_EXCHANGE
+    assert gla.gtr_gla_workspace_status(ws, nbytes) == gla.OK   # cleared
+    print(f"[case] recovery after give-up {case}", flush=True)
+    gla.gtr_gla_set_exchange_wait(20000, 0)
+    for d in (1, 2):
+        ws_call(x, w, d, ws, o, s)
+        torch.cuda.synchronize()
+        check_oracle(arrays, w, d, o, s)
+    assert gla.gtr_gla_workspace_status(ws, nbytes) == gla.OK
+
+
+def test_library_workspace_give_up_is_reported():
+    w = SMALL
+    arrays = gla_synth.generate(w)
+    x = [dev(a) for a in arrays]
+    o, s = outputs(w)
+    print("[case] library workspace give-up", flush=True)
+    gla.gtr_gla_fwd(*x, w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 0, 64, o, s)   # warm
+    assert gla.gtr_gla_workspace_status() == gla.OK
+    gla.gtr_gla_set_exchange_wait(2000, 1)
+    gla.gtr_gla_fwd(*x, w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 0, 64, o, s)
+    torch.cuda.synchronize()
+    assert all_nan(o) and all_nan(s)
+    assert gla.gtr_gla_workspace_status() == gla.ERR_EXCHANGE
+    gla.gtr_gla_set_exchange_wait(20000, 0)
+    gla.gtr_gla_fwd(*x, w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 0, 64, o, s)
+    torch.cuda.synchronize()
+    check_oracle(arrays, w, 0, o, s)
+
+
+def test_overwritten_workspace_is_not_trusted():
+    w = SMALL
+    arrays = gla_synth.generate(w)
+    x = [dev(a) for a in arrays]
+    nbytes = gla.gtr_gla_workspace_bytes(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 64, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    gla.gtr_gla_workspace_init(ws, nbytes)
+    o, s = outputs(w)
+    ws_call(x, w, 0, ws, o, s)
+    torch.cuda.synchronize()
+    check_oracle(arrays, w, 0, o, s)
+    # the same memory rewritten by someone else (as a caching allocator may hand it out)
+    print("[case] overwritten workspace", flush=True)
+    ws.copy_(torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda"))
+    ws_call(x, w, 0, ws, o, s)
+    torch.cuda.synchronize()
+    assert all_nan(o)
+    assert gla.gtr_gla_workspace_status(ws, nbytes) == gla.ERR_WS_STATE
+    ws_call(x, w, 0, ws, o, s)
+    torch.cuda.synchronize()
+    check_oracle(arrays, w, 0, o, s)
+
+
+def test_graph_after_other_layout_on_same_workspace():
+    """A captured call keeps the layout it was captured with; an eager call of another
+    layout on the same workspace in between makes the replay fail loudly (NaN and a
+    status), not read the other layout's words; after the status call it replays right."""
+    wa, wb = SMALL, SMALL.with_(name="other", H=3, grid_h=40, grid_w=40, seed=92)
+    xa_np, xb_np = gla_synth.generate(wa), gla_synth.generate(wb)
+    xa, xb = [dev(a) for a in xa_np], [dev(a) for a in xb_np]
+    la = gla.gtr_gla_plan(wa.B, wa.H, wa.grid_h, wa.grid_w, 64, 64, 64, 0)
+    lb = gla.gtr_gla_plan(wb.B, wb.H, wb.grid_h, wb.grid_w, 64, 64, 64, 0)
+    assert la != lb   # two exchange layouts
+    nbytes = max(gla.gtr_gla_workspace_bytes(w.B, w.H, w.grid_h, w.grid_w, 64, 64, 64, 0)
+                 for w in (wa, wb))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    gla.gtr_gla_workspace_init(ws, nbytes)
+    oa, sa = outputs(wa)
+    ob, sb = outputs(wb)
+    ws_call(xa, wa, 2, ws, oa, sa)   # eager warm-up of the captured call
+    torch.cuda.synchronize()
+    ref = oa.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ws_call(xa, wa, 2, ws, oa, sa)
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ref)
+    print("[case] eager call of another layout, then replay", flush=True)
+    ws_call(xb, wb, 0, ws, ob, sb)
+    torch.cuda.synchronize()
+    check_oracle(xb_np, wb, 0, ob, sb)
+    g.replay()
+    torch.cuda.synchronize()
+    assert all_nan(oa)
+    assert gla.gtr_gla_workspace_status(ws, nbytes) == gla.ERR_WS_STATE
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ref)
+
+
+MULTI = gla_synth.WORKLOADS["img640"].with_(name="multi", B=2, H=4, grid_h=16, grid_w=17, seed=93)
+
+
+@pytest.mark.parametrize("span,rk,cap", [("1", None, "6"), ("2", "1", "6"), ("2", None, "6"),
+                                         (None, None, "4")],
+                         ids=["one_chunk", "register_kept", "parked", "auto_streamed"])
+def test_multi_launch_loop_parity(span, rk, cap):
+    w = MULTI
+    if span:
+        os.environ["GTR_GLA_SPAN"] = span
+    if rk:
+        os.environ["GTR_GLA_RK"] = rk
+    os.environ["GTR_GLA_MAX_RESIDENT"] = cap
+    kern, sp, grid = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 64, 0)
+    n_spans = -(-(-(-w.L // 64)) // sp)
+    assert kern in (2, 3) and grid < w.B * w.H * n_spans, (kern, sp, grid)
+    arrays = gla_synth.generate(w)
+    x = [dev(a) for a in arrays]
+    for d in range(4):
+        print(f"[case] multi-launch span={span} rk={rk} cap={cap} dir={d}", flush=True)
+        o, s = gla.forward(*x, w.grid_h, w.grid_w, d)
+        torch.cuda.synchronize()
+        check_oracle(arrays, w, d, o, s)
