@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libgtrgla.so")
 
 # status codes (gtr_gla_status)
 OK, ERR_NULL, ERR_SHAPE, ERR_DIR, ERR_CHUNK, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, \
-    ERR_ALIAS, ERR_POLICY, ERR_VALUE, ERR_EXCHANGE, ERR_WS_STATE = range(13)
+    ERR_ALIAS, ERR_POLICY, ERR_VALUE, ERR_EXCHANGE, ERR_WS_STATE, ERR_SCRATCH = range(14)
+NOALLOC_SCRATCH_BYTES = 32 << 20   # GTR_GLA_NOALLOC_SCRATCH_BYTES
 # scan orders (gtr_gla_dir)
 L2R, R2L, T2B, B2T = 0, 1, 2, 3
 DIRS = {"l2r": L2R, "r2l": R2L, "t2b": T2B, "b2t": B2T}
@@ -36,6 +37,7 @@ EXPORTED = (
     "gtr_gla_lowrank_workspace_bytes", "gtr_gla_set_policy", "gtr_gla_get_policy",
     "gtr_gla_plan", "gtr_gla_plan_lowrank", "gtr_gla_status_str", "gtr_sswiglu_fwd",
     "gtr_sswiglu_workspace_bytes", "gtr_gla_workspace_status", "gtr_gla_set_exchange_wait",
+    "gtr_gla_fwd_noalloc",
 )
 
 
@@ -61,6 +63,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gtr_gla_fwd.argtypes = fwd + [P]
     lib.gtr_gla_fwd_f32.argtypes = fwd + [P]
     lib.gtr_gla_fwd_ws.argtypes = fwd + [P, Z, P]
+    lib.gtr_gla_fwd_noalloc.argtypes = fwd + [P]
+    lib.gtr_gla_fwd_noalloc.restype = I
     lib.gtr_gla_fwd_f32_ws.argtypes = fwd + [P, Z, P]
     for f in (lib.gtr_gla_fwd, lib.gtr_gla_fwd_f32, lib.gtr_gla_fwd_ws, lib.gtr_gla_fwd_f32_ws):
         f.restype = I
@@ -154,6 +158,18 @@ def gtr_gla_fwd(q, k, v, log_gamma, B: int, H: int, grid_h: int, grid_w: int, d_
                                    grid_w, d_k, d_v, dir, chunk, _ptr(out), _ptr(final_state),
                                    _stream(stream))
     _raise(r, "gtr_gla_fwd")
+
+
+def gtr_gla_fwd_noalloc(q, k, v, log_gamma, B: int, H: int, grid_h: int, grid_w: int, d_k: int,
+                        d_v: int, dir: int, chunk: int, out, final_state=None,
+                        stream=None) -> None:
+    """gtr_gla_fwd with the library's static per-GPU scratch (allocates nothing)."""
+    import torch
+    _check_all(q, k, v, log_gamma, B, H, grid_h, grid_w, d_k, d_v, out, final_state, torch.float16)
+    r = load_library().gtr_gla_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), B, H,
+                                           grid_h, grid_w, d_k, d_v, dir, chunk, _ptr(out),
+                                           _ptr(final_state), _stream(stream))
+    _raise(r, "gtr_gla_fwd_noalloc")
 
 
 def gtr_gla_fwd_f32(q, k, v, log_gamma, B: int, H: int, grid_h: int, grid_w: int, d_k: int,

@@ -47,6 +47,14 @@ hipError_t init_workspace(void* p, size_t bytes, hipStream_t st);
 // hook that silences span 0 of every sequence; read at each fused launch.
 void set_exchange_wait(unsigned int wait_us, int fault);
 unsigned int exchange_wait_us();
+// The static scratch of gtr_gla_fwd_noalloc on a device, registered at its
+// first use so that gtr_gla_workspace_status(NULL, ...) checks it too.
+void register_scratch(int dev, void* p, size_t bytes);
+// The argument checks of gtr_gla_fwd (sizes, direction, chunk, pointers,
+// aliasing): a gtr_gla_status.
+int validate_fwd_fp16(const void* q, const void* k, const void* v, const void* lg, int B, int H,
+                      int gh, int gw, int dk, int dv, int dir, int chunk, const void* out,
+                      const float* fs);
 // Exchange layout word of a plan (the header's word 2).
 unsigned int fused_layout_word(const FusedPlan& p);
 

@@ -528,11 +528,34 @@ const char* gtr_gla_status_str(int status)
     case GTR_GLA_ERR_VALUE: return "invalid scalar argument (norm_eps must be finite and >= 0, inv_tau finite and > 0, exchange wait 1 us .. 10 s)";
     case GTR_GLA_ERR_EXCHANGE: return "a call's boundary exchange gave up waiting (its outputs are NaN); the workspace was re-initialised";
     case GTR_GLA_ERR_WS_STATE: return "a call found its workspace neither initialised nor of its layout (its outputs are NaN); the workspace was re-initialised";
+    case GTR_GLA_ERR_SCRATCH: return "the call needs more workspace than gtr_gla_fwd_noalloc's static scratch holds (GTR_GLA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }
 
 }  // extern "C"
+
+namespace {
+std::mutex g_scratch_mu;
+std::map<int, std::pair<void*, size_t>> g_scratch;   // device -> gtr_gla_fwd_noalloc scratch
+}  // namespace
+
+namespace gtrgla {
+int validate_fwd_fp16(const void* q, const void* k, const void* v, const void* lg, int B, int H,
+                      int gh, int gw, int dk, int dv, int dir, int chunk, const void* out,
+                      const float* fs)
+{
+    Shape s;
+    const int r = validate_sizes(B, H, gh, gw, dk, dv, dir, chunk, &s);
+    return r != GTR_GLA_OK ? r : validate_pointers(q, k, v, lg, out, fs, s, 2);
+}
+
+void register_scratch(int dev, void* p, size_t bytes)
+{
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    g_scratch[dev] = std::make_pair(p, bytes);
+}
+}  // namespace gtrgla
 
 namespace {
 // Read and clear the error word of one workspace; re-initialise it when set.
@@ -571,6 +594,11 @@ int gtr_gla_workspace_status(void* workspace, size_t workspace_bytes, hipStream_
                 if (kv.first.first.first == dev && kv.first.first.second == (uintptr_t)stream &&
                     kv.second.ptr)
                     mine.emplace_back(kv.second.ptr, kv.second.bytes);
+        }
+        {
+            std::lock_guard<std::mutex> lk(g_scratch_mu);
+            auto it = g_scratch.find(dev);
+            if (it != g_scratch.end()) mine.push_back(it->second);
         }
         for (auto& m : mine) {
             const int r = check_workspace(m.first, m.second, stream, &err);

@@ -72,9 +72,11 @@ typedef enum {
     GTR_GLA_ERR_EXCHANGE = 11,   /* (gtr_gla_workspace_status only) a fused call's
                                     boundary exchange gave up waiting: that call wrote
                                     NaN outputs and final state                      */
-    GTR_GLA_ERR_WS_STATE = 12    /* (gtr_gla_workspace_status only) a fused call found
+    GTR_GLA_ERR_WS_STATE = 12,   /* (gtr_gla_workspace_status only) a fused call found
                                     its workspace neither initialised nor last used by
                                     calls of its layout: it wrote NaN outputs          */
+    GTR_GLA_ERR_SCRATCH = 13     /* gtr_gla_fwd_noalloc: the call needs more workspace
+                                    than its static scratch holds                     */
 } gtr_gla_status;
 
 /* Launch policies (the pages' length-aware scheduling: short sequences take
@@ -203,9 +205,32 @@ int gtr_gla_fwd_f32_ws(const float* q, const float* k, const float* v, const flo
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gtr_gla_fwd_noalloc -- gtr_gla_fwd for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, layouts, semantics and errors as
+ * gtr_gla_fwd; it allocates nothing (no hipMalloc, hipFree or allocating
+ * library call). Its workspace is a static device array of
+ * GTR_GLA_NOALLOC_SCRATCH_BYTES bytes per GPU (held until the process ends),
+ * cleared by a kernel on its first use and whenever the exchange layout
+ * changes. A call whose workspace would be larger returns
+ * GTR_GLA_ERR_SCRATCH and launches nothing (gtr_gla_workspace_bytes of the
+ * call, with is_fp32 = 0, gives the size). Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (different streams, or different
+ * host threads without ordering) race and must not be issued. The first call
+ * on each device looks the array's address up on that device; it may be
+ * captured in a HIP graph once a call of the same shape has run eagerly.
+ * gtr_gla_workspace_status(NULL, 0, stream) also checks this scratch.
+ */
+#define GTR_GLA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int gtr_gla_fwd_noalloc(const void* q, const void* k, const void* v, const void* log_gamma,
+                        int B, int H, int grid_h, int grid_w, int d_k, int d_v, int dir,
+                        int chunk, void* out, float* final_state, hipStream_t stream);
+
+/*
  * gtr_gla_workspace_status -- outside the hot path: waits for `stream`, reads
  * and clears the error word of a workspace (NULL: every workspace the library
- * owns for the current device and this stream), and re-initialises a workspace
+ * owns for the current device and this stream, and the device's
+ * gtr_gla_fwd_noalloc scratch), and re-initialises a workspace
  * whose word was set, so that the next call starts clean. Returns GTR_GLA_OK,
  * GTR_GLA_ERR_EXCHANGE (some fused call on it since the last check gave up in
  * its exchange; that call's outputs are NaN), GTR_GLA_ERR_WS_STATE (some fused

@@ -248,3 +248,18 @@ def test_status_and_exchange_wait_validation(lib):
     for st in (gla.ERR_EXCHANGE, gla.ERR_WS_STATE):
         text = gla.gtr_gla_status_str(st)
         assert text and "unknown" not in text and "NaN" in text
+
+
+def test_noalloc_scratch_limit(lib):
+    """gtr_gla_fwd_noalloc refuses a call whose workspace exceeds its static scratch
+    (before any HIP call), and reports invalid sizes as gtr_gla_fwd does."""
+    need = lib.gtr_gla_workspace_bytes(1, 16, 128, 128, 64, 32, 64, 0)
+    assert need > gla.NOALLOC_SCRATCH_BYTES
+    q, k, v, g, o, fs = PTRS
+    assert lib.gtr_gla_fwd_noalloc(q, k, v, g, 1, 16, 128, 128, 64, 32, 0, 64, o, fs,
+                                   None) == gla.ERR_SCRATCH
+    assert lib.gtr_gla_fwd_noalloc(q, k, v, g, 0, 16, 128, 128, 64, 32, 0, 64, o, fs,
+                                   None) == gla.ERR_SHAPE
+    assert lib.gtr_gla_fwd_noalloc(q, k, v, g, 1, 2, 8, 8, 64, 64, 9, 64, o, fs,
+                                   None) == gla.ERR_DIR
+    assert "scratch" in gla.gtr_gla_status_str(gla.ERR_SCRATCH)
