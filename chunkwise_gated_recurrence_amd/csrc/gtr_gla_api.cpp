@@ -58,9 +58,13 @@ bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
 int validate_sizes(int B, int H, int gh, int gw, int dk, int dv, int dir, int chunk, Shape* s)
 {
     if (B < 1 || H < 1 || gh < 1 || gw < 1 || dk < 1 || dv < 1) return GTR_GLA_ERR_SHAPE;
+    // each product is range-checked before the next one (no signed overflow)
     const long long L = (long long)gh * gw;
-    const long long rows = (long long)B * L * H;
-    if (L >= (1LL << 31) || rows >= (1LL << 31) || rows * (long long)(dk > dv ? dk : dv) >= (1LL << 40))
+    if (L >= (1LL << 31)) return GTR_GLA_ERR_SHAPE;
+    long long rows = (long long)B * L;
+    if (rows >= (1LL << 31)) return GTR_GLA_ERR_SHAPE;
+    rows *= H;
+    if (rows >= (1LL << 31) || rows * (long long)(dk > dv ? dk : dv) >= (1LL << 40))
         return GTR_GLA_ERR_SHAPE;
     if (dir < 0 || dir > 3) return GTR_GLA_ERR_DIR;
     if (!chunk_ok(chunk)) return GTR_GLA_ERR_CHUNK;

@@ -8,11 +8,12 @@
 // over the tokens of the patch grid (the convolution is a per-channel
 // cross-correlation with zero padding and an optional bias). Two kernels:
 //
-//  * up: one workgroup per (8x8 tile of tokens, 64 hidden channels). It forms
-//    X W_v for the tile and its one-token halo (100 tokens, 7 MFMA row blocks)
-//    and X W_g for the tile (4 row blocks) on fp16 MFMA 16x16x32 with fp32
-//    accumulation, the X rows staged in LDS by buffer-to-LDS DMA through a
-//    four-stage ring, then the convolution, the bias and the SiLU gate in fp32
+//  * up: one workgroup per (8x8 tile of tokens, 128 hidden channels, 32 per
+//    wave). It forms X W_v for the tile and its one-token halo (100 tokens, 7
+//    MFMA row blocks) and X W_g for the tile (4 row blocks) on fp16 MFMA
+//    16x16x32 with fp32 accumulation, the X rows and the slice's W_g / W_v
+//    rows staged in LDS by buffer-to-LDS DMA through a three-stage ring
+//    (kUpStages), then the convolution, the bias and the SiLU gate in fp32
 //    from the accumulators (X W_v goes through LDS for the neighbours), and
 //    writes the gated hidden tile A once, in fp16. X W_g and X W_v never go
 //    to memory.
