@@ -51,12 +51,22 @@ _lib = None
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libgtrgla.so (raises if it has not been built)."""
+    """Load libgtrgla.so (raises if it has not been built).
+
+    PyTorch-ROCm ships its own HIP and HSA runtimes (same sonames as ROCm's). The
+    library links libamdhip64.so.7 by soname: loaded after torch it binds to the
+    runtime torch already holds. Loaded first, it would pull in the system's copy
+    and the process would hold two HIP runtimes competing for the GPU (one of
+    them then sees no device). So torch's runtime is loaded first here."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m chunkwise_gated_recurrence_amd.build`")
+    try:
+        import torch  # noqa: F401  (loads torch's HIP runtime before the library binds one)
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     fwd = [P, P, P, P, I, I, I, I, I, I, I, I, P, P]

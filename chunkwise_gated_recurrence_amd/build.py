@@ -24,7 +24,7 @@ CEILING_PATH = os.path.join(PKG, "libgtrgla_ceiling.so")
 ARCH = "gfx950"
 
 SOURCES = ["gla_generic.hip", "gla_fused.hip", "gla_gate.hip", "sswiglu.hip", "gtr_gla_api.cpp",
-           "sswiglu_api.cpp", "gtr_gla_noalloc.hip"]
+           "sswiglu_api.cpp", "gtr_gla_noalloc.hip", "gla_span.hip"]
 
 # Packed fp32 instructions are turned off for every HIP translation unit.
 COMMON_FLAGS = [

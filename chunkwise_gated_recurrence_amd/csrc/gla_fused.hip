@@ -1848,8 +1848,10 @@ hipError_t init_workspace(void* p, size_t bytes, hipStream_t st)
     int blocks = (int)((n16 + 255) / 256);
     if (blocks < 1) blocks = 1;
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(init_ws_kernel, dim3(blocks), dim3(256), 0, st, (unsigned char*)p, bytes);
-    return hipGetLastError();
+    unsigned char* base = (unsigned char*)p;
+    void* args[] = {&base, &bytes};
+    // the launch's own status (not an earlier, unrelated error of the thread)
+    return hipLaunchKernel((const void*)init_ws_kernel, dim3(blocks), dim3(256), args, 0, st);
 }
 
 // Exchange wait limit and the give-up test hook (process-wide).
@@ -1879,8 +1881,20 @@ static unsigned long long wall_ticks_per_ms()
 
 unsigned int fused_layout_word(const FusedPlan& p)
 {
-    // one exchange slot layout per (spans per sequence, sequences per launch)
-    return 0x80000000u | ((unsigned int)p.seq_batch << 8) | (unsigned int)p.n_spans;
+    // one exchange slot layout per (kernel family, state rows, spans per
+    // sequence, sequences per launch)
+    return 0x80000000u | ((unsigned int)(p.family & 3) << 28) | ((p.dk == 32 ? 1u : 0u) << 27) |
+           ((unsigned int)p.seq_batch << 8) | (unsigned int)p.n_spans;
+}
+
+// Workgroups a plan may take as resident at once: 7/8 of the occupancy bound.
+// The dispatcher spreads a launch's workgroups evenly over the shader engines
+// rather than by their free slots, so a grid that needs every slot of the chip
+// can leave workgroups waiting for others to finish; the exchange, which needs
+// every workgroup of a launch running, would then time out.
+long long resident_cap(int per_cu, int cus)
+{
+    return (long long)per_cu * cus * 7 / 8;
 }
 
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st)
@@ -1967,11 +1981,14 @@ static int resident_per_cu(int span, bool keep, bool rk, int var)
         const void* fn = pick_kernel(span, keep, rk, var);
         int n = 0;
         const size_t sh = smem_bytes(rk, var);
-        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh) !=
-                hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, sh) != hipSuccess ||
-            n < 1)
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
+        if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, sh);
+        if (e != hipSuccess) {
+            log_hip("occupancy query of a fused kernel", e);
+            (void)hipGetLastError();   // do not leave it for a later call to report
             n = 1;
+        }
+        if (n < 1) n = 1;
         c = n;
     }
     return c;
@@ -1996,7 +2013,7 @@ FusedPlan fused_plan(const Shape& s, int span_override, int rk_override, int var
     const int nc = s.n_chunks;
     const long long cap_env = resident_cap_from_env();
     auto capacity = [&](int span, bool keep, bool rk) {
-        const long long cap = (long long)resident_per_cu(span, keep, rk, var) * device_cus();
+        const long long cap = resident_cap(resident_per_cu(span, keep, rk, var), device_cus());
         return cap_env > 0 && cap_env < cap ? cap_env : cap;
     };
     auto fill = [&](int span, bool keep, bool rk = false) {
@@ -2071,7 +2088,7 @@ static size_t park_bytes(const FusedPlan& p)
 
 size_t fused_workspace_bytes(const Shape& s, const FusedPlan& p)
 {
-    (void)s;
+    if (p.family == 2) return span_workspace_bytes(s, p);
     const size_t slots = (size_t)p.seq_batch * p.n_spans;
     return 256 + align256(slots * sizeof(unsigned int)) +
            align256((size_t)p.seq_batch * agg_seq_words(p.n_spans) * sizeof(unsigned int) +
@@ -2083,6 +2100,11 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
                         const Shape& s, const Extras& x, const FusedPlan& p, void* out,
                         float* final_state, void* ws, hipStream_t st)
 {
+    if (p.family == 2)
+        return launch_span(q, k, v, lg, s, x, p, out, final_state, ws, st, fused_layout_word(p),
+                           g_fault.load(std::memory_order_relaxed),
+                           (unsigned long long)g_wait_us.load(std::memory_order_relaxed) *
+                               wall_ticks_per_ms() / 1000ull);
     FusedArgs a;
     a.init = x.init;
     a.gate = (const __half*)x.gate;
@@ -2137,7 +2159,7 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const void*
                                              smem_bytes(p.rk, p.var), st);
         if (e != hipSuccess) return e;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace gtrgla

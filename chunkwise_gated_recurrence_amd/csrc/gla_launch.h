@@ -8,6 +8,15 @@
 
 namespace gtrgla {
 
+// GTR_GLA_LOG=1: diagnostics on stderr (gtr_gla_api.cpp). log_hip reports a
+// failed HIP call by name; it prints only when logging is on.
+bool log_enabled();
+void log_hip(const char* where, hipError_t e);
+
+// Workgroups of a launch the planners take as resident at once, given the
+// occupancy bound per CU and the CU count (gla_fused.hip).
+long long resident_cap(int per_cu, int cus);
+
 // Generic three-phase path (gla_generic.hip).
 size_t generic_workspace_bytes(const Shape& s);
 // The generic kernels use the workspace past its header and mark the header
@@ -27,6 +36,8 @@ struct FusedPlan {
     int slice_log2;  // log2 of the state elements each owning workgroup scans
     int var;         // kernel variant: 0 plain, 1 with initial state / output gate,
                      // 2 also with log_gamma computed from the low-rank gate
+    int family = 1;  // 1: the kernels of gla_fused.hip; 2: the span kernels (gla_span.hip)
+    int dk = 64;     // key dim of the exchanged state (span kernels: 32 or 64)
 };
 bool fused_supported(const Shape& s);
 // span_override > 0 forces the span; rk_override > 0 then asks for the
@@ -36,6 +47,17 @@ size_t fused_workspace_bytes(const Shape& s, const FusedPlan& p);
 hipError_t launch_fused(const void* q, const void* k, const void* v, const void* lg,
                         const Shape& s, const Extras& x, const FusedPlan& p, void* out,
                         float* final_state, void* ws, hipStream_t st);
+
+// Span kernels (gla_span.hip): d_v = 64, d_k 32 or 64, C = 64, no low-rank
+// gate, at most 448 chunks per sequence. span_plan returns family 0 when no
+// span plan fits; cap_override > 0 caps the resident workgroups (test hook).
+bool span_supported(const Shape& s);
+FusedPlan span_plan(const Shape& s, int span_override, long long cap_override, int var);
+size_t span_workspace_bytes(const Shape& s, const FusedPlan& p);
+hipError_t launch_span(const void* q, const void* k, const void* v, const void* lg, const Shape& s,
+                       const Extras& x, const FusedPlan& p, void* out, float* final_state,
+                       void* ws, hipStream_t st, unsigned int layout, int fault,
+                       unsigned long long wait_ticks);
 
 // Zero fill by a kernel (graph-capturable); p must be 16-byte aligned.
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);

@@ -18,6 +18,27 @@
 #include <cstdio>
 #include <vector>
 
+namespace gtrgla {
+
+// GTR_GLA_LOG=1: one line per call on stderr with the chosen kernel and launch
+// geometry, and the name of any HIP call that fails.
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char* env = std::getenv("GTR_GLA_LOG");
+        return env && env[0] && env[0] != '0';
+    }();
+    return on;
+}
+
+void log_hip(const char* where, hipError_t e)
+{
+    if (log_enabled() && e != hipSuccess)
+        std::fprintf(stderr, "gtr_gla: %s failed: %s (%d)\n", where, hipGetErrorName(e), (int)e);
+}
+
+}  // namespace gtrgla
+
 namespace {
 
 using gtrgla::Extras;
@@ -49,6 +70,27 @@ int span_override_from_env()
 int rk_override_from_env()
 {
     if (const char* env = std::getenv("GTR_GLA_RK")) return std::atoi(env);
+    return 0;
+}
+
+// GTR_GLA_KERNEL selects the fused kernel family: 1 the kernels of
+// gla_fused.hip, 2 the span kernels (gla_span.hip) for the calls they support
+// (the others keep gla_fused.hip: the low-rank gate, very long sequences);
+// unset, the default family.
+constexpr int kDefaultFamily = 1;
+bool span_kernels_allowed()
+{
+    const char* env = std::getenv("GTR_GLA_KERNEL");
+    const int family = (env && env[0]) ? std::atoi(env) : kDefaultFamily;
+    return family == 2;
+}
+
+long long resident_cap_from_env()
+{
+    if (const char* env = std::getenv("GTR_GLA_MAX_RESIDENT")) {
+        const long long v = std::atoll(env);
+        if (v > 0) return v;
+    }
     return 0;
 }
 
@@ -133,7 +175,7 @@ int validate_extras(const Extras& x, const void* out, const float* fs, const Sha
     return GTR_GLA_OK;
 }
 
-enum Kernel { kGeneric = 1, kFused = 2, kFusedRegisterKept = 3 };
+enum Kernel { kGeneric = 1, kFused = 2, kFusedRegisterKept = 3, kSpan = 4 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -159,7 +201,10 @@ Choice choose(const Shape& s, bool is_fp32, int policy, int var = 0)
     if (fused_ok && policy != GTR_GLA_POLICY_GENERIC) {
         c.kernel = kFused;
         const int span = (policy == GTR_GLA_POLICY_FUSED_ONE) ? 1 : span_override_from_env();
-        c.plan = gtrgla::fused_plan(s, span, rk_override_from_env(), var);
+        c.plan.family = 0;
+        if (!lowrank && gtrgla::span_supported(s) && span_kernels_allowed())
+            c.plan = gtrgla::span_plan(s, span, resident_cap_from_env(), var);
+        if (c.plan.family != 2) c.plan = gtrgla::fused_plan(s, span, rk_override_from_env(), var);
         c.base_bytes = gtrgla::fused_workspace_bytes(s, c.plan);
     } else {
         c.base_bytes = gtrgla::generic_workspace_bytes(s);
@@ -185,21 +230,16 @@ Choice choose(const Shape& s, bool is_fp32, int policy, int var = 0)
 // (the generic kernels, or a fused plan of another layout) invalidates it, and
 // the next fused call zeroes the region first.
 struct WsLayout {
-    int kind;        // 0 clean (zeroed), kGeneric, kFused
-    int n_spans;
-    int seq_batch;
-    bool operator==(const WsLayout& o) const
-    {
-        return kind == o.kind && n_spans == o.n_spans && seq_batch == o.seq_batch;
-    }
+    int kind;            // 0 clean (zeroed), kGeneric, kFused
+    unsigned int word;   // fused: the exchange layout word the kernels check
+                         // (kernel family, key width, sequences per launch, spans)
+    bool operator==(const WsLayout& o) const { return kind == o.kind && word == o.word; }
     bool operator<(const WsLayout& o) const
     {
-        if (kind != o.kind) return kind < o.kind;
-        if (n_spans != o.n_spans) return n_spans < o.n_spans;
-        return seq_batch < o.seq_batch;
+        return kind != o.kind ? kind < o.kind : word < o.word;
     }
 };
-const WsLayout kWsLayoutClean = {0, 0, 0};
+const WsLayout kWsLayoutClean = {0, 0};
 std::mutex g_state_mu;
 std::map<uintptr_t, WsLayout> g_ws_state;
 
@@ -280,15 +320,8 @@ int validate_lowrank(const LowRank& g, const void* out, const float* fs, const S
     return GTR_GLA_OK;
 }
 
-// GTR_GLA_LOG=1: one line per call on stderr with the chosen kernel and launch geometry.
-bool log_enabled()
-{
-    static const bool on = [] {
-        const char* env = std::getenv("GTR_GLA_LOG");
-        return env && env[0] && env[0] != '0';
-    }();
-    return on;
-}
+using gtrgla::log_enabled;
+using gtrgla::log_hip;
 
 void log_call(const Shape& s, bool is_fp32, const Choice& c, int var, bool own_ws)
 {
@@ -301,7 +334,8 @@ void log_call(const Shape& s, bool is_fp32, const Choice& c, int var, bool own_w
                      "launches=%d grid_wg=%d slice_log2=%d workspace=%zu (%s) wait_us=%u\n",
                      s.B, s.H, s.grid_h, s.grid_w, s.L, s.d_k, s.d_v, s.dir, s.chunk,
                      is_fp32 ? "fp32" : "fp16", current_policy(),
-                     p.rk ? "-rk" : (p.keep ? "-keep" : "-streamed"), var, p.span, p.n_spans,
+                     p.family == 2 ? "-span" : p.rk ? "-rk" : (p.keep ? "-keep" : "-streamed"), var,
+                     p.span, p.n_spans,
                      p.seq_batch, (n_seq + p.seq_batch - 1) / p.seq_batch, p.grid, p.slice_log2,
                      c.ws_bytes, own_ws ? "library" : "caller", gtrgla::exchange_wait_us());
     } else {
@@ -335,8 +369,9 @@ int run(const void* q, const void* k, const void* v, const void* lg, int B, int 
     const int var = lr ? 2 : (x0.init || x0.gate) ? 1 : 0;
     const Choice c = choose(s, is_fp32, current_policy(), var);
     if (log_enabled()) log_call(s, is_fp32, c, var, own_ws);
-    const WsLayout layout = c.kernel == kFused ? WsLayout{kFused, c.plan.n_spans, c.plan.seq_batch}
-                                               : WsLayout{kGeneric, 0, 0};
+    const WsLayout layout = c.kernel == kFused
+                                ? WsLayout{kFused, gtrgla::fused_layout_word(c.plan)}
+                                : WsLayout{kGeneric, 0};
     if (own_ws) {
         r = cached_workspace(c.ws_bytes, st, layout, &ws);
         if (r != GTR_GLA_OK) return r;
@@ -359,11 +394,19 @@ int run(const void* q, const void* k, const void* v, const void* lg, int B, int 
             lg = lgw;
         }
     }
+    log_hip("low-rank gate launch", e);
     if (e == hipSuccess && c.kernel == kFused) {
-        if (!workspace_ready_for(ws, layout)) e = gtrgla::init_workspace(ws, c.base_bytes, st);
-        if (e == hipSuccess) e = gtrgla::launch_fused(q, k, v, lg, s, x, c.plan, out, fs, ws, st);
+        if (!workspace_ready_for(ws, layout)) {
+            e = gtrgla::init_workspace(ws, c.base_bytes, st);
+            log_hip("workspace initialisation", e);
+        }
+        if (e == hipSuccess) {
+            e = gtrgla::launch_fused(q, k, v, lg, s, x, c.plan, out, fs, ws, st);
+            log_hip("fused launch", e);
+        }
     } else if (e == hipSuccess) {
         e = gtrgla::launch_generic(q, k, v, lg, is_fp32, s, x, out, fs, ws, st);
+        log_hip("generic launch", e);
     }
     mark_workspace(ws, layout);
     return e == hipSuccess ? GTR_GLA_OK : GTR_GLA_ERR_HIP;
@@ -405,7 +448,9 @@ int gtr_gla_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t 
     if (!workspace) return GTR_GLA_ERR_NULL;
     if (workspace_bytes == 0) return GTR_GLA_ERR_WORKSPACE;
     if (workspace_bytes < (size_t)gtrgla::kWsHeaderBytes) return GTR_GLA_ERR_WORKSPACE;
-    if (gtrgla::init_workspace(workspace, workspace_bytes, stream) != hipSuccess) return GTR_GLA_ERR_HIP;
+    const hipError_t e = gtrgla::init_workspace(workspace, workspace_bytes, stream);
+    log_hip("workspace initialisation", e);
+    if (e != hipSuccess) return GTR_GLA_ERR_HIP;
     mark_workspace(workspace, kWsLayoutClean);
     return GTR_GLA_OK;
 }
@@ -493,7 +538,10 @@ int describe_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int ch
     const int r = validate_sizes(B, H, grid_h, grid_w, d_k, d_v, 0, chunk, &s);
     if (r != GTR_GLA_OK) return r;
     const Choice c = choose(s, is_fp32 != 0, current_policy(), lowrank ? 2 : 0);
-    if (kernel_out) *kernel_out = c.kernel == kFused && c.plan.rk ? kFusedRegisterKept : (int)c.kernel;
+    if (kernel_out)
+        *kernel_out = c.kernel != kFused ? (int)c.kernel
+                      : c.plan.family == 2 ? kSpan
+                      : c.plan.rk ? kFusedRegisterKept : (int)kFused;
     if (span_out) *span_out = c.kernel == kFused ? c.plan.span : 1;
     if (grid_out) *grid_out = c.kernel == kFused ? c.plan.grid : B * H * s.n_chunks;
     return GTR_GLA_OK;

@@ -268,9 +268,12 @@ int gtr_gla_get_policy(void);
 /*
  * gtr_gla_plan -- describes the launch a call with these arguments would make
  * under the current policy, without launching anything. Any output pointer
- * may be NULL. kernel_out: 1 generic, 2 fused, 3 fused with every chunk's
- * outputs kept in registers through the exchange (long sequences). span_out:
- * chunks per workgroup (fused) or 1. grid_out: workgroups of the main kernel.
+ * may be NULL. kernel_out: 1 generic; 2 fused (one-chunk, parked or streamed
+ * spans) and 3 fused with register-kept spans; 4 the span kernels (spans of
+ * 1..7 chunks, outputs kept in registers through the exchange), taken when
+ * the environment variable GTR_GLA_KERNEL is 2 (1 or unset: kernels 2 and 3).
+ * span_out: chunks per workgroup (fused) or 1. grid_out: workgroups of the
+ * main kernel (of one launch, when the sequences need several).
  */
 int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunk,
                  int is_fp32, int* kernel_out, int* span_out, int* grid_out);

@@ -48,6 +48,22 @@ hipError_t launch_fused(const void*, const void*, const void*, const void*, cons
 {
     return hipSuccess;
 }
+// span kernels: shapes they take plan like the other fused kernels here
+bool span_supported(const Shape& s) { return s.d_k == 32 && s.d_v == 64 && s.chunk == 64; }
+FusedPlan span_plan(const Shape& s, int span_override, long long, int var)
+{
+    FusedPlan p = fused_plan(s, span_override, 0, var);
+    p.family = 2;
+    p.dk = s.d_k;
+    return p;
+}
+size_t span_workspace_bytes(const Shape& s, const FusedPlan& p) { return fused_workspace_bytes(s, p); }
+hipError_t launch_span(const void*, const void*, const void*, const void*, const Shape&,
+                       const Extras&, const FusedPlan&, void*, float*, void*, hipStream_t,
+                       unsigned int, int, unsigned long long)
+{
+    return hipSuccess;
+}
 hipError_t fill_zero(void*, size_t, hipStream_t) { return hipSuccess; }
 hipError_t init_workspace(void*, size_t bytes, hipStream_t)
 {
@@ -79,4 +95,5 @@ hipError_t hipMemcpyAsync(void* dst, const void*, size_t n, hipMemcpyKind, hipSt
     return hipSuccess;
 }
 hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
+const char* hipGetErrorName(hipError_t) { return "hipErrorStub"; }
 }

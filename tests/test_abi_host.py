@@ -34,6 +34,21 @@ def test_header_declares_the_api():
     assert set(names) == set(gla.EXPORTED)
 
 
+def test_one_hip_runtime_per_process(lib):
+    """Loaded before anything else touches torch, the binding still leaves one HIP
+    runtime and one HSA runtime in the process (torch's): two would compete for
+    the GPU and one of them would report no device."""
+    import subprocess
+    import sys
+    code = ("import chunkwise_gated_recurrence_amd as g; g.load_library(); import torch; "
+            "print(open('/proc/self/maps').read())")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                         check=True).stdout
+    hip = {l.split()[-1] for l in out.splitlines() if "libamdhip64" in l}
+    hsa = {l.split()[-1] for l in out.splitlines() if "libhsa-runtime64" in l}
+    assert len(hip) == 1 and len(hsa) == 1, (hip, hsa)
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name

@@ -31,8 +31,17 @@ def gpu_ready():
     gla.load_library()
     yield
     gla.gtr_gla_set_policy(gla.POLICY_AUTO)
-    os.environ.pop("GTR_GLA_SPAN", None)
-    os.environ.pop("GTR_GLA_RK", None)
+    for key in ("GTR_GLA_SPAN", "GTR_GLA_RK", "GTR_GLA_KERNEL"):
+        os.environ.pop(key, None)
+
+
+@pytest.fixture
+def old_family():
+    """The kernels of gla_fused.hip (one-chunk, parked, streamed and register-kept
+    spans), selected with GTR_GLA_KERNEL=1 for the duration of a test."""
+    os.environ["GTR_GLA_KERNEL"] = "1"
+    yield
+    os.environ.pop("GTR_GLA_KERNEL", None)
 
 
 def say(*a):
@@ -63,7 +72,8 @@ def ref(w, arrays, d, key=None):
 def check(w, arrays, d, tag, key=None, chunk=None, tol=None):
     say(f"[case] {tag} {w.name} B={w.B} H={w.H} grid={w.grid_h}x{w.grid_w} dk={w.d_k} dv={w.d_v} "
         f"{w.dtype} dir={d} chunk={chunk or w.chunk} policy={gla.gtr_gla_get_policy()} "
-        f"span_env={os.environ.get('GTR_GLA_SPAN')} rk_env={os.environ.get('GTR_GLA_RK')}")
+        f"span_env={os.environ.get('GTR_GLA_SPAN')} rk_env={os.environ.get('GTR_GLA_RK')} "
+        f"kernel_env={os.environ.get('GTR_GLA_KERNEL')}")
     o, s = run_gpu(w, arrays, d, chunk)
     o_ref, s_ref = ref(w, arrays, d, key)
     eo, es = oracle.rel_err(o, o_ref), oracle.rel_err(s, s_ref)
@@ -109,7 +119,7 @@ def test_default_plans(name, plan):
 
 @pytest.mark.parametrize("span", [1, 2, 4, 8])
 @pytest.mark.parametrize("name", ["img1024", "ragged30"])
-def test_fused_spans(name, span):
+def test_fused_spans(name, span, old_family):
     w = gla_synth.WORKLOADS["img1024"]
     if name == "ragged30":
         w = w.with_(name="ragged30", B=2, H=3, grid_h=30, grid_w=30, seed=17)
@@ -128,7 +138,7 @@ def test_fused_spans(name, span):
 
 @pytest.mark.parametrize("span", [2, 3, 5, 7])
 @pytest.mark.parametrize("name", ["img1024", "ragged30"])
-def test_fused_register_kept(name, span):
+def test_fused_register_kept(name, span, old_family):
     """Spans whose every chunk's outputs stay in registers through the exchange
     while the next chunk's g, k, v are staged in LDS (the long-sequence variant);
     ragged30's last span is shorter than the others and its last chunk partial."""
@@ -152,7 +162,7 @@ def test_fused_register_kept(name, span):
 
 @pytest.mark.parametrize("span,rk,kernel", [(1, None, 2), (4, None, 2), (3, None, 2), (3, "1", 3)],
                          ids=["one-chunk", "parked4", "streamed3", "rk3"])
-def test_fused_dk32(span, rk, kernel):
+def test_fused_dk32(span, rk, kernel, old_family):
     """The pages' operator shape (d_k = 32, d_v = 64) on every fused kernel family:
     the key dim is zero-padded to 64 on load, the final state keeps its 32 rows."""
     w = gla_synth.WORKLOADS["img640_dk32"].with_(name="dk32-30x30", B=2, H=2, grid_h=30, grid_w=30,
@@ -171,6 +181,31 @@ def test_fused_dk32(span, rk, kernel):
         os.environ.pop("GTR_GLA_SPAN", None)
         os.environ.pop("GTR_GLA_RK", None)
         gla.gtr_gla_set_policy(gla.POLICY_AUTO)
+
+
+@pytest.mark.parametrize("span", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("dk", [64, 32])
+@pytest.mark.parametrize("name", ["img1024", "ragged30"])
+def test_span_kernels(name, dk, span):
+    """The span kernels (GTR_GLA_KERNEL=2) at every span length, for both key
+    widths they hold natively: every chunk's outputs stay in registers through
+    the exchange while the next chunk's tiles stream into LDS; ragged30's last
+    span is shorter than the others and its last chunk partial."""
+    w = gla_synth.WORKLOADS["img1024"].with_(d_k=dk)
+    if name == "ragged30":
+        w = w.with_(name="ragged30", B=2, H=3, grid_h=30, grid_w=30, seed=17)
+    key = w.name if dk == 64 else f"{w.name}-dk32"   # the dk=64 cases share the oracle runs above
+    arrays = gla_synth.generate(w)
+    os.environ["GTR_GLA_SPAN"] = str(span)
+    os.environ["GTR_GLA_KERNEL"] = "2"
+    try:
+        kern, sp, _ = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, dk, 64, 64, 0)
+        assert (kern, sp) == (4, span)
+        for d in DIRS:
+            check(w, arrays, d, f"span-kernel-span{span}", key=key)
+    finally:
+        os.environ.pop("GTR_GLA_SPAN", None)
+        os.environ.pop("GTR_GLA_KERNEL", None)
 
 
 # --------------------------------------------------------------------------- odd shapes
@@ -225,13 +260,43 @@ def test_decay_extremes(lg_value, policy):
         gla.gtr_gla_set_policy(gla.POLICY_AUTO)
 
 
-def test_mixed_decay_chunks():
-    """Some chunks inside the factorised-score range and some far outside it."""
+@pytest.mark.parametrize("kernel_env,span", [("1", None), ("2", None), ("2", 3), ("2", 7)],
+                         ids=["fused-auto", "span-auto", "span3", "span7"])
+def test_mixed_decay_chunks(kernel_env, span):
+    """Some chunks inside the factorised-score range and some far outside it,
+    on spans of one chunk and of several (where a wide chunk sits between
+    ordinary ones of the same span)."""
     w = BASE16.with_(name="mixed", grid_h=32, grid_w=64, H=2)
     q, k, v, lg = gla_synth.generate(w.with_(seed=61))
     lg = lg.astype(np.float32)
     lg[:, 640:1280] = -0.6          # ~ 55 log2 units per chunk: exact-score path
     lg[:, 1500] = -30.0             # one very small gate
     arrays = (q, k, v, lg.astype(np.float16))
-    for d in DIRS:
-        check(w, arrays, d, "mixed", key="mixed")
+    for key, val in (("GTR_GLA_KERNEL", kernel_env), ("GTR_GLA_SPAN", span)):
+        if val is not None:
+            os.environ[key] = str(val)
+    try:
+        if span is not None:
+            kern, sp, _ = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, 64, 64, 64, 0)
+            assert (kern, sp) == (4, span)
+        for d in DIRS:
+            check(w, arrays, d, "mixed", key="mixed")
+    finally:
+        os.environ.pop("GTR_GLA_KERNEL", None)
+        os.environ.pop("GTR_GLA_SPAN", None)
+
+
+@pytest.mark.parametrize("lg_value", [0.0, -1.0, -1e4])
+def test_span_decay_extremes(lg_value):
+    """The decay extremes on a span of four chunks of the span kernels."""
+    w = BASE16.with_(name=f"decay{lg_value}", grid_h=32, grid_w=40, H=2)
+    arrays = _with_gates(w, lg_value, 51)
+    os.environ["GTR_GLA_SPAN"] = "4"
+    os.environ["GTR_GLA_KERNEL"] = "2"
+    try:
+        assert gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, 64, 64, 64, 0)[:2] == (4, 4)
+        for d in DIRS:
+            check(w, arrays, d, f"span4 lg={lg_value}", key=w.name)
+    finally:
+        os.environ.pop("GTR_GLA_SPAN", None)
+        os.environ.pop("GTR_GLA_KERNEL", None)

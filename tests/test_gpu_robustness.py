@@ -36,7 +36,7 @@ SMALL = gla_synth.WORKLOADS["img640"].with_(name="robust", B=1, H=2, grid_h=24, 
 def clean_state():
     assert torch.cuda.is_available(), "the gpu tests need an MI355X"
     saved = {k: os.environ.pop(k, None) for k in ("GTR_GLA_SPAN", "GTR_GLA_RK",
-                                                  "GTR_GLA_MAX_RESIDENT")}
+                                                  "GTR_GLA_MAX_RESIDENT", "GTR_GLA_KERNEL")}
     gla.gtr_gla_set_policy(gla.POLICY_AUTO)
     gla.gtr_gla_set_exchange_wait(20000, 0)
     yield
@@ -75,17 +75,22 @@ def all_nan(t):
 
 
 GIVE_UP_CASES = {
-    # name: (workload, GTR_GLA_SPAN, GTR_GLA_RK, expected kernel of gtr_gla_plan)
-    "one_chunk": (SMALL, "1", None, 2),
-    "register_kept": (SMALL, "2", "1", 3),
-    "ranged_fold": (SMALL.with_(name="ranged", grid_h=64, grid_w=32), "1", None, 2),
+    # name: (workload, GTR_GLA_SPAN, GTR_GLA_RK, GTR_GLA_KERNEL, expected kernel of gtr_gla_plan)
+    "one_chunk": (SMALL, "1", None, "1", 2),
+    "register_kept": (SMALL, "2", "1", "1", 3),
+    "ranged_fold": (SMALL.with_(name="ranged", grid_h=64, grid_w=32), "1", None, "1", 2),
+    "span_one_chunk": (SMALL, "1", None, "2", 4),
+    "span_three": (SMALL, "3", None, "2", 4),
+    "span_ranged_fold": (SMALL.with_(name="ranged", grid_h=64, grid_w=32), "1", None, "2", 4),
+    "span_dk32": (SMALL.with_(name="dk32", d_k=32), "2", None, "2", 4),
 }
 
 
 @pytest.mark.parametrize("case", sorted(GIVE_UP_CASES))
 def test_exchange_gives_up_loudly_and_recovers(case):
-    w, span, rk, kernel = GIVE_UP_CASES[case]
+    w, span, rk, family, kernel = GIVE_UP_CASES[case]
     os.environ["GTR_GLA_SPAN"] = span
+    os.environ["GTR_GLA_KERNEL"] = family
     if rk:
         os.environ["GTR_GLA_RK"] = rk
     assert gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 64, 0)[0] == kernel
@@ -194,19 +199,22 @@ def test_graph_after_other_layout_on_same_workspace():
 MULTI = gla_synth.WORKLOADS["img640"].with_(name="multi", B=2, H=4, grid_h=16, grid_w=17, seed=93)
 
 
-@pytest.mark.parametrize("span,rk,cap", [("1", None, "6"), ("2", "1", "6"), ("2", None, "6"),
-                                         (None, None, "4")],
-                         ids=["one_chunk", "register_kept", "parked", "auto_streamed"])
-def test_multi_launch_loop_parity(span, rk, cap):
+@pytest.mark.parametrize("span,rk,cap,family", [("1", None, "6", "1"), ("2", "1", "6", "1"),
+                                                ("2", None, "6", "1"), (None, None, "4", "1"),
+                                                ("1", None, "6", "2"), ("3", None, "6", "2")],
+                         ids=["one_chunk", "register_kept", "parked", "auto_streamed", "span1",
+                              "span3"])
+def test_multi_launch_loop_parity(span, rk, cap, family):
     w = MULTI
     if span:
         os.environ["GTR_GLA_SPAN"] = span
     if rk:
         os.environ["GTR_GLA_RK"] = rk
     os.environ["GTR_GLA_MAX_RESIDENT"] = cap
+    os.environ["GTR_GLA_KERNEL"] = family
     kern, sp, grid = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 64, 0)
     n_spans = -(-(-(-w.L // 64)) // sp)
-    assert kern in (2, 3) and grid < w.B * w.H * n_spans, (kern, sp, grid)
+    assert kern in ((2, 3) if family == "1" else (4,)) and grid < w.B * w.H * n_spans, (kern, sp, grid)
     arrays = gla_synth.generate(w)
     x = [dev(a) for a in arrays]
     for d in range(4):
@@ -214,3 +222,26 @@ def test_multi_launch_loop_parity(span, rk, cap):
         o, s = gla.forward(*x, w.grid_h, w.grid_w, d)
         torch.cuda.synchronize()
         check_oracle(arrays, w, d, o, s)
+
+
+def test_library_workspace_alternates_kernel_families():
+    """The library's own workspace, reused by calls of the two fused kernel
+    families whose plans agree on spans per sequence and sequences per launch
+    (a forced cap of six resident workgroups): the exchange layouts still differ,
+    so each call re-initialises the workspace instead of tripping the other
+    family's header (which would give NaN); every call matches the oracle."""
+    w = MULTI
+    arrays = gla_synth.generate(w)
+    x = [dev(a) for a in arrays]
+    os.environ["GTR_GLA_SPAN"] = "1"
+    os.environ["GTR_GLA_MAX_RESIDENT"] = "6"
+    plans = {}
+    for family in ("1", "2", "1", "2"):
+        os.environ["GTR_GLA_KERNEL"] = family
+        plans[family] = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 64, 0)
+        print(f"[case] family {family} plan {plans[family]}", flush=True)
+        o, s = gla.forward(*x, w.grid_h, w.grid_w, 1)
+        torch.cuda.synchronize()
+        check_oracle(arrays, w, 1, o, s)
+        assert gla.gtr_gla_workspace_status() == gla.OK
+    assert plans["1"][1:] == plans["2"][1:] and plans["1"][0] != plans["2"][0]
