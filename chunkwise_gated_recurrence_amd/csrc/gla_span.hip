@@ -115,15 +115,39 @@ typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 tr_h4;
 // (e = 0 .. 3) of column col0 + m of the tile (the hardware gathers the 8-byte
 // pieces that lanes 4e + q of each 16-lane group address: row row0 + 4 kb + e,
 // columns col0 + 4q .. + 3).
+//
+// Addresses of the accesses below split in two: with the row a multiple of 16
+// plus a lane part and the column a multiple of 16 (32 for 8-wide pieces) plus
+// a lane part, the swizzled piece ((col >> 3) ^ row) & (P - 1) is the block's
+// bits (col & (R - 8)) XOR the lane's, so the lane's terms are computed once
+// per chunk and an access adds only its block's (no carries: the block's
+// column bits and the lane's column bits do not overlap).
 template <int R>
 __device__ __forceinline__ h4 tr_read(const _Float16* tile, int row0, int col0, int lane)
 {
-    const int si = lane & 15;
-    const int row = row0 + 4 * (lane >> 4) + (si >> 2);
-    const int col = col0 + 4 * (si & 3);
+    constexpr int P = R / 8;
+    const int rl = 4 * (lane >> 4) + ((lane & 15) >> 2);   // row within the block
+    const int x8 = ((((lane >> 1) & 1) ^ rl) & (P - 1)) << 3;
+    const int off = row0 * R + rl * R + 4 * (lane & 1) + ((col0 & (R - 8)) ^ x8);
     auto p = (__attribute__((address_space(3))) tr_h4*)(
-        (__attribute__((address_space(3))) _Float16*)(tile + sw<R>(row, col)));
+        (__attribute__((address_space(3))) _Float16*)(tile + off));
     return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(p));
+}
+// Row rb + n, columns c + 4g .. + 3 (lane (n, g); rb and c multiples of 16).
+template <int R>
+__device__ __forceinline__ int off4g(int rb, int c, int lane)
+{
+    constexpr int P = R / 8;
+    const int n = lane & 15, g = lane >> 4;
+    return (rb + n) * R + 4 * (g & 1) + ((c & (R - 8)) ^ ((((g >> 1) ^ n) & (P - 1)) << 3));
+}
+// Row rb + n, columns c + 8g .. + 7 (rb a multiple of 16, c of 32).
+template <int R>
+__device__ __forceinline__ int off8g(int rb, int c, int lane)
+{
+    constexpr int P = R / 8;
+    const int n = lane & 15, g = lane >> 4;
+    return (rb + n) * R + ((c & (R - 8)) ^ (((g ^ n) & (P - 1)) << 3));
 }
 // The two transposed reads of one 32-deep contraction step in the permuted
 // order used throughout: lane (m, kb), element e' < 4: row 32 ks + 4 kb + e';
@@ -149,9 +173,24 @@ __device__ __forceinline__ h8 ld8(const _Float16* tile, int row, int col)
     return *reinterpret_cast<const h8*>(tile + sw<R>(row, col));
 }
 template <int R>
-__device__ __forceinline__ void st8(_Float16* tile, int row, int col, h8 x)
+__device__ __forceinline__ h4 ld4g(const _Float16* tile, int rb, int c, int lane)
 {
-    *reinterpret_cast<h8*>(tile + sw<R>(row, col)) = x;
+    return *reinterpret_cast<const h4*>(tile + off4g<R>(rb, c, lane));
+}
+template <int R>
+__device__ __forceinline__ void st4g(_Float16* tile, int rb, int c, int lane, h4 x)
+{
+    *reinterpret_cast<h4*>(tile + off4g<R>(rb, c, lane)) = x;
+}
+template <int R>
+__device__ __forceinline__ h8 ld8g(const _Float16* tile, int rb, int c, int lane)
+{
+    return *reinterpret_cast<const h8*>(tile + off8g<R>(rb, c, lane));
+}
+template <int R>
+__device__ __forceinline__ void st8g(_Float16* tile, int rb, int c, int lane, h8 x)
+{
+    *reinterpret_cast<h8*>(tile + off8g<R>(rb, c, lane)) = x;
 }
 
 // Tagged exchange words: summaries are fp32 rounded to nearest at 16 mantissa
@@ -197,6 +236,7 @@ struct SpanArgs {
     int slice_log2;             // log2 of the state elements each owner folds
     int agg_words;              // summary words per sequence
     float scale;                // d_k^{-1/2}
+    float inv_gh;               // 1 / grid_h
     const float* init;          // [B, H, d_k, 64] state before the first step, or null
     const __half* gate;         // [B, L, H, 64] output gate, or null
     const float* norm_w;        // [64] RMSNorm weight (with gate)
@@ -227,7 +267,7 @@ struct Lds {
     unsigned int tags[kMaxSpans];   // expected tag of every span slot of the sequence
     unsigned int hdr[4];        // the workspace header, staged at the start
     float dd[DK];               // the span's decay per state row, for the publish
-    int stale, dstale, expired, poison, wsbad;
+    int stale, dstale, expired, poison, wsbad, arrived;
 
     static constexpr int kTin = kDV * DK * 2;   // incoming state, fp16 [j][permuted i]
     __device__ unsigned char* region() { return reinterpret_cast<unsigned char*>(&stage[0]); }
@@ -243,13 +283,50 @@ struct Lds {
 // ---------------------------------------------------------------------------
 // loads
 
-// Row (scan step t of sequence (b, h)) byte offset in a [B, L, H, R] fp16
-// tensor, relative to batch b; past the sequence end: `end` (reads zeros).
-__device__ __forceinline__ int row_bytes(const SpanArgs& a, int h, int t, int R, int end)
+// Scan order -> spatial position for the rows of one chunk. The scan orders
+// l2r / r2l walk the grid row-major (forwards / backwards), t2b / b2t
+// column-major. The uniform part (for the column-major orders: the column and
+// row of the chunk's first step) is computed once per chunk; a lane's row then
+// takes a few VALU operations and no integer division: with x the row offset
+// from the chunk start's row, floor((x + 1/2) / grid_h) is exact in fp32, as
+// (x + 1/2) / grid_h stays 1 / (2 grid_h) away from every integer, far more
+// than the rounding error for |x| < grid_h + 64.
+struct RowMap {
+    int t0;       // first scan step of the chunk
+    int c0, r0;   // column-major orders: column and row of t0's scan position
+};
+__device__ __forceinline__ RowMap row_map(const SpanArgs& a, int t0)
 {
-    if (t >= a.L) return end;
-    const int p = scan_to_spatial(t, a.L, a.grid_h, a.grid_w, a.dir);
-    return (p * a.H + h) * (R * 2);
+    RowMap m;
+    m.t0 = t0;
+    m.c0 = m.r0 = 0;
+    if (a.dir >= 2) {   // uniform
+        const int u0 = a.dir == 3 ? a.L - 1 - t0 : t0;
+        m.c0 = u0 / a.grid_h;
+        m.r0 = u0 - m.c0 * a.grid_h;
+    }
+    return m;
+}
+// spatial position of scan step t0 + r (0 <= r < 64), or -1 past the sequence end
+__device__ __forceinline__ int row_pos(const SpanArgs& a, const RowMap& m, int r)
+{
+    const int t = m.t0 + r;
+    int p;
+    if (a.dir >= 2) {
+        const int x = a.dir == 3 ? m.r0 - r : m.r0 + r;
+        const int q = (int)__builtin_floorf(((float)x + 0.5f) * a.inv_gh);
+        p = (x - q * a.grid_h) * a.grid_w + m.c0 + q;
+    } else {
+        p = a.dir == 1 ? a.L - 1 - t : t;
+    }
+    return t < a.L ? p : -1;
+}
+// byte offset of spatial position p of head h in a [B, L, H, R] fp16 tensor,
+// relative to batch b; -1 (past the end): `end` (reads zeros)
+template <int R>
+__device__ __forceinline__ int pos_bytes(const SpanArgs& a, int h, int p, int end)
+{
+    return p < 0 ? end : (p * a.H + h) * (R * 2);
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t batch_rsrc(const __half* base, const SpanArgs& a,
                                                              int b, int R)
@@ -258,13 +335,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t batch_rsrc(const __half* base,
     return rsrc(base + b * per_batch, (int)(per_batch * 2));
 }
 
-// Stage the log gates and v of the chunk starting at scan step t0 into an LDS
-// slot by buffer-to-LDS DMA. A DMA instruction writes 64 consecutive 16-byte
-// pieces; lane l fetches the piece of its row that the row's XOR swizzle puts
-// at LDS position l. Each wave stages rows 16w .. 16w + 15.
+// Stage the chunk's g, v, q and k tiles into an LDS stage by buffer-to-LDS DMA.
+// A DMA instruction writes 64 consecutive 16-byte pieces; lane l fetches the
+// piece of its row that the row's XOR swizzle puts at LDS position l. Each wave
+// stages rows 16w .. 16w + 15: a 64-wide tile in two instructions (rows
+// 16w + 8i + l / 8), a 32-wide one in one (rows 16w + l / 4); the rows'
+// positions are shared by the tiles of one width.
 template <int R>
 __device__ __forceinline__ void dma_tile(const SpanArgs& a, __amdgpu_buffer_rsrc_t rs, _Float16* tile,
-                                         int h, int t0, int w, int lane)
+                                         int h, const int* pos, int w, int lane)
 {
     constexpr int P = R / 8;           // pieces per row
     constexpr int RPI = 64 / P;        // rows per DMA instruction
@@ -273,22 +352,25 @@ __device__ __forceinline__ void dma_tile(const SpanArgs& a, __amdgpu_buffer_rsrc
     for (int i = 0; i < 16 / RPI; ++i) {
         const int row = 16 * w + RPI * i + lane / P;
         const int piece = (lane % P) ^ (row & (P - 1));
-        const int off = row_bytes(a, h, t0 + row, R, end);
+        const int off = pos_bytes<R>(a, h, pos[i], end);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, (__attribute__((address_space(3))) void*)(tile + (16 * w + RPI * i) * R), 16,
             off == end ? end : off + 16 * piece, 0, 0, 0);
     }
 }
 template <class St>
-__device__ __forceinline__ void dma_stage(const SpanArgs& a, St& st, int dk, int b, int h, int t0,
-                                          int w, int lane)
+__device__ __forceinline__ void dma_stage(const SpanArgs& a, St& st, int b, int h, int t0, int w,
+                                          int lane)
 {
     constexpr int DK = sizeof(st.q) / (2 * kC);
-    (void)dk;
-    dma_tile<DK>(a, batch_rsrc(a.lg, a, b, DK), st.g, h, t0, w, lane);
-    dma_tile<kDV>(a, batch_rsrc(a.v, a, b, kDV), st.v, h, t0, w, lane);
-    dma_tile<DK>(a, batch_rsrc(a.q, a, b, DK), st.q, h, t0, w, lane);
-    dma_tile<DK>(a, batch_rsrc(a.k, a, b, DK), st.k, h, t0, w, lane);
+    const RowMap m = row_map(a, t0);
+    const int p64[2] = {row_pos(a, m, 16 * w + (lane >> 3)), row_pos(a, m, 16 * w + 8 + (lane >> 3))};
+    const int p32[1] = {DK == 32 ? row_pos(a, m, 16 * w + (lane >> 2)) : 0};
+    const int* pk = DK == 32 ? p32 : p64;
+    dma_tile<DK>(a, batch_rsrc(a.lg, a, b, DK), st.g, h, pk, w, lane);
+    dma_tile<kDV>(a, batch_rsrc(a.v, a, b, kDV), st.v, h, p64, w, lane);
+    dma_tile<DK>(a, batch_rsrc(a.q, a, b, DK), st.q, h, pk, w, lane);
+    dma_tile<DK>(a, batch_rsrc(a.k, a, b, DK), st.k, h, pk, w, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -386,8 +468,8 @@ __device__ __forceinline__ void chunk_step(St& st, int w, int lane, const f4 (&b
             fq[e] = ex2(__builtin_fmaf(tot[db][e], -be, b2));
             fk[e] = ex2(__builtin_fmaf(tot[db][e], al, -b2));
         }
-        qh[db] = ld4<DK>(st.q, row, 16 * db + 4 * g) * cvt4(fq);
-        kh[db] = ld4<DK>(st.k, row, 16 * db + 4 * g) * cvt4(fk);
+        qh[db] = ld4g<DK>(st.q, 16 * w, 16 * db, lane) * cvt4(fq);
+        kh[db] = ld4g<DK>(st.k, 16 * w, 16 * db, lane) * cvt4(fk);
     }
     h8 qk[NKS];   // the q operand of the scores and of the state term
 #pragma unroll
@@ -424,7 +506,7 @@ __device__ __forceinline__ void chunk_step(St& st, int w, int lane, const f4 (&b
         // underflows towards 0, as the true weight does)
 #pragma unroll 1
         for (int db = 0; db < NDB; ++db) {
-            const f4 qq = up4(ld4<DK>(st.q, row, 16 * db + 4 * g));
+            const f4 qq = up4(ld4g<DK>(st.q, 16 * w, 16 * db, lane));
             f4 E = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
             for (int s = 16 * w + 15; s >= 0; --s) {
@@ -458,9 +540,9 @@ __device__ __forceinline__ void chunk_step(St& st, int w, int lane, const f4 (&b
     // its own raw k rows
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-        st8<DK>(st.q, row, 32 * ks + 8 * g, cat(cvt4(Tp[2 * ks]), cvt4(Tp[2 * ks + 1])));
+        st8g<DK>(st.q, 16 * w, 32 * ks, lane, cat(cvt4(Tp[2 * ks]), cvt4(Tp[2 * ks + 1])));
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) st4<DK>(st.k, row, 16 * db + 4 * g, kh[db]);
+    for (int db = 0; db < NDB; ++db) st4g<DK>(st.k, 16 * w, 16 * db, lane, kh[db]);
     lds_barrier();   // (Y) the k operand tile and the state tile are complete
 
     if (!wide) {
@@ -471,8 +553,8 @@ __device__ __forceinline__ void chunk_step(St& st, int w, int lane, const f4 (&b
             if (sb <= w) {
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
-                    const h8 A = cat(ld4<DK>(st.k, 16 * sb + n, 32 * ks + 4 * g),
-                                     ld4<DK>(st.k, 16 * sb + n, 32 * ks + 16 + 4 * g));
+                    const h8 A = cat(ld4g<DK>(st.k, 16 * sb, 32 * ks, lane),
+                                     ld4g<DK>(st.k, 16 * sb, 32 * ks + 16, lane));
                     sc[sb] = mfma(A, qk[ks], sc[sb]);
                 }
                 if (sb == w) {
@@ -492,7 +574,7 @@ __device__ __forceinline__ void chunk_step(St& st, int w, int lane, const f4 (&b
         f4 O = mfma(tr_step<kDV>(st.v, 0, 16 * jt, lane), bs0, f4{0.f, 0.f, 0.f, 0.f});
         if (w >= 2) O = mfma(tr_step<kDV>(st.v, 1, 16 * jt, lane), bs1, O);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) O = mfma(ld8<DK>(st.q, 16 * jt + n, 32 * ks + 8 * g), qk[ks], O);
+        for (int ks = 0; ks < NKS; ++ks) O = mfma(ld8g<DK>(st.q, 16 * jt, 32 * ks, lane), qk[ks], O);
         kept.o[jt] = cvt4(O);
     }
     // state, the wave's columns: S <- 2^{a' t} (S 2^{a t} + (k operand)^T V)
@@ -551,10 +633,9 @@ __device__ __forceinline__ void store_rows(const SpanArgs& a, int b, int h, int 
                                            f4 (&O)[4], bool poison)
 {
     const int n = lane & 15, g = lane >> 4;
-    const int t = t0 + 16 * w + n;
     const long long per_batch = (long long)a.L * a.H * kDV;
     const int end = (int)(per_batch * 2);
-    const int off = row_bytes(a, h, t, kDV, end);
+    const int off = pos_bytes<kDV>(a, h, row_pos(a, row_map(a, t0), 16 * w + n), end);
     float f = a.scale;
     u2 z[4];
     if (a.gate) {
@@ -696,13 +777,43 @@ __device__ bool exchange(const SpanArgs& a, L& sm, int local_seq, int seq, int j
     constexpr int kSlot = 2 * NE;            // bytes of one incoming-state slot
     const int tid = 64 * w + lane;
     const int n = lane & 15, g = lane >> 4;
+    const int ns = a.n_spans;
+    const int lo = a.slice_log2;            // 2^lo elements per owner
+    const bool owner = j < (NE >> lo);
+    // Arrival: wave 0 of an owner polls the decay words of its slice (a few
+    // words per span, written by each publisher after its state words) until
+    // every span's carry its tag, while the other waves may still be issuing
+    // this workgroup's own publish; the slice's state words are loaded once
+    // they are all likely there. (A word that is still stale then is polled
+    // again below; the tags, not this order, make the result right.)
+    if (owner && w == 0) {
+        const int lrows = lo - 6;
+        const int nd = ns << lrows;
+        const __amdgpu_buffer_rsrc_t rd = rsrc(
+            a.agg + local_seq * (long long)a.agg_words + (long long)j * owner_region_words(ns, lo) +
+                (ns << lo), 4 * nd);
+        const unsigned long long t_start = now_ticks();
+        bool expired = false;
+        for (;;) {
+            asm volatile("" ::: "memory");   // a fresh load every round
+            bool ok = true;
+            for (int k = lane; k < nd; k += 64)
+                ok &= ll_ok(__builtin_amdgcn_raw_buffer_load_b32(rd, 4 * k, 0, kDevScope),
+                            sm.tags[k >> lrows]);
+            if (__all(ok)) break;
+            if (now_ticks() - t_start > a.wait_ticks) {   // wave-uniform
+                expired = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(kPollSleep);
+        }
+        if (lane == 0) sm.arrived = expired ? 0 : 1;
+    }
     if (tid == 0) sm.poison = 0;
     lds_barrier();   // every wave is done with the stages: scratch now
     unsigned char* scr = sm.region();
-    const int ns = a.n_spans;
-    const int lo = a.slice_log2;            // 2^lo elements per owner
     const __amdgpu_buffer_rsrc_t rsl = rsrc(a.sin + seq_slot * kSlot, ns * kSlot);
-    if (j < (NE >> lo)) {
+    if (owner) {
         const int e_first = j << lo;
         const int lrows = lo - 6;
         const int ow = owner_region_words(ns, lo);
@@ -726,24 +837,29 @@ __device__ bool exchange(const SpanArgs& a, L& sm, int local_seq, int seq, int j
         const bool uni = __all(lane >= ns || sm.tags[lane] == tag0);
         float run0 = 0.f;
         const unsigned long long t_start = now_ticks();
-        bool gave_up = false;
-        for (int polls = 0;; ++polls) {
-            for (int k0 = 64 * w; k0 < nl; k0 += 256) {
-                if (k0 + lane < nl)
-                    __builtin_amdgcn_global_load_lds(src + 4 * (k0 + lane), ubuf + 4 * k0, 16, 0,
-                                                     kDevScope);
-            }
-            if (a.init && polls == 0) {
-                const __amdgpu_buffer_rsrc_t ri = rsrc(a.init + (long long)seq * NE, NE * 4);
-                const int nq = (1 << lo) >> 2;
-                for (int k0 = 64 * w; k0 < nq; k0 += 256) {
-                    if (k0 + lane < nq)
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                            ri, (__attribute__((address_space(3))) void*)(s0buf + 4 * k0), 16,
-                            4 * (e_first + 4 * (k0 + lane)), 0, 0, 0);
+        bool gave_up = sm.arrived == 0;
+        // (waves 0-1 load: waves 2-3 may still have this workgroup's publish
+        // stores in flight, which a wait for their loads would include)
+        const bool gave_up_arrival = sm.arrived == 0;
+        for (int polls = 0; !gave_up_arrival; ++polls) {
+            if (w < 2) {
+                for (int k0 = 64 * w; k0 < nl; k0 += 128) {
+                    if (k0 + lane < nl)
+                        __builtin_amdgcn_global_load_lds(src + 4 * (k0 + lane), ubuf + 4 * k0, 16, 0,
+                                                         kDevScope);
                 }
+                if (a.init && polls == 0) {
+                    const __amdgpu_buffer_rsrc_t ri = rsrc(a.init + (long long)seq * NE, NE * 4);
+                    const int nq = (1 << lo) >> 2;
+                    for (int k0 = 64 * w; k0 < nq; k0 += 128) {
+                        if (k0 + lane < nq)
+                            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                                ri, (__attribute__((address_space(3))) void*)(s0buf + 4 * k0), 16,
+                                4 * (e_first + 4 * (k0 + lane)), 0, 0, 0);
+                    }
+                }
+                wait_vm0();
             }
-            wait_vm0();
             if (tid == 0) {
                 sm.stale = 0;
                 sm.dstale = 0;
@@ -899,7 +1015,7 @@ __device__ bool exchange(const SpanArgs& a, L& sm, int local_seq, int seq, int j
             for (int e = 0; e < 4; ++e) bad |= __builtin_isnan((float)x[it][e]);
         if (__any(bad) && lane == 0) sm.poison = 1;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) st8<DK>(sm.tin(), col, 32 * ks + 8 * g, cat(x[2 * ks], x[2 * ks + 1]));
+        for (int ks = 0; ks < NKS; ++ks) st8g<DK>(sm.tin(), 16 * w, 32 * ks, lane, cat(x[2 * ks], x[2 * ks + 1]));
         // Every owner has read this slot's epoch (it wrote S_in after reading
         // the epochs), and so has every wave here: advance it.
         lds_barrier();
@@ -945,7 +1061,7 @@ gla_span_kernel(SpanArgs a_arg)
     const unsigned int ep = __builtin_amdgcn_raw_buffer_load_b32(
         rsrc(a.epoch + seq_slot, 4 * a.n_spans), 4 * tid, 0, kDevScope);
     stage_ws_header(a, sm.hdr, w, lane0);
-    dma_stage(a, sm.stage[0], DK, b, h, c_first * kC, w, lane0);
+    dma_stage(a, sm.stage[0], b, h, c_first * kC, w, lane0);
     if (tid == 0) sm.wsbad = 0;   // ordered by the first chunk's barrier
     ChunkState<DK> cs;
 #pragma unroll
@@ -967,7 +1083,7 @@ gla_span_kernel(SpanArgs a_arg)
         wait_vm0();
         lds_barrier();   // (X) chunk c is staged; chunk c - 1's tiles are free
         if (c + 1 < SPAN)   // wave-uniform
-            dma_stage(a, sm.stage[(c + 1) & (NS - 1)], DK, b, h, (c_first + c + 1) * kC, w, lane);
+            dma_stage(a, sm.stage[(c + 1) & (NS - 1)], b, h, (c_first + c + 1) * kC, w, lane);
         auto& st = sm.stage[c & (NS - 1)];
         f4 bsum[NDB], tot[NDB];
         chunk_gates<DK>(st.g, w, lane, bsum, tot);
@@ -1009,7 +1125,7 @@ gla_span_kernel(SpanArgs a_arg)
                 for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
-                        O[jt] = mfma(ld8<DK>(tin, 16 * jt + n, 32 * ks + 8 * g), kept[c].qs[ks], O[jt]);
+                        O[jt] = mfma(ld8g<DK>(tin, 16 * jt, 32 * ks, lane), kept[c].qs[ks], O[jt]);
             }
             store_rows(a, b, h, (c_first + c) * kC, w, lane, O, poison);
         }
@@ -1187,6 +1303,7 @@ hipError_t launch_span(const void* q, const void* k, const void* v, const void* 
     a.n_spans = p.n_spans;
     a.slice_log2 = p.slice_log2;
     a.scale = s.scale;
+    a.inv_gh = 1.0f / (float)s.grid_h;
     a.init = x.init;
     a.gate = (const __half*)x.gate;
     a.norm_w = x.norm_w;
