@@ -251,10 +251,9 @@ struct SpanArgs {
 // span has two or more chunks). Within a chunk each wave reads only its own
 // rows of q and k, then overwrites them: its rows of the q tile with its
 // columns of the state operand T[j][permuted i], its rows of the k tile with
-// k 2^{r-b}. After the local pass: the U tile of the publish (a free stage, or
-// `extra` for one-chunk spans), the exchange's scratch (everything below the
-// last kTin bytes of the stage region) and the incoming state (those last
-// kTin bytes).
+// k 2^{a t - b}. After the local pass: the exchange's scratch (the fold's
+// range aggregates, at the start of the stage region) and the incoming state
+// (the last kTin bytes).
 template <int DK, int NS>
 struct Lds {
     struct Stage {
@@ -263,21 +262,16 @@ struct Lds {
         _Float16 q[kC * DK];    // q; then T
         _Float16 k[kC * DK];    // k; then k 2^{r-b} (or k 2^{b_last-b})
     } stage[NS];
-    unsigned char extra[NS == 1 ? DK * kDV * 4 : 16];
     unsigned int tags[kMaxSpans];   // expected tag of every span slot of the sequence
     unsigned int hdr[4];        // the workspace header, staged at the start
-    float dd[DK];               // the span's decay per state row, for the publish
-    int stale, dstale, expired, poison, wsbad, arrived;
+    int stale, expired, poison;
 
     static constexpr int kTin = kDV * DK * 2;   // incoming state, fp16 [j][permuted i]
     __device__ unsigned char* region() { return reinterpret_cast<unsigned char*>(&stage[0]); }
-    static constexpr int kRegion = (int)(sizeof(Stage) * NS) + (NS == 1 ? DK * kDV * 4 : 16);
+    static constexpr int kRegion = (int)(sizeof(Stage) * NS);
     __device__ _Float16* tin() { return reinterpret_cast<_Float16*>(region() + kRegion - kTin); }
-    __device__ float* utile(int span)
-    {
-        return NS == 1 ? reinterpret_cast<float*>(extra) : reinterpret_cast<float*>(&stage[span & 1]);
-    }
     static constexpr int kScratch = kRegion - kTin;
+    static_assert(kScratch >= 256 * 4, "the fold's decays fit below the incoming state");
 };
 
 // ---------------------------------------------------------------------------
@@ -694,81 +688,121 @@ __device__ void fail_untrusted(const SpanArgs& a, int b, int h, int seq, int j, 
 }
 
 // ---------------------------------------------------------------------------
-// The exchange.
-//
-// Summary words of one sequence, owner-major: for each owner o (a slice of
-// 2^lo state elements = 2^(lo-6) state rows) a contiguous region of the U
-// words of every span [ns][slice], then the decays of the slice's rows
-// [ns][rows], padded to 16 bytes; an owner reads its whole input as one block.
-__host__ __device__ inline int owner_region_words(int ns, int lo)
+// Value of lane i - N of the same 16-lane row (a lane of the row's first N
+// reads 0).
+template <int N>
+__device__ __forceinline__ float row_shr(float x)
 {
-    return (ns << lo) + (((ns << (lo - 6)) + 3) & ~3);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 0x110 + N, 0xF, 0xF, true));
+}
+// One step of an inclusive scan over groups of P adjacent lanes (P <= 16, a
+// power of two; lane p of its group) of affine maps x -> A x + B, the later
+// lane's map applied after the earlier one's.
+template <int N>
+__device__ __forceinline__ void scan_step(f4& A, f4& B, int p, int P)
+{
+    if (N >= P) return;   // uniform
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float a2 = row_shr<N>(A[q]), b2 = row_shr<N>(B[q]);
+        const bool take = p >= N;
+        B[q] = take ? A[q] * b2 + B[q] : B[q];
+        A[q] = take ? A[q] * a2 : A[q];
+    }
 }
 
-// Publish the span summary U = S (local final state), D = decay of the span,
-// as tagged words. The state goes through an fp32 LDS tile [DK][64] (16-byte
-// pieces swizzled by row) so that waves 2-3 store whole 16-byte pieces
-// (device scope); waves 0-1 keep no stores in flight before their polls.
-template <int DK, class L>
-__device__ __forceinline__ void publish(const SpanArgs& a, L& sm, float* utile,
-                                        const ChunkState<DK>& cs, long long seq_slot, int j,
-                                        unsigned int ep, int w, int lane)
+// The exchange.
+//
+// State elements travel in exchange order: element (i, c) of the DK x 64 state
+// (i: key dim, c: value column) has index ((i >> 2) << 8) + (c << 2) + (i & 3),
+// i.e. row quads, each column's four rows of a quad contiguous. A lane holds
+// rows 4q .. 4q + 3 of one column: one 16-byte piece of the summary, one
+// 8-byte piece of its incoming state. Owner o folds the elements
+// [o 2^lo, (o + 1) 2^lo); its slice covers nr = 2^lr rows (lr = max(2, lo - 6):
+// a slice of at most one quad covers that quad's four rows).
+//
+// Summary words of one sequence, owner-major: owner o's region holds the U
+// words of every span [ns][2^lo], then the decays of its rows [ns][nr], padded
+// to 16 bytes; the last ranks of the fold read nothing else.
+__host__ __device__ inline int slice_rows_log2(int lo) { return lo > 8 ? lo - 6 : 2; }
+__host__ __device__ inline int owner_region_words(int ns, int lo)
+{
+    return (ns << lo) + (((ns << slice_rows_log2(lo)) + 3) & ~3);
+}
+__device__ __forceinline__ int xelem(int i, int c) { return ((i >> 2) << 8) + (c << 2) + (i & 3); }
+
+// The owner's threads: thread t folds piece t >> (8 - lp) of the slice (4
+// elements) over span range t mod P (P = 2^(8 - lp) <= 16 ranges of `per`
+// spans; the ranges of a piece sit in adjacent lanes of one 16-lane row), in
+// n_pass passes when the slice has more than 256 pieces.
+struct FoldMap {
+    int lp, P, per, n_pass;
+};
+__host__ __device__ inline FoldMap fold_map(int ns, int lo)
+{
+    FoldMap f;
+    f.lp = lo - 2 < 8 ? lo - 2 : 8;
+    f.P = 1 << (8 - f.lp);
+    f.per = (ns + f.P - 1) / f.P;
+    f.n_pass = 1 << (lo - 2 - f.lp);
+    return f;
+}
+constexpr int kMaxPer = 8;   // spans per fold range (checked on the host for every plan)
+
+// Publish the span summary U = S (local final state) and D = the span's decay
+// as tagged words, straight from the registers: each lane stores its 16-byte
+// pieces of U; wave 0 stores the decays of its rows to every owner whose slice
+// covers them. Nothing waits for these stores here.
+template <int DK>
+__device__ __forceinline__ void publish(const SpanArgs& a, const ChunkState<DK>& cs,
+                                        long long seq_slot, int j, unsigned int tag, int w, int lane)
 {
     constexpr int NDB = DK / 16;
     const int n = lane & 15, g = lane >> 4;
-    const int tid = 64 * w + lane;
-    wait_vm0();   // wave 0's staged header has landed (and nothing else is in flight)
-#pragma unroll
-    for (int it = 0; it < NDB; ++it)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * it + 4 * g + e, jc = 16 * w + n;
-            utile[i * kDV + ((((jc >> 2) ^ i) & 15) << 2) + (jc & 3)] = cs.S[it][e];
-        }
-    float* dd = sm.dd;
-    if (w == 0 && n == 0) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dd[16 * db + 4 * g + e] = (float)cs.Dp[db][e];
-    }
-    if (tid < kMaxSpans) sm.tags[tid] = (ep + 1u) & 0xFFu;
-    if (w == 0 && lane == 0 && !ws_header_ok(a, sm.hdr)) sm.wsbad = 1;
-    lds_barrier();
-    if (w < 2 || sm.wsbad || (a.fault && j == 0)) return;
-    const unsigned int tag = sm.tags[j];
-    const int ns = a.n_spans, lo = a.slice_log2, lr = lo - 6;
+    const int ns = a.n_spans, lo = a.slice_log2, lr = slice_rows_log2(lo);
     const int ow = owner_region_words(ns, lo);
     const __amdgpu_buffer_rsrc_t rs =
         rsrc(a.agg + (seq_slot / ns) * a.agg_words, a.agg_words * 4);
-    auto row_word = [&](int i) { return (i >> lr) * ow + (j << lo) + ((i & ((1 << lr) - 1)) << 6); };
-    constexpr int kPieces = DK * kDV / 4;
+    const int col = 16 * w + n;
 #pragma unroll
-    for (int k = 0; k < kPieces / 128; ++k) {
-        const int q = tid - 128 + 128 * k;
-        const int row = q >> 4, p = q & 15;
-        const f4 x = *reinterpret_cast<const f4*>(utile + row * kDV + (((p ^ row) & 15) << 2));
+    for (int it = 0; it < NDB; ++it) {
+        const int e = xelem(16 * it + 4 * g, col);
         u4 tw;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tw[e] = ll_word(x[e], tag);
-        __builtin_amdgcn_raw_buffer_store_b128(tw, rs, 4 * (row_word(row) + 4 * p), 0, kDevScope);
+        for (int k = 0; k < 4; ++k) tw[k] = ll_word(cs.S[it][k], tag);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            tw, rs, 4 * ((e >> lo) * ow + (j << lo) + (e & ((1 << lo) - 1))), 0, kDevScope);
     }
-    if (w == 2 && lane < DK) {
-        const int i = lane;
-        __builtin_amdgcn_raw_buffer_store_b32(
-            ll_word(dd[i], tag), rs, 4 * ((i >> lr) * ow + (ns << lo) + (j << lr) + (i & ((1 << lr) - 1))),
-            0, kDevScope);
+    if (w == 0) {
+        // owners per row quad: 2^(8 - lo) (slices within a quad) or one
+        const int nown = lo <= 8 ? 1 << (8 - lo) : 1;
+        if (n < nown) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int i = 16 * db + 4 * g;   // rows i .. i + 3
+                const int o = lo <= 8 ? ((i >> 2) << (8 - lo)) + n : i >> (lo - 6);
+                u4 tw;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) tw[k] = ll_word((float)cs.Dp[db][k], tag);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    tw, rs, 4 * (o * ow + (ns << lo) + (j << lr) + (i & ((1 << lr) - 1))), 0,
+                    kDevScope);
+            }
+        }
     }
 }
 
 // Boundary exchange of span j of sequence local_seq: owners fold their slice of
 // every span's summary and write each span's incoming state; every workgroup
 // then reads its own incoming state into the operand tile sm.tin() ([j][permuted
-// i], fp16) and advances its slot's epoch. Waits are bounded by a.wait_ticks on the
-// 100 MHz wall clock: a wait that passes it gives up (the header's error word
-// records it; an owner hands NaN incoming states, with the expected tags, and
-// a NaN final state to its slice; a reader that gives up or receives NaN
-// poisons its workgroup's outputs). Returns the poison flag.
+// i], fp16) and advances its slot's epoch. An owner's thread polls its own
+// pieces (device scope) and loads again only those still stale; the fold runs
+// on registers. Waits are bounded by a.wait_ticks on the 100 MHz wall clock: a
+// wait that passes it gives up (the header's error word records it; an owner
+// hands NaN incoming states, with the expected tags, and a NaN final state to
+// its slice; a reader that gives up or receives NaN poisons its workgroup's
+// outputs). Returns the poison flag.
 template <int DK, class L>
 __device__ bool exchange(const SpanArgs& a, L& sm, int local_seq, int seq, int j,
                          long long seq_slot, int w, int lane)
@@ -779,200 +813,176 @@ __device__ bool exchange(const SpanArgs& a, L& sm, int local_seq, int seq, int j
     const int n = lane & 15, g = lane >> 4;
     const int ns = a.n_spans;
     const int lo = a.slice_log2;            // 2^lo elements per owner
-    const bool owner = j < (NE >> lo);
-    // Arrival: wave 0 of an owner polls the decay words of its slice (a few
-    // words per span, written by each publisher after its state words) until
-    // every span's carry its tag, while the other waves may still be issuing
-    // this workgroup's own publish; the slice's state words are loaded once
-    // they are all likely there. (A word that is still stale then is polled
-    // again below; the tags, not this order, make the result right.)
-    if (owner && w == 0) {
-        const int lrows = lo - 6;
-        const int nd = ns << lrows;
-        const __amdgpu_buffer_rsrc_t rd = rsrc(
-            a.agg + local_seq * (long long)a.agg_words + (long long)j * owner_region_words(ns, lo) +
-                (ns << lo), 4 * nd);
-        const unsigned long long t_start = now_ticks();
-        bool expired = false;
-        for (;;) {
-            asm volatile("" ::: "memory");   // a fresh load every round
-            bool ok = true;
-            for (int k = lane; k < nd; k += 64)
-                ok &= ll_ok(__builtin_amdgcn_raw_buffer_load_b32(rd, 4 * k, 0, kDevScope),
-                            sm.tags[k >> lrows]);
-            if (__all(ok)) break;
-            if (now_ticks() - t_start > a.wait_ticks) {   // wave-uniform
-                expired = true;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(kPollSleep);
-        }
-        if (lane == 0) sm.arrived = expired ? 0 : 1;
-    }
+    const __amdgpu_buffer_rsrc_t rsl = rsrc(a.sin + seq_slot * kSlot, ns * kSlot);
     if (tid == 0) sm.poison = 0;
     lds_barrier();   // every wave is done with the stages: scratch now
-    unsigned char* scr = sm.region();
-    const __amdgpu_buffer_rsrc_t rsl = rsrc(a.sin + seq_slot * kSlot, ns * kSlot);
-    if (owner) {
-        const int e_first = j << lo;
-        const int lrows = lo - 6;
+    if (j < (NE >> lo)) {
+        const int lr = slice_rows_log2(lo);
         const int ow = owner_region_words(ns, lo);
-        const unsigned int* src = a.agg + local_seq * (long long)a.agg_words + (long long)j * ow;
-        unsigned int* ubuf = reinterpret_cast<unsigned int*>(scr);   // [ns][2^lo] U, [ns][rows] D
-        float* s0buf = reinterpret_cast<float*>(ubuf + ow);         // initial state of the slice
-        float* dfl = s0buf + (1 << lo);                               // decoded decays [ns][rows]
-        float* compA = dfl + ((ns << lrows) + 3) / 4 * 4;              // [256]
-        float* compB = compA + 256;                                   // [256]
-        // (ubuf .. compB end below L::kScratch: checked on the host for every plan)
-        const int nl = ow >> 2;          // 16-byte pieces of the region
-        const int lT = lo < 8 ? 8 - lo : 0, P = 1 << lT;
-        const int per = (ns + P - 1) >> lT;
-        const int lW = lo < 8 ? lo : 8;
-        const int ei = tid & ((1 << lW) - 1), p = tid >> lW;
-        const int m_lo = min(p * per, ns), m_hi = min(m_lo + per, ns);
-        const int n_pass = 1 << (lo - lW);
+        const FoldMap f = fold_map(ns, lo);
+        const int p = tid & (f.P - 1), pc = tid >> (8 - f.lp);
+        const int m_lo = min(p * f.per, ns), m_hi = min(m_lo + f.per, ns);
+        const int cnt = m_hi - m_lo;
+        const __amdgpu_buffer_rsrc_t rr =
+            rsrc(a.agg + local_seq * (long long)a.agg_words + (long long)j * ow, ow * 4);
         const __amdgpu_buffer_rsrc_t rf = final_rsrc<DK>(a, seq);
-        const int nd = ns << lrows;
-        const unsigned int tag0 = sm.tags[0];
-        const bool uni = __all(lane >= ns || sm.tags[lane] == tag0);
-        float run0 = 0.f;
-        const unsigned long long t_start = now_ticks();
-        bool gave_up = sm.arrived == 0;
-        // (waves 0-1 load: waves 2-3 may still have this workgroup's publish
-        // stores in flight, which a wait for their loads would include)
-        const bool gave_up_arrival = sm.arrived == 0;
-        for (int polls = 0; !gave_up_arrival; ++polls) {
-            if (w < 2) {
-                for (int k0 = 64 * w; k0 < nl; k0 += 128) {
-                    if (k0 + lane < nl)
-                        __builtin_amdgcn_global_load_lds(src + 4 * (k0 + lane), ubuf + 4 * k0, 16, 0,
-                                                         kDevScope);
+        float* dl = reinterpret_cast<float*>(sm.region());   // decays [ns][nr] (<= 256)
+        const int nd = ns << lr;
+        for (int ps = 0; ps < f.n_pass; ++ps) {
+            const int el = ((ps << f.lp) + pc) << 2;         // my piece, in the slice
+            const int e = (j << lo) + el;                      // ... in the state
+            const int i0 = (e >> 8) << 2, col = (e >> 2) & 63; // rows i0 .. i0 + 3, column col
+            const int dr = (((e >> 8) - ((j << lo) >> 8)) << 2); // first of my rows, in the slice
+            // Every round loads all of my pieces and (wave 0) all of the slice's
+            // decay words, with no branches between the loads (a load past the
+            // resource reads zero, which no tag accepts; one past my range is
+            // not checked), then checks them.
+            u4 U[kMaxPer];
+            unsigned int tg[kMaxPer];
+#pragma unroll
+            for (int k = 0; k < kMaxPer; ++k) tg[k] = sm.tags[min(m_lo + k, kMaxSpans - 1)];
+            const unsigned long long t_start = now_ticks();
+            bool gave_up = false;
+            for (;;) {
+                asm volatile("" ::: "memory");   // a fresh load every round
+#pragma unroll
+                for (int k = 0; k < kMaxPer; ++k)
+                    U[k] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rr, 4 * (((m_lo + k) << lo) + el), 0, kDevScope));
+                unsigned int wd[4];
+                if (ps == 0 && w == 0) {   // the slice's decays (the same for all its columns)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        wd[x] = __builtin_amdgcn_raw_buffer_load_b32(
+                            rr, 4 * ((ns << lo) + lane + 64 * x), 0, kDevScope);
                 }
-                if (a.init && polls == 0) {
-                    const __amdgpu_buffer_rsrc_t ri = rsrc(a.init + (long long)seq * NE, NE * 4);
-                    const int nq = (1 << lo) >> 2;
-                    for (int k0 = 64 * w; k0 < nq; k0 += 128) {
-                        if (k0 + lane < nq)
-                            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                                ri, (__attribute__((address_space(3))) void*)(s0buf + 4 * k0), 16,
-                                4 * (e_first + 4 * (k0 + lane)), 0, 0, 0);
+                bool mine = true;
+#pragma unroll
+                for (int k = 0; k < kMaxPer; ++k) {
+                    bool ok = true;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) ok = ok && ll_ok(U[k][q], tg[k]);
+                    mine = mine && (k >= cnt || ok);
+                }
+                if (ps == 0 && w == 0) {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int dk = lane + 64 * x;
+                        const bool ok = dk >= nd || ll_ok(wd[x], sm.tags[min(dk >> lr, kMaxSpans - 1)]);
+                        mine = mine && ok;
+                        if (dk < nd) dl[dk] = ll_value(wd[x]);
                     }
                 }
-                wait_vm0();
-            }
-            if (tid == 0) {
-                sm.stale = 0;
-                sm.dstale = 0;
-            }
-            bool ok = true;
-            lds_barrier();
-            if (tid < nd) {
-                const unsigned int x = ubuf[(ns << lo) + tid];
-                if (!ll_ok(x, sm.tags[tid >> lrows])) {
-                    ok = false;
-                    sm.dstale = 1;
+                if (tid == 0) {
+                    sm.stale = 0;
+                    sm.expired = (now_ticks() - t_start) > a.wait_ticks ? 1 : 0;
                 }
-                dfl[tid] = ll_value(x);
+                lds_barrier();
+                if (!__all(mine) && lane == 0) sm.stale = 1;
+                lds_barrier();
+                const bool stale = sm.stale != 0, expired = sm.expired != 0;
+                lds_barrier();   // every thread has read the flags before they are reset
+                if (!stale) break;
+                if (expired) {
+                    gave_up = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(kPollSleep);
             }
-            lds_barrier();
-            if (P == 1) {
-                // one pass from the initial state; span m's incoming state is
-                // stored once the words of spans 0 .. m-1 have passed their checks
-                const bool d_ok = sm.dstale == 0;
-                for (int ps = 0; ps < n_pass; ++ps) {
-                    const int e = (ps << 8) + tid;
-                    float run = a.init ? s0buf[e] : 0.f;
-                    bool mine = d_ok;
-                    const unsigned int* pu = ubuf + e;
-                    const float* pd = dfl + (e >> 6);
-                    int voff = 2 * (e_first + e);
-#pragma unroll 4
-                    for (int m = 0; m < ns; ++m) {
-                        const unsigned int xu = *pu;
-                        const unsigned int tg = uni ? tag0 : sm.tags[m];
-                        const float d = *pd;
-                        if (mine)
-                            __builtin_amdgcn_raw_buffer_store_b16(sin_word(run, tg), rsl, voff, 0,
-                                                                  kDevScope);
-                        mine = mine && ll_ok(xu, tg);
-                        run = d * run + ll_value(xu);
-                        pu += 1 << lo;
-                        pd += 1 << lrows;
-                        voff += kSlot;
+            // (every load of the poll has returned: said explicitly, so that the
+            // stores below are not each made to wait for the ones before them)
+            wait_vm0();
+            // the slice's initial state (rows i0 .. i0 + 3 of column col)
+            f4 s0 = f4{0.f, 0.f, 0.f, 0.f};
+            if (a.init) {
+                const __amdgpu_buffer_rsrc_t ri = rsrc(a.init + (long long)seq * NE, NE * 4);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    s0[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        ri, 4 * ((i0 + q) * kDV + col), 0, 0));
+            }
+            if (gave_up) {
+                if (tid == 0) atomicOr(a.hdr + kWsErrWord, kWsErrExchange);
+                for (int m = m_lo; m < m_hi; ++m) {
+                    // four fp16 NaNs whose lowest bits carry the slot's tag parity
+                    const unsigned int hw = 0x7E007E00u | ((sm.tags[m] & 1u) * 0x00010001u);
+                    const u2 x = {hw, hw};
+                    __builtin_amdgcn_raw_buffer_store_b64(x, rsl, m * kSlot + 2 * e, 0, kDevScope);
+                }
+                if (p == f.P - 1) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        __builtin_amdgcn_raw_buffer_store_b32(0x7FC00000u, rf,
+                                                              4 * ((i0 + q) * kDV + col), 0, 0);
+                }
+                continue;   // (uniform: every thread of the workgroup gives up together)
+            }
+            // my range's decays and tag parities, read from LDS once (both
+            // passes below then run on registers; the decays are fp16 values,
+            // as the spans keep them)
+            h4 Dk[kMaxPer];
+#pragma unroll
+            for (int k = 0; k < kMaxPer; ++k)
+                Dk[k] = cvt4(*reinterpret_cast<const f4*>(dl + ((min(m_lo + k, ns - 1)) << lr) + dr));
+            // fold my range: product of its decays A and its summary from zero B
+            f4 run = f4{0.f, 0.f, 0.f, 0.f};
+            if (f.P > 1) {
+                f4 A = f4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+                for (int k = 0; k < kMaxPer; ++k) {
+                    const bool in = k < cnt;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float d = (float)Dk[k][q];
+                        A[q] = in ? A[q] * d : A[q];
+                        run[q] = in ? d * run[q] + ll_value(U[k][q]) : run[q];
                     }
-                    if (mine)
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(run), rf,
-                                                              4 * (e_first + e), 0, 0);
-                    ok = ok && mine;
+                }
+                // the ranges before mine, from the initial state: an exclusive
+                // scan of the (A, B) pairs over the piece's adjacent lanes
+                // (compose: a later range (A, B) after an earlier (A', B') is
+                // (A A', A B' + B))
+                scan_step<1>(A, run, p, f.P);
+                scan_step<2>(A, run, p, f.P);
+                scan_step<4>(A, run, p, f.P);
+                scan_step<8>(A, run, p, f.P);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // (the shifts run in every lane, before the select: a lane
+                    // reading one masked off would read zero)
+                    const float sa = row_shr<1>(A[q]), sb = row_shr<1>(run[q]);
+                    const float xa = p > 0 ? sa : 1.f;
+                    const float xb = p > 0 ? sb : 0.f;
+                    run[q] = xa * s0[q] + xb;
                 }
             } else {
-                // my range's product of decays and fold from zero
-                float A = 1.f, run = 0.f;
-                const unsigned int* pu = ubuf + (m_lo << lo) + ei;
-                const float* pd = dfl + (m_lo << lrows) + (ei >> 6);
-                for (int m = m_lo; m < m_hi; ++m) {
-                    const unsigned int xu = *pu;
-                    const unsigned int tg = uni ? tag0 : sm.tags[m];
-                    const float d = *pd;
-                    ok &= ll_ok(xu, tg);
-                    A *= d;
-                    run = d * run + ll_value(xu);
-                    pu += 1 << lo;
-                    pd += 1 << lrows;
-                }
-                compA[tid] = A;
-                compB[tid] = run;
-                run0 = a.init ? s0buf[ei] : 0.f;
+                run = s0;
             }
-            if (!__all(ok) && lane == 0) sm.stale = 1;
-            if (tid == 0) sm.expired = (now_ticks() - t_start) > a.wait_ticks ? 1 : 0;
-            lds_barrier();
-            if (!sm.stale) break;
-            if (sm.expired) {
-                gave_up = true;
-                break;
-            }
-            lds_barrier();   // every thread has read the flags before they are reset
-            __builtin_amdgcn_s_sleep(2);
-        }
-        if (gave_up) {
-            if (tid == 0) atomicOr(a.hdr + kWsErrWord, kWsErrExchange);
-            for (int e = tid; e < (1 << lo); e += kThreads) {
-                int voff = 2 * (e_first + e);
-                for (int m = 0; m < ns; ++m, voff += kSlot)
-                    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(0x7E00u | (sm.tags[m] & 1u)),
-                                                          rsl, voff, 0, kDevScope);
-                __builtin_amdgcn_raw_buffer_store_b32(0x7FC00000u, rf, 4 * (e_first + e), 0, 0);
-            }
-        } else if (P > 1) {
-            // the ranges before mine (at most three), from the initial state; then
-            // my range again, storing the incoming states; the last range ends with
-            // the final state
-            float run = run0;
+            // my range again, storing each span's incoming state; the last range
+            // ends with the final state
 #pragma unroll
-            for (int pp = 0; pp < 3; ++pp) {
-                if (pp < p) run = compA[(pp << lW) + ei] * run + compB[(pp << lW) + ei];
+            for (int k = 0; k < kMaxPer; ++k) {
+                if (k < cnt) {
+                    const unsigned int t1 = tg[k] & 1u;
+                    u2 x;
+                    x[0] = (unsigned int)sin_word(run[0], t1) | ((unsigned int)sin_word(run[1], t1) << 16);
+                    x[1] = (unsigned int)sin_word(run[2], t1) | ((unsigned int)sin_word(run[3], t1) << 16);
+                    __builtin_amdgcn_raw_buffer_store_b64(x, rsl, (m_lo + k) * kSlot + 2 * e, 0,
+                                                          kDevScope);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) run[q] = (float)Dk[k][q] * run[q] + ll_value(U[k][q]);
+                }
             }
-            const unsigned int* pu = ubuf + (m_lo << lo) + ei;
-            const float* pd = dfl + (m_lo << lrows) + (ei >> 6);
-            int voff = m_lo * kSlot + 2 * (e_first + ei);
-#pragma unroll 4
-            for (int m = m_lo; m < m_hi; ++m) {
-                const unsigned int xu = *pu;
-                const float d = *pd;
-                const unsigned int tg = uni ? tag0 : sm.tags[m];
-                __builtin_amdgcn_raw_buffer_store_b16(sin_word(run, tg), rsl, voff, 0, kDevScope);
-                run = d * run + ll_value(xu);
-                pu += 1 << lo;
-                pd += 1 << lrows;
-                voff += kSlot;
+            if (p == f.P - 1) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(run[q]), rf,
+                                                          4 * ((i0 + q) * kDV + col), 0, 0);
             }
-            if (p == P - 1)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(run), rf, 4 * (e_first + ei), 0, 0);
         }
     }
 
-    // my incoming state: each wave polls its entries (rows 16 it + 4 g + e,
+    // my incoming state: each wave polls its pieces (rows 16 it + 4 g .. + 3,
     // column 16w + n) until every word carries the slot's tag, then writes them
     // to the operand tile in the permuted order; span 0 reads its zeros like
     // the others so that its epoch, too, advances only once every owner has
@@ -986,20 +996,20 @@ __device__ bool exchange(const SpanArgs& a, L& sm, int local_seq, int seq, int j
         h4 x[NDB];
         for (;;) {
             asm volatile("" ::: "memory");   // a fresh load every round
-            unsigned short u[NDB][4];
+            u2 u[NDB];
 #pragma unroll
             for (int it = 0; it < NDB; ++it)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    u[it][e] = __builtin_amdgcn_raw_buffer_load_b16(
-                        rsl, j * kSlot + 2 * ((16 * it + 4 * g + e) * kDV + col), 0, kDevScope);
+                u[it] = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                   rsl, j * kSlot + 2 * xelem(16 * it + 4 * g, col), 0,
+                                                   kDevScope));
             bool ok = true;
 #pragma unroll
             for (int it = 0; it < NDB; ++it)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ok &= sin_ok(u[it][e], tag);
-                    x[it][e] = sin_value(u[it][e]);
+                for (int q = 0; q < 4; ++q) {
+                    const unsigned short hw = (unsigned short)(u[it][q >> 1] >> (16 * (q & 1)));
+                    ok &= sin_ok(hw, tag);
+                    x[it][q] = sin_value(hw);
                 }
             if (__all(ok)) break;
             if (now_ticks() - t_start > a.wait_ticks) {   // wave-uniform
@@ -1012,10 +1022,11 @@ __device__ bool exchange(const SpanArgs& a, L& sm, int local_seq, int seq, int j
 #pragma unroll
         for (int it = 0; it < NDB; ++it)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bad |= __builtin_isnan((float)x[it][e]);
+            for (int q = 0; q < 4; ++q) bad |= __builtin_isnan((float)x[it][q]);
         if (__any(bad) && lane == 0) sm.poison = 1;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) st8g<DK>(sm.tin(), 16 * w, 32 * ks, lane, cat(x[2 * ks], x[2 * ks + 1]));
+        for (int ks = 0; ks < NKS; ++ks)
+            st8g<DK>(sm.tin(), 16 * w, 32 * ks, lane, cat(x[2 * ks], x[2 * ks + 1]));
         // Every owner has read this slot's epoch (it wrote S_in after reading
         // the epochs), and so has every wave here: advance it.
         lds_barrier();
@@ -1029,12 +1040,10 @@ __device__ bool exchange(const SpanArgs& a, L& sm, int local_seq, int seq, int j
 // ---------------------------------------------------------------------------
 // The kernel. VAR 0: plain; 1: with an initial state and/or the output gate
 // (the plain kernel's copy of the arguments has constant nulls for them).
-// Three workgroups per CU where the registers allow it (168 per lane), else two.
-template <int DK, int SPAN>
-constexpr int kPerCU = (DK == 32 ? SPAN <= 4 : SPAN <= 1) ? 3 : 2;
-
+// Two workgroups per CU (256 registers per lane): the exchange's fold holds a
+// range of summaries in registers next to the kept outputs.
 template <int DK, int SPAN, int VAR>
-__global__ void __launch_bounds__(kThreads, (kPerCU<DK, SPAN>))
+__global__ void __launch_bounds__(kThreads, 2)
 gla_span_kernel(SpanArgs a_arg)
 {
     constexpr int NDB = DK / 16, NKS = DK / 32;
@@ -1062,7 +1071,6 @@ gla_span_kernel(SpanArgs a_arg)
         rsrc(a.epoch + seq_slot, 4 * a.n_spans), 4 * tid, 0, kDevScope);
     stage_ws_header(a, sm.hdr, w, lane0);
     dma_stage(a, sm.stage[0], b, h, c_first * kC, w, lane0);
-    if (tid == 0) sm.wsbad = 0;   // ordered by the first chunk's barrier
     ChunkState<DK> cs;
 #pragma unroll
     for (int it = 0; it < NDB; ++it) {
@@ -1082,6 +1090,8 @@ gla_span_kernel(SpanArgs a_arg)
         asm volatile("" : "+v"(lane));
         wait_vm0();
         lds_barrier();   // (X) chunk c is staged; chunk c - 1's tiles are free
+        if (c == 0 && tid < kMaxSpans)   // seen by every wave after the chunk's next barrier
+            sm.tags[tid] = (ep + 1u) & 0xFFu;
         if (c + 1 < SPAN)   // wave-uniform
             dma_stage(a, sm.stage[(c + 1) & (NS - 1)], b, h, (c_first + c + 1) * kC, w, lane);
         auto& st = sm.stage[c & (NS - 1)];
@@ -1102,12 +1112,14 @@ gla_span_kernel(SpanArgs a_arg)
     const int lane = lane0;
     const int n = lane & 15, g = lane >> 4;
 
-    // ---- 2. publish and exchange
-    publish<DK>(a, sm, sm.utile(SPAN), cs, seq_slot, j, ep, w, lane);
-    if (sm.wsbad) {   // set before the publish's barrier
+    // ---- 2. publish and exchange (the header, staged at the start, has landed:
+    // wave 0 waited for it before the first chunk's barrier; every wave reads
+    // the same words, so the decision is the workgroup's)
+    if (!ws_header_ok(a, sm.hdr)) {
         fail_untrusted<DK>(a, b, h, seq, j, c_first, n_c, w, lane);
         return;
     }
+    if (!(a.fault && j == 0)) publish<DK>(a, cs, seq_slot, j, sm.tags[j], w, lane);
     const bool has_in = j > 0 || a.init != nullptr;
     const bool poison = exchange<DK>(a, sm, local_seq, seq, j, seq_slot, w, lane);
     if (!poison) mark_ws_header(a, sm.hdr, tid);
@@ -1210,14 +1222,14 @@ int span_agg_words(int dk, int n_spans, int lo)
     const int owners = (dk * 64) >> lo;
     return (owners * span::owner_region_words(n_spans, lo) + 63) / 64 * 64;
 }
-// the exchange's LDS scratch holds an owner's region
+// the exchange's fold: at most kMaxPer spans per range of one thread, at most
+// 256 decay words per slice
 bool span_scratch_ok(int dk, int sp, int n_spans, int lo)
 {
-    const size_t scratch = dk == 32 ? (sp > 1 ? span::Lds<32, 2>::kScratch : span::Lds<32, 1>::kScratch)
-                                    : (sp > 1 ? span::Lds<64, 2>::kScratch : span::Lds<64, 1>::kScratch);
-    const size_t need = 4 * ((size_t)span::owner_region_words(n_spans, lo) + (1u << lo) +
-                             (((size_t)n_spans << (lo - 6)) + 3) / 4 * 4 + 512);
-    return need <= scratch;
+    (void)dk;
+    (void)sp;
+    return lo >= 6 && span::fold_map(n_spans, lo).per <= span::kMaxPer &&
+           (n_spans << span::slice_rows_log2(lo)) <= 256;   // the slice's decays, in LDS
 }
 
 }  // namespace

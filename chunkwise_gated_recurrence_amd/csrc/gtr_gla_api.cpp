@@ -75,14 +75,15 @@ int rk_override_from_env()
 
 // GTR_GLA_KERNEL selects the fused kernel family: 1 the kernels of
 // gla_fused.hip, 2 the span kernels (gla_span.hip) for the calls they support
-// (the others keep gla_fused.hip: the low-rank gate, very long sequences);
-// unset, the default family.
-constexpr int kDefaultFamily = 1;
-bool span_kernels_allowed()
+// (the others keep gla_fused.hip: the low-rank gate, very long sequences).
+// Unset: the span kernels for 32-wide keys (which they hold natively, with
+// half the key-side bytes and work of the padded 64-wide tiles), gla_fused.hip
+// for 64-wide ones (measured faster there on most image sizes).
+bool span_kernels_allowed(int d_k)
 {
     const char* env = std::getenv("GTR_GLA_KERNEL");
-    const int family = (env && env[0]) ? std::atoi(env) : kDefaultFamily;
-    return family == 2;
+    if (env && env[0]) return std::atoi(env) == 2;
+    return d_k == 32;
 }
 
 long long resident_cap_from_env()
@@ -202,7 +203,7 @@ Choice choose(const Shape& s, bool is_fp32, int policy, int var = 0)
         c.kernel = kFused;
         const int span = (policy == GTR_GLA_POLICY_FUSED_ONE) ? 1 : span_override_from_env();
         c.plan.family = 0;
-        if (!lowrank && gtrgla::span_supported(s) && span_kernels_allowed())
+        if (!lowrank && gtrgla::span_supported(s) && span_kernels_allowed(s.d_k))
             c.plan = gtrgla::span_plan(s, span, resident_cap_from_env(), var);
         if (c.plan.family != 2) c.plan = gtrgla::fused_plan(s, span, rk_override_from_env(), var);
         c.base_bytes = gtrgla::fused_workspace_bytes(s, c.plan);

@@ -270,8 +270,9 @@ int gtr_gla_get_policy(void);
  * under the current policy, without launching anything. Any output pointer
  * may be NULL. kernel_out: 1 generic; 2 fused (one-chunk, parked or streamed
  * spans) and 3 fused with register-kept spans; 4 the span kernels (spans of
- * 1..7 chunks, outputs kept in registers through the exchange), taken when
- * the environment variable GTR_GLA_KERNEL is 2 (1 or unset: kernels 2 and 3).
+ * 1..7 chunks, outputs kept in registers through the exchange), the default
+ * for d_k = 32 (the environment variable GTR_GLA_KERNEL = 2 takes them for
+ * d_k = 64 too, 1 takes kernels 2 and 3 for both).
  * span_out: chunks per workgroup (fused) or 1. grid_out: workgroups of the
  * main kernel (of one launch, when the sequences need several).
  */
