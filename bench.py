@@ -85,7 +85,7 @@ def mfma_flops(w) -> int:
 
 
 # sources of the fused token-mixer kernels, whose counters profiles/ holds
-FUSED_SOURCES = ("gla_common.h", "gla_fused.hip")
+FUSED_SOURCES = ("gla_common.h", "gla_ws.h", "gla_fused.hip", "gla_span.hip")
 
 
 def kernel_hash() -> str:
@@ -422,8 +422,10 @@ def run_ceiling(w, steps: int, warmup: int):
         for blocks in (512, 1024, 2048, 4096):
             def call(i):
                 a, b, c, d, o = sets[i % nsets]
+                # the stream current at the call: under capture, the capturing one
+                st = torch.cuda.current_stream().cuda_stream
                 r = lib.gtr_stream_ceiling(a.data_ptr(), b.data_ptr(), c.data_ptr(), d.data_ptr(),
-                                           o.data_ptr(), n, blocks, unroll, stream.cuda_stream)
+                                           o.data_ptr(), n, blocks, unroll, st)
                 if r != 0:
                     raise RuntimeError(f"gtr_stream_ceiling failed ({r})")
 
@@ -446,6 +448,9 @@ def run_ceiling(w, steps: int, warmup: int):
             t1.record(stream)
             torch.cuda.synchronize()
             us = 1e3 * t0.elapsed_time(t1) / (reps * nsets)
+            if per_call / (us * 1e-6) / 1e9 > HBM_PEAK_GBS:
+                raise RuntimeError("streaming ceiling above the HBM peak: the timed graph "
+                                   "did not hold its kernels")
             if best is None or us < best[0]:
                 best = (us, {"unroll": unroll, "blocks": blocks})
             del graph
