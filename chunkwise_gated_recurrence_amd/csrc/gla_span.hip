@@ -404,8 +404,8 @@ struct ChunkState {
 // The chunk's gates: inclusive prefix b (b-layout) and total b_last, both as
 // natural logs, from the staged gate tile.
 template <int DK>
-__device__ __forceinline__ void chunk_gates(const _Float16* G, int w, int lane, f4 (&bsum)[DK / 16],
-                                            f4 (&tot)[DK / 16])
+__device__ __forceinline__ void chunk_gates(const _Float16* G, int w, int lane, int lane_tri,
+                                            f4 (&bsum)[DK / 16], f4 (&tot)[DK / 16])
 {
     constexpr int NDB = DK / 16;
     const h8 ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
@@ -417,7 +417,7 @@ __device__ __forceinline__ void chunk_gates(const _Float16* G, int w, int lane, 
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        const h8 tri = tri_operand(w, lane, ks);
+        const h8 tri = tri_operand(w, lane_tri, ks);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             const h8 A = tr_step<DK>(G, ks, 16 * db, lane);   // G^T: dims x tokens
@@ -441,7 +441,7 @@ __device__ __forceinline__ void chunk_gates(const _Float16* G, int w, int lane, 
 // values and the scores are computed exactly in fp32 (q_t k_s 2^{b_t - b_s}
 // summed over the dims), walking the keys down from each token with the
 // running weight.
-template <int DK, class St>
+template <int DK, bool KEEPF, class St>
 __device__ __forceinline__ void chunk_step(St& st, int w, int lane, const f4 (&bsum)[DK / 16],
                                            const f4 (&tot)[DK / 16], bool wide,
                                            ChunkState<DK>& cs, Kept<DK>& kept)
@@ -471,15 +471,17 @@ __device__ __forceinline__ void chunk_step(St& st, int w, int lane, const f4 (&b
     // kept operand of the incoming state: q 2^b D_c; then D_{c+1} = D_c d_c;
     // the state operand of the outputs S 2^{a' t} (written to T once the q rows
     // are free) and the update's first term S 2^{a t}
-    f4 Tp[NDB], Sp[NDB];
+    // (2^{a' t} is 2^{a t} for a factorised chunk, 1 for a wide one)
+    f4 Tp[NDB], Sp[NDB], fbk[NDB];
 #pragma unroll
     for (int it = 0; it < NDB; ++it) {
         f4 fa, fb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             fa[e] = ex2(al * tot[it][e]);
-            fb[e] = ex2(be * tot[it][e]);
+            fb[e] = KEEPF ? (wide ? 1.f : fa[e]) : ex2(be * tot[it][e]);
         }
+        if (KEEPF) fbk[it] = fb;
         const f4 dp = up4(cs.Dp[it]);
         Tp[it] = cs.S[it] * fb;
         Sp[it] = cs.S[it] * fa;
@@ -578,7 +580,8 @@ __device__ __forceinline__ void chunk_step(St& st, int w, int lane, const f4 (&b
         Sp[it] = mfma(tr_step<DK>(st.k, 0, 16 * it, lane), vw0, Sp[it]);
         Sp[it] = mfma(tr_step<DK>(st.k, 1, 16 * it, lane), vw1, Sp[it]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cs.S[it][e] = Sp[it][e] * ex2(be * tot[it][e]);
+        for (int e = 0; e < 4; ++e)
+            cs.S[it][e] = Sp[it][e] * (KEEPF ? fbk[it][e] : ex2(be * tot[it][e]));
     }
 }
 
@@ -1040,6 +1043,11 @@ __device__ bool exchange(const SpanArgs& a, L& sm, int local_seq, int seq, int j
 // ---------------------------------------------------------------------------
 // The kernel. VAR 0: plain; 1: with an initial state and/or the output gate
 // (the plain kernel's copy of the arguments has constant nulls for them).
+// Spans short enough that per-chunk constants of a lane (the prefix operand,
+// the row factor) stay in registers across the chunk instead of being rebuilt.
+template <int DK, int SPAN>
+constexpr bool kHoist = DK == 32 || SPAN <= 4;
+
 // Two workgroups per CU (256 registers per lane): the exchange's fold holds a
 // range of summaries in registers next to the kept outputs.
 template <int DK, int SPAN, int VAR>
@@ -1096,15 +1104,18 @@ gla_span_kernel(SpanArgs a_arg)
             dma_stage(a, sm.stage[(c + 1) & (NS - 1)], b, h, (c_first + c + 1) * kC, w, lane);
         auto& st = sm.stage[c & (NS - 1)];
         f4 bsum[NDB], tot[NDB];
-        chunk_gates<DK>(st.g, w, lane, bsum, tot);
+        // the 0/1 operand of the gate prefix depends on the lane and the wave
+        // only: built once before the loop (from the lane index that is not
+        // recomputed per chunk) where the registers allow, else per chunk
+        chunk_gates<DK>(st.g, w, lane, kHoist<DK, SPAN> ? lane0 : lane, bsum, tot);
         bool wide = false;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wide |= -tot[db][e] * kLog2e > kGuard;
+            for (int e = 0; e < 4; ++e) wide |= tot[db][e] < -kGuard / kLog2e;
         Kept<DK> kc_out;
         // every wave sees the same totals: the decision is the same in every wave
-        chunk_step<DK>(st, w, lane, bsum, tot, __any(wide), cs, kc_out);
+        chunk_step<DK, kHoist<DK, SPAN>>(st, w, lane, bsum, tot, __any(wide), cs, kc_out);
 #pragma unroll
         for (int i = 0; i < SPAN; ++i)
             if (i == c) kept[i] = kc_out;   // c is wave-uniform: a scalar branch
