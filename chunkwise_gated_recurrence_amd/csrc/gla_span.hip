@@ -441,10 +441,11 @@ __device__ __forceinline__ void chunk_gates(const _Float16* G, int w, int lane, 
 // values and the scores are computed exactly in fp32 (q_t k_s 2^{b_t - b_s}
 // summed over the dims), walking the keys down from each token with the
 // running weight.
-template <int DK, bool KEEPF, class St>
+template <int DK, bool KEEPF, bool EARLY, class St, class AfterState>
 __device__ __forceinline__ void chunk_step(St& st, int w, int lane, const f4 (&bsum)[DK / 16],
                                            const f4 (&tot)[DK / 16], bool wide,
-                                           ChunkState<DK>& cs, Kept<DK>& kept)
+                                           ChunkState<DK>& cs, Kept<DK>& kept,
+                                           AfterState after_state)
 {
     constexpr int NDB = DK / 16, NKS = DK / 32;
     const int n = lane & 15, g = lane >> 4;
@@ -541,6 +542,25 @@ __device__ __forceinline__ void chunk_step(St& st, int w, int lane, const f4 (&b
     for (int db = 0; db < NDB; ++db) st4g<DK>(st.k, 16 * w, 16 * db, lane, kh[db]);
     lds_barrier();   // (Y) the k operand tile and the state tile are complete
 
+    // the state update, the wave's columns: S <- 2^{a' t} (S 2^{a t} + (k operand)^T V),
+    // then the hook (the last chunk publishes the span's summary there). EARLY
+    // (one-chunk spans, where the exchange is most of the time): before the
+    // scores and outputs, so that the summary travels while they are computed;
+    // else after them (fewer registers live across the scores).
+    auto state_update = [&]() {
+        const h8 vw0 = tr_step<kDV>(st.v, 0, 16 * w, lane), vw1 = tr_step<kDV>(st.v, 1, 16 * w, lane);
+#pragma unroll
+        for (int it = 0; it < NDB; ++it) {
+            Sp[it] = mfma(tr_step<DK>(st.k, 0, 16 * it, lane), vw0, Sp[it]);
+            Sp[it] = mfma(tr_step<DK>(st.k, 1, 16 * it, lane), vw1, Sp[it]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                cs.S[it][e] = Sp[it][e] * (KEEPF ? fbk[it][e] : ex2(be * tot[it][e]));
+        }
+        after_state(cs);
+    };
+    if (EARLY) state_update();
+
     if (!wide) {
         // scores S^T[s][t] for the s-blocks up to the wave's own (lane (n, g):
         // token 16w + n, keys 16 sb + 4 g + e), the diagonal block masked
@@ -573,16 +593,7 @@ __device__ __forceinline__ void chunk_step(St& st, int w, int lane, const f4 (&b
         for (int ks = 0; ks < NKS; ++ks) O = mfma(ld8g<DK>(st.q, 16 * jt, 32 * ks, lane), qk[ks], O);
         kept.o[jt] = cvt4(O);
     }
-    // state, the wave's columns: S <- 2^{a' t} (S 2^{a t} + (k operand)^T V)
-    const h8 vw0 = tr_step<kDV>(st.v, 0, 16 * w, lane), vw1 = tr_step<kDV>(st.v, 1, 16 * w, lane);
-#pragma unroll
-    for (int it = 0; it < NDB; ++it) {
-        Sp[it] = mfma(tr_step<DK>(st.k, 0, 16 * it, lane), vw0, Sp[it]);
-        Sp[it] = mfma(tr_step<DK>(st.k, 1, 16 * it, lane), vw1, Sp[it]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            cs.S[it][e] = Sp[it][e] * (KEEPF ? fbk[it][e] : ex2(be * tot[it][e]));
-    }
+    if (!EARLY) state_update();
 }
 
 // ---------------------------------------------------------------------------
@@ -1115,7 +1126,17 @@ gla_span_kernel(SpanArgs a_arg)
             for (int e = 0; e < 4; ++e) wide |= tot[db][e] < -kGuard / kLog2e;
         Kept<DK> kc_out;
         // every wave sees the same totals: the decision is the same in every wave
-        chunk_step<DK, kHoist<DK, SPAN>>(st, w, lane, bsum, tot, __any(wide), cs, kc_out);
+        // the last chunk publishes the span's summary as soon as its state
+        // update is done (a workspace the header does not admit gets no
+        // publish; the test hook silences span 0)
+        // (one-chunk spans only; longer ones publish after the loop, which keeps
+        // the publish's registers out of the chunk loop)
+        auto publish_last = [&](const ChunkState<DK>& s_) {
+            if (SPAN == 1 && ws_header_ok(a, sm.hdr) && !(a.fault && j == 0))   // uniform
+                publish<DK>(a, s_, seq_slot, j, sm.tags[j], w, lane);
+        };
+        chunk_step<DK, kHoist<DK, SPAN>, SPAN == 1>(st, w, lane, bsum, tot, __any(wide), cs, kc_out,
+                                                    publish_last);
 #pragma unroll
         for (int i = 0; i < SPAN; ++i)
             if (i == c) kept[i] = kc_out;   // c is wave-uniform: a scalar branch
@@ -1126,11 +1147,11 @@ gla_span_kernel(SpanArgs a_arg)
     // ---- 2. publish and exchange (the header, staged at the start, has landed:
     // wave 0 waited for it before the first chunk's barrier; every wave reads
     // the same words, so the decision is the workgroup's)
-    if (!ws_header_ok(a, sm.hdr)) {
+    if (!ws_header_ok(a, sm.hdr)) {   // (published nothing)
         fail_untrusted<DK>(a, b, h, seq, j, c_first, n_c, w, lane);
         return;
     }
-    if (!(a.fault && j == 0)) publish<DK>(a, cs, seq_slot, j, sm.tags[j], w, lane);
+    if (SPAN > 1 && !(a.fault && j == 0)) publish<DK>(a, cs, seq_slot, j, sm.tags[j], w, lane);
     const bool has_in = j > 0 || a.init != nullptr;
     const bool poison = exchange<DK>(a, sm, local_seq, seq, j, seq_slot, w, lane);
     if (!poison) mark_ws_header(a, sm.hdr, tid);
