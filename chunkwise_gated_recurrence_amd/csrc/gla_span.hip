@@ -15,8 +15,11 @@
 //      outputs plus the contribution of the span-local state, kept on chip
 //      (fp16, registers) with the operand q 2^{b+P} that the incoming state
 //      will multiply; the state in registers.
-//   2. Boundary exchange between the span workgroups of a sequence (owners
-//      fold a slice of every span's summary, write each span's incoming state).
+//   2. Boundary exchange between the span workgroups of a sequence: each span
+//      publishes its summary as tagged words; owners fold a slice of every
+//      span's summary on registers and write each span's incoming state; every
+//      span polls its own (state elements travel in row-quad order, so that
+//      each lane moves whole 16- and 8-byte pieces).
 //   3. Outputs: kept outputs plus (q 2^{b+P}) S_in, stored at the spatial rows.
 //
 // Per chunk, wave w owns tokens 16w .. 16w+15 (scores and outputs) and value
@@ -24,24 +27,25 @@
 // 16x16x32 fp16 -> fp32 throughout. With lane l = (n = l & 15, g = l >> 4):
 //   * "b-layout": lane (n, g) of wave w holds, for token t = 16w + n, the key
 //     dims 16 db + 4 g + e (db = 0 .. d_k/16 - 1, e = 0 .. 3). q and k are
-//     loaded straight into it (8-byte pieces); the log-gate prefix lands in it.
+//     read into it from their staged tiles (8-byte pieces); the log-gate
+//     prefix lands in it.
 //   * The log-gate prefix b_t = sum_{s <= t} log gamma_s is an MFMA of the
 //     staged gate tile (read transposed from LDS) against a 0/1 lower-triangle
 //     operand, and the chunk total against ones, so every wave has every
 //     per-dim quantity of its dims without any exchange between waves.
 //   * Scores use (q 2^{b-r}) (k 2^{r-b})^T with r = b_last / 2 (every factor in
 //     [2^-8, 2^8] while the chunk's log2 decay is at most 16 per dim); a chunk
-//     with a stronger decay runs an exact token-by-token recurrence instead.
-//   * g and v are staged by buffer-to-LDS DMA one chunk ahead; operands that
-//     need a tile transposed (v^T, (k 2^{r-b})^T, the gate tile) are read with
-//     the LDS transpose read (ds_read_b64_tr_b16). 16-byte pieces of every
+//     with a stronger decay takes its scores exactly in fp32 instead (a walk
+//     over the keys with the running decay).
+//   * g, v, q and k are staged by buffer-to-LDS DMA one chunk ahead; operands
+//     that need a tile transposed (v^T, (k 2^{r-b})^T, the gate tile) are read
+//     with the LDS transpose read (ds_read_b64_tr_b16). 16-byte pieces of every
 //     tile row are XOR-swizzled by the row index.
 //   * The contraction index of every product is permuted consistently on both
 //     operands, so that an MFMA result feeds the next MFMA straight from its
 //     accumulator registers (scores into scores x V; the state into q S).
 // Two barriers per chunk: after the staged data has landed (and the previous
 // chunk's tiles are free), and after the k 2^{r-b} and state tiles are written.
-#include <atomic>
 #include <cstdlib>
 
 #include "gla_common.h"
@@ -161,16 +165,6 @@ template <int R>
 __device__ __forceinline__ h4 ld4(const _Float16* tile, int row, int col)
 {
     return *reinterpret_cast<const h4*>(tile + sw<R>(row, col));
-}
-template <int R>
-__device__ __forceinline__ void st4(_Float16* tile, int row, int col, h4 x)
-{
-    *reinterpret_cast<h4*>(tile + sw<R>(row, col)) = x;
-}
-template <int R>
-__device__ __forceinline__ h8 ld8(const _Float16* tile, int row, int col)
-{
-    return *reinterpret_cast<const h8*>(tile + sw<R>(row, col));
 }
 template <int R>
 __device__ __forceinline__ h4 ld4g(const _Float16* tile, int rb, int c, int lane)
@@ -1256,7 +1250,7 @@ int span_agg_words(int dk, int n_spans, int lo)
 }
 // the exchange's fold: at most kMaxPer spans per range of one thread, at most
 // 256 decay words per slice
-bool span_scratch_ok(int dk, int sp, int n_spans, int lo)
+bool span_exchange_ok(int dk, int sp, int n_spans, int lo)
 {
     (void)dk;
     (void)sp;
@@ -1293,7 +1287,7 @@ FusedPlan span_plan(const Shape& s, int span_override, long long cap_override, i
         p.grid = p.seq_batch * p.n_spans;
         p.slice_log2 = span_slice_log2(s.d_k, p.n_spans);
         return (long long)p.n_spans <= cap && p.n_spans <= span::kMaxSpans &&
-               span_scratch_ok(s.d_k, sp, p.n_spans, p.slice_log2);
+               span_exchange_ok(s.d_k, sp, p.n_spans, p.slice_log2);
     };
     if (span_override >= 1 && span_override <= span::kMaxSpan && fill(span_override)) return p;
     // the shortest span whose whole call is resident at once, else the shortest
@@ -1323,7 +1317,7 @@ hipError_t launch_span(const void* q, const void* k, const void* v, const void* 
     if (p.family != 2 || p.span < 1 || p.span > span::kMaxSpan) return hipErrorInvalidValue;
     if (p.var == 0 && (x.init || x.gate)) return hipErrorInvalidValue;
     if (x.z) return hipErrorInvalidValue;   // the low-rank gate runs on the other kernels
-    if (!span_scratch_ok(s.d_k, p.span, p.n_spans, p.slice_log2)) return hipErrorInvalidValue;
+    if (!span_exchange_ok(s.d_k, p.span, p.n_spans, p.slice_log2)) return hipErrorInvalidValue;
     span::SpanArgs a;
     a.q = (const __half*)q;
     a.k = (const __half*)k;
