@@ -33,6 +33,14 @@ COMMON_FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
+# Per-source additions. The Spatial SwiGLU up kernel keeps 22 MFMA accumulators
+# across its K loop; in their accumulation-register form the register allocator
+# rotates them with about 120 accvgpr moves per K step, more vector-ALU issue
+# than the step's MFMA time. The VGPR form keeps each accumulator in place.
+SOURCE_FLAGS = {
+    "sswiglu.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -50,7 +58,7 @@ def build(verbose: bool = False, extra_flags: List[str] | None = None) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmd = [cc, "-c", os.path.join(CSRC, src), "-o", obj] + flags
+        cmd = [cc, "-c", os.path.join(CSRC, src), "-o", obj] + flags + SOURCE_FLAGS.get(src, [])
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -97,7 +97,8 @@ __device__ __forceinline__ void halo_coord(int r, int& hi, int& hj)
     }
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
+// z * sigmoid(z) with the hardware reciprocal (1 ulp; the result is rounded to fp16)
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
 // Workgroup barrier for LDS: this wave's LDS accesses complete, then the
 // barrier, which the compiler may not move memory accesses across. (A fence
@@ -131,8 +132,12 @@ __global__ void __launch_bounds__(256) sswiglu_up_kernel(SsUpArgs p)
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int item = (int)(blockIdx.x & 7) * p.per_xcd + (int)(blockIdx.x >> 3);
-    if (item >= p.items) return;
+    // A padding block (the grid is rounded up to whole XCD shares) works out
+    // item 0's addresses and taps and leaves before its first DMA: the exit
+    // after the argument loads lets them issue together.
+    const int item_id = (int)(blockIdx.x & 7) * p.per_xcd + (int)(blockIdx.x >> 3);
+    const bool live = item_id < p.items;
+    const int item = live ? item_id : 0;
     const int tile = item / p.slices, slice = item - tile * p.slices;
     const int b = tile / p.tiles_img, st = tile - b * p.tiles_img;
     const int ti0 = (st / p.tiles_w) * kTileSide, tj0 = (st % p.tiles_w) * kTileSide;
@@ -195,6 +200,8 @@ __global__ void __launch_bounds__(256) sswiglu_up_kernel(SsUpArgs p)
         for (int t = 0; t < 9; ++t) tap[c][t] = p.cw[(size_t)ch * 9 + t];
         bias[c] = p.cb ? p.cb[ch] : 0.f;
     }
+
+    if (!live) return;
 
     sf4 accv[kRowBlocks][kNB], accg[4][kNB];
 #pragma unroll

@@ -26,6 +26,7 @@ TOL = 5e-3
 # (name, B, grid_h, grid_w, C, Hd, bias)
 CASES = [
     ("img640-L", 1, 40, 40, 384, 1536, True),
+    ("batch2-640", 2, 40, 40, 384, 1536, True),
     ("ragged-S", 2, 30, 34, 192, 768, True),
     ("ratio6-X", 1, 24, 20, 384, 2304, True),
     ("no-bias", 1, 17, 23, 128, 256, False),
