@@ -1423,6 +1423,12 @@ constexpr int kPlain = 0, kExtras = 1, kLowRank = 2;
 template <int VAR>
 __device__ __forceinline__ FusedArgs variant_args(const FusedArgs& in)
 {
+    {
+        // one word of each 64-byte line of the arguments, in one batch: every
+        // later argument load hits the scalar cache
+        const unsigned int* aw = reinterpret_cast<const unsigned int*>(&in);
+        asm volatile("" ::"s"(aw[0]), "s"(aw[16]), "s"(aw[32]), "s"(aw[48]));
+    }
     FusedArgs a = in;
     if (VAR < kLowRank) a.z = nullptr;
     if (VAR < kExtras) {

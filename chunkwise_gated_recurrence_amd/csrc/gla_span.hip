@@ -1061,6 +1061,12 @@ gla_span_kernel(SpanArgs a_arg)
 {
     constexpr int NDB = DK / 16, NKS = DK / 32;
     constexpr int NS = SPAN > 1 ? 2 : 1;
+    {
+        // one word of each 64-byte line of the arguments, in one batch: every
+        // later argument load hits the scalar cache
+        const unsigned int* aw = reinterpret_cast<const unsigned int*>(&a_arg);
+        asm volatile("" ::"s"(aw[0]), "s"(aw[16]), "s"(aw[32]));
+    }
     SpanArgs a = a_arg;
     if (VAR == 0) {
         a.init = nullptr;
