@@ -7,7 +7,8 @@ A step is one pass of the hot path over one batch: the four scan-order calls
 blocks make, each on its own input tensors. Inputs are synthetic
 (gla_synth, seeded) and already resident in HBM when timing starts. They are
 rotated over at least 512 MiB of distinct buffers so that the 256 MB Infinity
-Cache cannot serve them from a previous call. Steps are captured into HIP
+Cache cannot serve them from a previous call (--rotate-mib: less, for counter
+runs, where the profiler serialises every dispatch). Steps are captured into HIP
 graphs and replayed (--no-graph: direct calls).
 
 Prints ONE JSON line. `value` is tokens/s over the timed steps: calls x B x L
@@ -86,15 +87,18 @@ def mfma_flops(w) -> int:
 
 # sources of the fused token-mixer kernels, whose counters profiles/ holds
 FUSED_SOURCES = ("gla_common.h", "gla_ws.h", "gla_fused.hip", "gla_span.hip")
+# sources of the Spatial SwiGLU kernels and of the low-rank gate path (the
+# projection kernel and the fused kernels' low-rank variant)
+MIXER_SOURCES = ("gla_common.h", "gla_ws.h", "gla_fused.hip", "gla_gate.hip", "sswiglu.hip")
 
 
-def kernel_hash() -> str:
-    """Hash of the fused kernels' code: line comments, trailing blanks and
-    empty lines are dropped first, so that a comment edit keeps the counter
-    summaries taken on the same code valid."""
+def kernel_hash(sources=FUSED_SOURCES) -> str:
+    """Hash of the kernels' code (by default the fused token-mixer kernels):
+    line comments, trailing blanks and empty lines are dropped first, so that a
+    comment edit keeps the counter summaries taken on the same code valid."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "chunkwise_gated_recurrence_amd", "csrc")
-    for f in FUSED_SOURCES:
+    for f in sources:
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             lines = (re.sub(r"//.*", "", l).rstrip() for l in fh)
             code = "\n".join(l for l in lines if l)
@@ -315,7 +319,7 @@ def run_workload(w, steps: int, warmup: int, rotate: bool, use_graph: bool = Tru
         "alg_bytes_per_call": per_call,
         "rotating_sets": nsets,
         "graph": use_graph,
-        "kernel": {1: "generic", 2: "fused", 3: "fused-rk"}.get(kern, str(kern)),
+        "kernel": {1: "generic", 2: "fused", 3: "fused-rk", 4: "span"}.get(kern, str(kern)),
         "span": span,
         "grid": grid,
         "per_dir_us": dir_us,
@@ -518,6 +522,7 @@ def cpu_baseline(w, budget_s: float):
 
 
 def main() -> int:
+    global ROTATE_BYTES
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -532,6 +537,10 @@ def main() -> int:
     ap.add_argument("--sswiglu", default="sswiglu640,sswiglu1024",
                     help="Spatial SwiGLU workloads to time as well (comma list, may be empty)")
     ap.add_argument("--warm", action="store_true", help="reuse one input set (cache-warm)")
+    ap.add_argument("--rotate-mib", type=int, default=ROTATE_BYTES >> 20,
+                    help="bytes (MiB) the rotating input sets span; counter runs use less, since a "
+                         "profiler serialises every dispatch")
+    ap.add_argument("--verbose", action="store_true", help="a line on stderr as each workload ends")
     ap.add_argument("--no-graph", action="store_true", help="time direct calls, not graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -539,6 +548,9 @@ def main() -> int:
                     help="only run a plain device copy of COPY_BYTES (for counter calibration)")
     args = ap.parse_args()
 
+    ROTATE_BYTES = args.rotate_mib << 20
+    say = (lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)) if args.verbose else (
+        lambda m: None)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this build runs on "
               "one GPU; the B*H sequences shard across GPUs with no communication, so N GPUs run "
@@ -564,6 +576,7 @@ def main() -> int:
     graph = not args.no_graph
     r = run_workload(w, args.steps, args.warmup, rotate=not args.warm, use_graph=graph,
                      per_dir=True)
+    say(f"{w.name} done")
     achieved = r["alg_bytes_per_call"] / (r["call_us_mean"] * 1e-6) / 1e9
     traffic = measured_traffic(w.name)
     secondary = []
@@ -572,6 +585,7 @@ def main() -> int:
         ws = gla_synth.WORKLOADS[base_name]
         rs = run_workload(ws, max(20, args.steps // 4), args.warmup, rotate=not args.warm,
                           use_graph=graph, per_dir=not any(variant.values()), **variant)
+        say(f"{name} done")
         gbs = rs["alg_bytes_per_call"] / (rs["call_us_mean"] * 1e-6) / 1e9
         ceil_us = run_ceiling(ws, max(20, args.steps // 4), args.warmup)[0] if not any(
             variant.values()) else None
@@ -585,8 +599,10 @@ def main() -> int:
             "call_us_per_dir": rs["per_dir_call_us"], "errors_vs_oracle": rs["errors"],
         })
 
-    mixer = [run_sswiglu(name, max(20, args.steps // 4), args.warmup, rotate=not args.warm)
-             for name in args.sswiglu.split(",") if name]
+    mixer = []
+    for name in [n for n in args.sswiglu.split(",") if n]:
+        mixer.append(run_sswiglu(name, max(20, args.steps // 4), args.warmup, rotate=not args.warm))
+        say(f"{name} done")
 
     ceil_us, ceil_cfg = run_ceiling(w, max(20, args.steps // 4), args.warmup)
     ceiling = {
@@ -610,7 +626,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f16" if w.dtype == "fp16" else "f32",
         "data": (f"synthetic (seeded gla_synth inputs, rotated over {r['rotated_bytes'] / 2**20:.0f} "
-                 f"MiB of HBM buffers, >= 512 MiB)"
+                 f"MiB of HBM buffers, >= {ROTATE_BYTES >> 20} MiB)"
                  if not args.warm else "synthetic (seeded gla_synth inputs, one warm set)"),
         "config": {
             "workload": w.name, "B": w.B, "grid": f"{w.grid_h}x{w.grid_w}", "L": w.L, "H": w.H,
@@ -626,8 +642,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": {"fused": "gla_fused_kernel", "fused-rk": "gla_fused_rk_kernel"}.get(
-                r["kernel"], "generic (3 kernels)"),
+            "kernel": {"fused": "gla_fused_kernel", "fused-rk": "gla_fused_rk_kernel",
+                       "span": "gla_span_kernel"}.get(r["kernel"], "generic (3 kernels)"),
             "alg_bytes_per_launch": r["alg_bytes_per_call"],
             "launch_us_mean": r["call_us_mean"],
             "launch_us_per_dir": r["per_dir_us"],
@@ -639,6 +655,7 @@ def main() -> int:
         "secondary": secondary,
         "spatial_swiglu": mixer,
         "kernel_hash": kernel_hash(),
+        "mixer_kernel_hash": kernel_hash(MIXER_SOURCES),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
