@@ -51,8 +51,12 @@ constexpr int kUpHvBytes = 4 * kHaloTokens * kHvStride * 4;
 constexpr int kUpLds = kUpHvBytes + 64 * kOtStride * 2;   // epilogue
 constexpr int kUpRing = kUpStages * kUpStage;
 constexpr int kUpLdsAll = kUpLds > kUpRing ? kUpLds : kUpRing;   // the epilogue reuses the ring
-constexpr int kDownStage = 2 * 64 * 128;           // A and W_o tiles, 64 features each
-constexpr int kDownLds = kStages * kDownStage;
+// down-kernel ring stage: the A tile (64 rows) and the W_o tile (TN rows), 64
+// features each
+template <int TN>
+constexpr int kDownStage = (64 + TN) * 128;
+template <int TN>
+constexpr int kDownLds = kStages * kDownStage<TN>;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_bytes(const void* p, unsigned bytes)
 {
@@ -311,75 +315,90 @@ struct SsDownArgs {
     int n_tiles, items, per_xcd;
 };
 
-// 64x64 tiles of Y; wave (wm, wn) computes rows 32wm .. +31 and columns
-// 32wn .. +31. A stage holds 64 features of the A rows and of the W_o rows
-// (128 bytes per row; DMA instruction i covers rows 8i .. 8i + 7, lane l row
-// 8i + (l >> 3) into slot l & 7, holding piece (l & 7) ^ ((row >> 1) & 7)).
+// 64 x TN tiles of Y (TN = 64 or 32); wave (wm, wn) computes rows 32wm .. +31
+// and columns (TN / 2) wn .. + TN / 2 - 1. A stage holds 64 features of the
+// A rows and of the W_o rows (128 bytes per row; DMA instruction i covers
+// rows 8i .. 8i + 7, lane l row 8i + (l >> 3) into slot l & 7, holding piece
+// (l & 7) ^ ((row >> 1) & 7)). Narrow tiles double the workgroups of a small
+// product, so that every CU takes part.
+template <int TN>
 __global__ void __launch_bounds__(256) sswiglu_down_kernel(SsDownArgs p)
 {
+    constexpr int NJ = TN / 32;             // 16-column blocks per wave
+    constexpr int NW = TN / 32;             // W_o DMA instructions per wave and stage
+    constexpr int kPer = 2 + NW;            // DMA instructions per wave and stage
+    constexpr int kStage = kDownStage<TN>;
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int item = (int)(blockIdx.x & 7) * p.per_xcd + (int)(blockIdx.x >> 3);
     if (item >= p.items) return;
     const int mt = item / p.n_tiles, nt = item - mt * p.n_tiles;
-    const int m0 = mt * 64, n0 = nt * 64;
+    const int m0 = mt * 64, n0 = nt * TN;
     const unsigned abytes = (unsigned)p.M * (unsigned)p.Hd * 2u;
     const __amdgpu_buffer_rsrc_t ra = rsrc_bytes(p.a, abytes);
     const __amdgpu_buffer_rsrc_t rw = rsrc_bytes(p.wo, (unsigned)p.C * (unsigned)p.Hd * 2u);
-    // wave w issues A instructions 2w, 2w + 1 and W_o instructions 2w, 2w + 1
-    unsigned va[2], vw[2];
+    // wave w issues A instructions 2w, 2w + 1 and W_o instructions NW w .. NW w + NW - 1
+    unsigned va[2], vw[NW];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int row = 8 * (2 * w + j) + (lane >> 3);
         const int piece = (lane & 7) ^ ((row >> 1) & 7);
         va[j] = m0 + row < p.M ? (unsigned)(m0 + row) * (unsigned)p.Hd * 2u + 16u * piece : abytes;
+    }
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+        const int row = 8 * (NW * w + j) + (lane >> 3);
+        const int piece = (lane & 7) ^ ((row >> 1) & 7);
         vw[j] = (unsigned)(n0 + row) * (unsigned)p.Hd * 2u + 16u * piece;
     }
     auto issue = [&](int s) {
-        unsigned char* slot = lds + (s % kStages) * kDownStage;
+        unsigned char* slot = lds + (s % kStages) * kStage;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            dma16(ra, slot + (2 * w + j) * 1024, va[j] + 128u * s);
-            dma16(rw, slot + 8192 + (2 * w + j) * 1024, vw[j] + 128u * s);
-        }
+        for (int j = 0; j < 2; ++j) dma16(ra, slot + (2 * w + j) * 1024, va[j] + 128u * s);
+#pragma unroll
+        for (int j = 0; j < NW; ++j) dma16(rw, slot + 8192 + (NW * w + j) * 1024, vw[j] + 128u * s);
     };
     const int wm = w >> 1, wn = w & 1;
     const int n = lane & 15, kb = lane >> 4;
-    sf4 acc[2][2];
+    sf4 acc[2][NJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = sf4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NJ; ++j) acc[i][j] = sf4{0.f, 0.f, 0.f, 0.f};
     const int nk = p.Hd >> 6;
     for (int s = 0; s < kStages - 1 && s < nk; ++s) issue(s);
     for (int s = 0; s < nk; ++s) {
         const int after = nk - 1 - s;
-        if (after >= kStages - 2) wait_vm<4 * (kStages - 2)>();
-        else if (after == 1) wait_vm<4>();
+        if (after >= kStages - 2) wait_vm<kPer * (kStages - 2)>();
+        else if (after == 1) wait_vm<kPer>();
         else wait_vm<0>();
         lds_sync();
         if (s + kStages - 1 < nk) issue(s + kStages - 1);
-        const unsigned char* slot = lds + (s % kStages) * kDownStage;
+        const unsigned char* slot = lds + (s % kStages) * kStage;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int piece = 4 * ks + kb;
-            sh8 fa[2], fw[2];
+            sh8 fa[2], fw[NJ];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int ra_ = 32 * wm + 16 * i + n, rw_ = 32 * wn + 16 * i + n;
+                const int ra_ = 32 * wm + 16 * i + n;
                 fa[i] = *reinterpret_cast<const sh8*>(slot + ra_ * 128 + 16 * (piece ^ ((ra_ >> 1) & 7)));
-                fw[i] = *reinterpret_cast<const sh8*>(slot + 8192 + rw_ * 128 +
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int rw_ = (TN / 2) * wn + 16 * j + n;
+                fw[j] = *reinterpret_cast<const sh8*>(slot + 8192 + rw_ * 128 +
                                                       16 * (piece ^ ((rw_ >> 1) & 7)));
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < NJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fw[j], acc[i][j], 0, 0, 0);
         }
     }
-    // lane (n, kb) holds Y[row 32wm + 16i + 4kb + e][col 32wn + 16j + n]
+    // lane (n, kb) holds Y[row 32wm + 16i + 4kb + e][col (TN / 2) wn + 16j + n]
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -387,13 +406,27 @@ __global__ void __launch_bounds__(256) sswiglu_down_kernel(SsDownArgs p)
             const int row = m0 + 32 * wm + 16 * i + 4 * kb + e;
             if (row < p.M) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    p.y[(size_t)row * p.C + n0 + 32 * wn + 16 * j + n] = (_Float16)acc[i][j][e];
+                for (int j = 0; j < NJ; ++j)
+                    p.y[(size_t)row * p.C + n0 + (TN / 2) * wn + 16 * j + n] = (_Float16)acc[i][j][e];
             }
         }
 }
 
 static int per_xcd(int items) { return (items + 7) / 8; }
+
+static int cu_count()
+{
+    static int cached = 0;
+    if (cached == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1)
+            cus = 256;
+        cached = cus;
+    }
+    return cached;
+}
 
 hipError_t launch_sswiglu(const void* x, const void* wg, const void* wv, const float* cw,
                           const float* cb, const void* wo, int B, int gh, int gw, int C, int Hd,
@@ -403,8 +436,10 @@ hipError_t launch_sswiglu(const void* x, const void* wg, const void* wv, const f
     if (!attrs) {
         if (hipFuncSetAttribute((const void*)sswiglu_up_kernel,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kUpLdsAll) != hipSuccess ||
-            hipFuncSetAttribute((const void*)sswiglu_down_kernel,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kDownLds) != hipSuccess)
+            hipFuncSetAttribute((const void*)sswiglu_down_kernel<64>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kDownLds<64>) != hipSuccess ||
+            hipFuncSetAttribute((const void*)sswiglu_down_kernel<32>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kDownLds<32>) != hipSuccess)
             return hipGetLastError();
         attrs = true;
     }
@@ -434,10 +469,15 @@ hipError_t launch_sswiglu(const void* x, const void* wg, const void* wv, const f
     d.M = B * gh * gw;
     d.Hd = Hd;
     d.C = C;
-    d.n_tiles = C / 64;
+    // 64-column tiles; 32-column ones when the 64-column tiles would leave CUs idle
+    const bool narrow = ((d.M + 63) / 64) * (C / 64) < cu_count();
+    d.n_tiles = narrow ? C / 32 : C / 64;
     d.items = ((d.M + 63) / 64) * d.n_tiles;
     d.per_xcd = per_xcd(d.items);
-    hipLaunchKernelGGL(sswiglu_down_kernel, dim3(8 * d.per_xcd), dim3(256), kDownLds, st, d);
+    if (narrow)
+        hipLaunchKernelGGL(sswiglu_down_kernel<32>, dim3(8 * d.per_xcd), dim3(256), kDownLds<32>, st, d);
+    else
+        hipLaunchKernelGGL(sswiglu_down_kernel<64>, dim3(8 * d.per_xcd), dim3(256), kDownLds<64>, st, d);
     return hipGetLastError();
 }
 
