@@ -17,8 +17,9 @@
 //    from the accumulators (X W_v goes through LDS for the neighbours), and
 //    writes the gated hidden tile A once, in fp16. X W_g and X W_v never go
 //    to memory.
-//  * down: Y = A W_o as a plain tiled MFMA product, 64x64 output tiles, A and
-//    W_o staged by DMA through a four-stage ring.
+//  * down: Y = A W_o as a plain tiled MFMA product, 64x64 output tiles (64x32
+//    when the 64x64 tiles would not cover the CUs), A and W_o staged by DMA
+//    through a four-stage ring.
 //
 // Weights are linear-layer weights [out, in] (fp16): W_g, W_v [Hd, C],
 // W_o [C, Hd]; every operand row is contiguous along the reduced dimension,

@@ -1,6 +1,7 @@
 """Host-side checks of bench.py's bookkeeping (no GPU): the fused-kernel code
 hash that keys the committed traffic summaries ignores comments and blank
-lines but not code, and a summary is used only while its hash matches."""
+lines but not code, a summary is used only while its hash matches, and the
+Spatial SwiGLU / low-rank summary's hash covers those kernels' sources."""
 import os
 import shutil
 
@@ -61,3 +62,14 @@ def test_host_cpu_fields():
     h = bench.host_cpu()
     assert h["nproc"] >= 1 and 1 <= h["affinity"] <= h["nproc"]
     assert h["cpu_model"] is None or isinstance(h["cpu_model"], str)
+
+
+def test_mixer_hash_covers_the_mixer_sources():
+    src = os.path.join(bench.ROOT, "chunkwise_gated_recurrence_amd", "csrc")
+    for f in bench.MIXER_SOURCES:
+        assert os.path.exists(os.path.join(src, f)), f
+    assert "sswiglu.hip" in bench.MIXER_SOURCES and "gla_gate.hip" in bench.MIXER_SOURCES
+    assert bench.kernel_hash(bench.MIXER_SOURCES) != bench.kernel_hash()
+    # the committed summary names the hash it was taken at
+    with open(os.path.join(bench.ROOT, "profiles", "mixer_and_lowrank_kernels.txt")) as fh:
+        assert "kernel_hash(MIXER_SOURCES)" in fh.read()
