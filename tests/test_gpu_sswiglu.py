@@ -2,7 +2,10 @@
 oracle (oracle/sswiglu.py; GTR summary page, section 前置知识 › SwiGLU前馈块),
 on the pages' model widths (C = 192 / 384 with Hd = 4 C, and Hd = 6 C), ragged
 grids whose 8x8 tiles and 64-token output tiles are partial, degenerate grids,
-batches, and without the convolution bias.
+batches, and without the convolution bias. The down projection uses 64x64
+output tiles when they number at least the CU count and 64x32 tiles below
+that: batch2-640 (300 tiles of 64x64) takes the first, the other cases the
+second.
 
 Bar: max|gpu - oracle| / max|oracle| <= 5e-3 over y (fp16 operands with fp32
 accumulation; the gated hidden tensor and y are each rounded to fp16 once,
