@@ -1,7 +1,9 @@
 """GPU parity of gtr_gla_fwd_ex's additions against the fp64 oracle: a nonzero
 initial state, and the RMSNorm + SiLU output-gate epilogue (0539edu.com page,
 appendix E.3.1), on every kernel family (fused one-chunk spans, parked spans,
-register-kept spans, streamed spans, generic fp16 and fp32) and scan order.
+register-kept spans, streamed spans, the span kernels at d_k = 64 and 32, the
+gla_fused.hip kernels at d_k = 32 zero-padded to 64, generic fp16 and fp32)
+and scan order.
 
 Bar: as for the plain forward, max|gpu - oracle| / max|oracle| over a tensor,
 5e-3 for fp16 and 1e-5 for fp32 inputs; the gated outputs are compared with
@@ -27,19 +29,30 @@ EPS = 1e-5
 
 BASE = gla_synth.WORKLOADS["img640"]
 TINY = gla_synth.WORKLOADS["tiny"]
-# (name, workload, policy, span env, register-kept env)
+# (name, workload, policy, span env, register-kept env, kernel-family env)
 CASES = [
-    ("fused-one", BASE.with_(H=3, seed=51), gla.POLICY_AUTO, None, None),
-    ("fused-parked", BASE.with_(B=2, H=2, grid_h=30, grid_w=30, seed=52), gla.POLICY_FUSED, "4", None),
-    ("fused-rk", BASE.with_(B=2, H=2, grid_h=30, grid_w=30, seed=53), gla.POLICY_FUSED, "3", "1"),
-    ("fused-streamed", BASE.with_(H=2, grid_h=40, grid_w=40, seed=54), gla.POLICY_FUSED, "3", None),
-    ("generic-fp16", BASE.with_(H=2, grid_h=24, grid_w=20, seed=55), gla.POLICY_GENERIC, None, None),
+    ("fused-one", BASE.with_(H=3, seed=51), gla.POLICY_AUTO, None, None, None),
+    ("fused-parked", BASE.with_(B=2, H=2, grid_h=30, grid_w=30, seed=52), gla.POLICY_FUSED, "4", None,
+     None),
+    ("fused-rk", BASE.with_(B=2, H=2, grid_h=30, grid_w=30, seed=53), gla.POLICY_FUSED, "3", "1", None),
+    ("fused-streamed", BASE.with_(H=2, grid_h=40, grid_w=40, seed=54), gla.POLICY_FUSED, "3", None,
+     None),
+    ("generic-fp16", BASE.with_(H=2, grid_h=24, grid_w=20, seed=55), gla.POLICY_GENERIC, None, None,
+     None),
     ("generic-fp32", TINY.with_(d_k=64, d_v=64, grid_h=20, grid_w=21, H=2, seed=56),
-     gla.POLICY_AUTO, None, None),
-    # the pages' operator shape, d_k = 32 (zero-padded to 64 inside the fused kernels)
-    ("fused-one-dk32", BASE.with_(d_k=32, H=3, seed=57), gla.POLICY_AUTO, None, None),
-    ("fused-rk-dk32", BASE.with_(d_k=32, B=2, H=2, grid_h=30, grid_w=30, seed=58),
-     gla.POLICY_FUSED, "3", "1"),
+     gla.POLICY_AUTO, None, None, None),
+    # the pages' operator shape, d_k = 32: the span kernels' 32-wide tiles (the default) ...
+    ("span-one-dk32", BASE.with_(d_k=32, H=3, seed=57), gla.POLICY_AUTO, None, None, None),
+    ("span-3-dk32", BASE.with_(d_k=32, B=2, H=2, grid_h=30, grid_w=30, seed=58),
+     gla.POLICY_FUSED, "3", None, None),
+    # ... and the gla_fused.hip kernels, zero-padded to 64
+    ("fused-one-dk32", BASE.with_(d_k=32, H=3, seed=60), gla.POLICY_AUTO, None, None, "1"),
+    ("fused-rk-dk32", BASE.with_(d_k=32, B=2, H=2, grid_h=30, grid_w=30, seed=61),
+     gla.POLICY_FUSED, "3", "1", "1"),
+    # the span kernels at d_k = 64
+    ("span-one-dk64", BASE.with_(H=3, seed=62), gla.POLICY_AUTO, None, None, "2"),
+    ("span-3-dk64", BASE.with_(B=2, H=2, grid_h=30, grid_w=30, seed=63), gla.POLICY_FUSED, "3", None,
+     "2"),
 ]
 
 
@@ -49,8 +62,8 @@ def clean_env():
     gla.load_library()
     yield
     gla.gtr_gla_set_policy(gla.POLICY_AUTO)
-    os.environ.pop("GTR_GLA_SPAN", None)
-    os.environ.pop("GTR_GLA_RK", None)
+    for key in ("GTR_GLA_SPAN", "GTR_GLA_RK", "GTR_GLA_KERNEL"):
+        os.environ.pop(key, None)
 
 
 def say(*a):
@@ -62,9 +75,9 @@ def dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def setup(policy, span, rk):
+def setup(policy, span, rk, kernel=None):
     gla.gtr_gla_set_policy(policy)
-    for key, val in (("GTR_GLA_SPAN", span), ("GTR_GLA_RK", rk)):
+    for key, val in (("GTR_GLA_SPAN", span), ("GTR_GLA_RK", rk), ("GTR_GLA_KERNEL", kernel)):
         if val is None:
             os.environ.pop(key, None)
         else:
@@ -91,11 +104,11 @@ def errs(tag, w, d, o, s, o_ref, s_ref):
 
 
 @pytest.mark.parametrize("d", DIRS)
-@pytest.mark.parametrize("name,w,policy,span,rk", CASES, ids=[c[0] for c in CASES])
-def test_initial_state(name, w, policy, span, rk, d):
+@pytest.mark.parametrize("name,w,policy,span,rk,kernel", CASES, ids=[c[0] for c in CASES])
+def test_initial_state(name, w, policy, span, rk, kernel, d):
     arrays = gla_synth.generate(w)
     S0, _, _ = extras(w, w.seed + 100)
-    setup(policy, span, rk)
+    setup(policy, span, rk, kernel)
     q, k, v, lg = [dev(a) for a in arrays]
     o, s = gla.forward(q, k, v, lg, w.grid_h, w.grid_w, d, initial_state=dev(S0))
     torch.cuda.synchronize()
@@ -104,11 +117,11 @@ def test_initial_state(name, w, policy, span, rk, d):
 
 
 @pytest.mark.parametrize("d", DIRS)
-@pytest.mark.parametrize("name,w,policy,span,rk", CASES, ids=[c[0] for c in CASES])
-def test_output_gate(name, w, policy, span, rk, d):
+@pytest.mark.parametrize("name,w,policy,span,rk,kernel", CASES, ids=[c[0] for c in CASES])
+def test_output_gate(name, w, policy, span, rk, kernel, d):
     arrays = gla_synth.generate(w)
     _, gate, nw = extras(w, w.seed + 200)
-    setup(policy, span, rk)
+    setup(policy, span, rk, kernel)
     q, k, v, lg = [dev(a) for a in arrays]
     y, s = gla.forward(q, k, v, lg, w.grid_h, w.grid_w, d, gate=dev(gate), norm_weight=dev(nw),
                        norm_eps=EPS)
@@ -118,14 +131,15 @@ def test_output_gate(name, w, policy, span, rk, d):
     errs(f"gate/{name}", w, d, y.cpu().numpy(), s.cpu().numpy(), y_ref, s_ref)
 
 
-@pytest.mark.parametrize("name,w,policy,span,rk", CASES[:3], ids=[c[0] for c in CASES[:3]])
-def test_both_additions_and_in_place_chaining(name, w, policy, span, rk):
+@pytest.mark.parametrize("name,w,policy,span,rk,kernel", CASES[:3] + CASES[-2:],
+                         ids=[c[0] for c in CASES[:3] + CASES[-2:]])
+def test_both_additions_and_in_place_chaining(name, w, policy, span, rk, kernel):
     """Two calls over the top and bottom rows of an L->R scan, the second from the
     first's final state updated in place, with the output gate: the outputs and
     final state of one scan of the whole grid (oracle), and of one GPU call."""
     arrays = gla_synth.generate(w)
     _, gate, nw = extras(w, w.seed + 300)
-    setup(policy, span, rk)
+    setup(policy, span, rk, kernel)
     gh, gw, h1 = w.grid_h, w.grid_w, w.grid_h // 3
     top = lambda x: np.ascontiguousarray(x[:, : h1 * gw])
     bot = lambda x: np.ascontiguousarray(x[:, h1 * gw:])
