@@ -2,9 +2,10 @@
 
 * Direction folding changes addresses only: the output for scan order `dir`
   equals the left-to-right output on the correspondingly reversed/transposed
-  inputs, bit for bit, for the generic and the fused kernels alike (the two
-  calls have the same B, H and L, so the same plan, chunk contents and
-  arithmetic; the exchange's fold order is fixed).
+  inputs, bit for bit, for the generic kernels and both fused families (the
+  gla_fused.hip kernels and the span kernels, each at d_k = 64 and 32) alike
+  (the two calls have the same B, H and L, so the same plan, chunk contents
+  and arithmetic; the exchange's fold order is fixed).
 * Repeated calls agree bit for bit, and workspaces are reusable across calls
   and shapes (per-slot epochs; a layout change re-initialises the workspace).
 * The caller-managed workspace entry point equals the library-managed one,
@@ -23,7 +24,12 @@ pytestmark = pytest.mark.gpu
 
 W = gla_synth.WORKLOADS["img1024"]
 RAG = W.with_(name="rag", B=2, H=3, grid_h=30, grid_w=34, seed=71)
+RAG32 = RAG.with_(name="rag32", d_k=32, seed=72)
 TIGHT = 1e-3
+# (policy, GTR_GLA_KERNEL): generic; the fused kernels' default family for the
+# key dim; the gla_fused.hip kernels; the span kernels
+FAMILIES = [(gla.POLICY_GENERIC, None), (gla.POLICY_AUTO, None), (gla.POLICY_AUTO, "1"),
+            (gla.POLICY_AUTO, "2")]
 
 
 @pytest.fixture(autouse=True)
@@ -60,14 +66,16 @@ def tr(x, gh, gw):
     return x.reshape(B, gh, gw, H, d).transpose(0, 2, 1, 3, 4).reshape(B, L, H, d).copy()
 
 
-@pytest.mark.parametrize("policy", [gla.POLICY_AUTO, gla.POLICY_GENERIC])
-@pytest.mark.parametrize("w", [W, RAG], ids=["img1024", "ragged"])
-def test_direction_folding(w, policy):
+@pytest.mark.parametrize("policy,family", FAMILIES, ids=["generic", "auto", "fused", "span"])
+@pytest.mark.parametrize("w", [W, RAG, RAG32], ids=["img1024", "ragged", "ragged-dk32"])
+def test_direction_folding(w, policy, family, monkeypatch):
     gla.gtr_gla_set_policy(policy)
+    if family is not None:
+        monkeypatch.setenv("GTR_GLA_KERNEL", family)
     bitwise = True
     x = gla_synth.generate(w)
     gh, gw = w.grid_h, w.grid_w
-    print(f"[case] direction folding {w.name} policy={policy}", flush=True)
+    print(f"[case] direction folding {w.name} policy={policy} family={family}", flush=True)
     o, s = fwd(x, gh, gw, "r2l")
     o2, s2 = fwd([rev(a) for a in x], gh, gw, "l2r")
     assert same(o, rev(o2), bitwise) and same(s, s2, bitwise)
