@@ -66,8 +66,14 @@ def eager_other():
     assert torch.isfinite(o.float()).all()
 
 
-def test_graph_fwd_ex_caller_workspace():
-    w = W
+@pytest.mark.parametrize("d_k,family", [(64, None), (32, None), (64, "2")],
+                         ids=["dk64-fused", "dk32-span", "dk64-span"])
+def test_graph_fwd_ex_caller_workspace(d_k, family, monkeypatch):
+    """On the gla_fused.hip kernels (d_k = 64 by default) and the span kernels
+    (d_k = 32 by default, d_k = 64 forced)."""
+    if family is not None:
+        monkeypatch.setenv("GTR_GLA_KERNEL", family)
+    w = W.with_(d_k=d_k)
     q, k, v, lg = [dev(a) for a in gla_synth.generate(w)]
     rng = np.random.default_rng(83)
     s0 = dev((0.5 * rng.standard_normal((w.B, w.H, w.d_k, w.d_v))).astype(np.float32))
