@@ -87,32 +87,43 @@ def test_direction_folding(w, policy, family, monkeypatch):
     assert same(o, tr(o2, gw, gh), bitwise) and same(s, s2, bitwise)
 
 
-@pytest.mark.parametrize("policy", [gla.POLICY_AUTO, gla.POLICY_GENERIC])
-def test_repeat_calls_and_shape_changes(policy):
+@pytest.mark.parametrize("policy,family", FAMILIES, ids=["generic", "auto", "fused", "span"])
+def test_repeat_calls_and_shape_changes(policy, family, monkeypatch):
+    """Alternating shapes (and, with the default family, key dims: d_k = 32
+    takes the span kernels) on the library's workspace."""
     gla.gtr_gla_set_policy(policy)
+    if family is not None:
+        monkeypatch.setenv("GTR_GLA_KERNEL", family)
     bitwise = True
     big = gla_synth.generate(W)
     small = gla_synth.generate(RAG)
-    print(f"[case] repeat calls policy={policy}", flush=True)
+    small32 = gla_synth.generate(RAG32)
+    print(f"[case] repeat calls policy={policy} family={family}", flush=True)
     o0, s0 = fwd(big, W.grid_h, W.grid_w, "t2b")
     r0 = fwd(small, RAG.grid_h, RAG.grid_w, "l2r")
+    q0 = fwd(small32, RAG32.grid_h, RAG32.grid_w, "b2t")
     for _ in range(3):
         o, s = fwd(big, W.grid_h, W.grid_w, "t2b")
         assert same(o, o0, bitwise) and same(s, s0, bitwise)
         r = fwd(small, RAG.grid_h, RAG.grid_w, "l2r")
         assert same(r[0], r0[0], bitwise) and same(r[1], r0[1], bitwise)
+        q = fwd(small32, RAG32.grid_h, RAG32.grid_w, "b2t")
+        assert same(q[0], q0[0], bitwise) and same(q[1], q0[1], bitwise)
 
 
-def test_many_back_to_back_launches():
+@pytest.mark.parametrize("w", [W, W.with_(name="img1024_dk32", d_k=32)], ids=["dk64", "dk32"])
+def test_many_back_to_back_launches(w):
     """Launch after launch without host synchronisation: the ticket/epoch
-    protocol must hand a clean workspace to every launch."""
-    x = [dev(a) for a in gla_synth.generate(W)]
+    protocol must hand a clean workspace to every launch (d_k = 32: the span
+    kernels)."""
+    x = [dev(a) for a in gla_synth.generate(w)]
     B, L, H, dk = x[0].shape
+    dv = x[2].shape[3]
     outs = []
     for i in range(20):
-        o = torch.empty((B, L, H, dk), dtype=torch.float16, device="cuda")
-        s = torch.empty((B, H, dk, dk), dtype=torch.float32, device="cuda")
-        gla.gtr_gla_fwd(*x, B, H, W.grid_h, W.grid_w, dk, dk, i % 4, 64, o, s)
+        o = torch.empty((B, L, H, dv), dtype=torch.float16, device="cuda")
+        s = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+        gla.gtr_gla_fwd(*x, B, H, w.grid_h, w.grid_w, dk, dv, i % 4, 64, o, s)
         outs.append((i % 4, o, s))
     torch.cuda.synchronize()
     first = {}
