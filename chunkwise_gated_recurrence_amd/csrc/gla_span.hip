@@ -1277,6 +1277,7 @@ FusedPlan span_plan(const Shape& s, int span_override, long long cap_override, i
 {
     FusedPlan p{};
     p.family = 2;
+    p.dk = s.d_k;   // the state rows set the exchange's slot layout (and its layout word)
     p.keep = true;
     p.rk = false;
     p.var = var;

@@ -194,8 +194,14 @@ def test_non_default_stream():
         q, k, v, lg = [dev(a) for a in x]
         o, s = gla.forward(q, k, v, lg, RAG.grid_h, RAG.grid_w, "b2t")
     st.synchronize()
-    assert same(o.cpu().numpy().astype(np.float64), ref_o, True)
-    assert same(s.cpu().numpy(), ref_s, True)
+    o, s = o.cpu().numpy().astype(np.float64), s.cpu().numpy()
+    o_or, s_or = oracle.recurrent(*x, RAG.grid_h, RAG.grid_w, "b2t")
+    print(f"[case] default stream err_o={oracle.rel_err(ref_o, o_or):.3e} "
+          f"err_S={oracle.rel_err(ref_s, s_or):.3e}; other stream err_o={oracle.rel_err(o, o_or):.3e} "
+          f"err_S={oracle.rel_err(s, s_or):.3e}", flush=True)
+    assert oracle.rel_err(ref_o, o_or) <= 5e-3 and oracle.rel_err(o, o_or) <= 5e-3
+    assert same(o, ref_o, True)
+    assert same(s, ref_s, True)
 
 
 def test_null_final_state_is_allowed():

@@ -245,3 +245,43 @@ def test_library_workspace_alternates_kernel_families():
         check_oracle(arrays, w, 1, o, s)
         assert gla.gtr_gla_workspace_status() == gla.OK
     assert plans["1"][1:] == plans["2"][1:] and plans["1"][0] != plans["2"][0]
+
+
+ALT64 = gla_synth.WORKLOADS["img1024"].with_(name="alt64", B=2, H=3, grid_h=30, grid_w=34, seed=95)
+ALT32 = ALT64.with_(name="alt32", d_k=32, seed=96)
+
+
+@pytest.mark.parametrize("own_ws", [False, True], ids=["library-ws", "caller-ws"])
+def test_span_key_widths_alternate_on_one_workspace(own_ws):
+    """Span-kernel calls at d_k = 64 and 32 with the same spans per sequence and
+    sequences per launch (16 and 6 here) hold differently sized exchange slots,
+    so their exchange layouts must differ: a call after one of the other key
+    width then starts from a re-initialised workspace instead of reading the
+    incoming-state words that a call two launches back left, whose tag parity
+    matches (a regression: the span plans once carried the default key width in
+    their layout word). The scan order changes from call to call, so that
+    stale states would give wrong outputs."""
+    os.environ["GTR_GLA_KERNEL"] = "2"
+    p64 = gla.gtr_gla_plan(ALT64.B, ALT64.H, ALT64.grid_h, ALT64.grid_w, 64, 64, 64, 0)
+    p32 = gla.gtr_gla_plan(ALT32.B, ALT32.H, ALT32.grid_h, ALT32.grid_w, 32, 64, 64, 0)
+    assert p64 == p32 and p64[0] == 4, (p64, p32)   # same kernel family, span and grid
+    ws = None
+    if own_ws:
+        nbytes = max(gla.gtr_gla_workspace_bytes(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 64, 0)
+                     for w in (ALT64, ALT32))
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        gla.gtr_gla_workspace_init(ws, nbytes)
+    data = {w.name: (gla_synth.generate(w), w) for w in (ALT64, ALT32)}
+    for i, (name, d) in enumerate([("alt64", 0), ("alt32", 3), ("alt64", 3), ("alt32", 2),
+                                   ("alt64", 1), ("alt64", 2), ("alt32", 0), ("alt64", 0)]):
+        arrays, w = data[name]
+        x = [dev(a) for a in arrays]
+        o, s = outputs(w)
+        print(f"[case] alternate key widths {'caller' if own_ws else 'library'} ws call {i}: "
+              f"{name} dir={d}", flush=True)
+        if own_ws:
+            ws_call(x, w, d, ws, o, s)
+        else:
+            o, s = gla.forward(*x, w.grid_h, w.grid_w, d)
+        torch.cuda.synchronize()
+        check_oracle(arrays, w, d, o, s)
