@@ -76,15 +76,17 @@ int rk_override_from_env()
 // GTR_GLA_KERNEL selects the fused kernel family: 1 the kernels of
 // gla_fused.hip, 2 the span kernels (gla_span.hip) for the calls they support
 // (the others keep gla_fused.hip: the low-rank gate, very long sequences).
-// Unset: the span kernels for 32-wide keys (which they hold natively, with
-// half the key-side bytes and work of the padded 64-wide tiles), gla_fused.hip
-// for 64-wide ones (measured faster there on most image sizes).
-bool span_kernels_allowed(int d_k)
+// Unset (0): the span kernels for 32-wide keys (which they hold natively, with
+// half the key-side bytes and work of the padded 64-wide tiles), and for
+// 64-wide keys when each sequence takes at most kSpanFamilyMaxSpans spans
+// (many sequences, few spans each: measured 2-6 % faster there); gla_fused.hip
+// for the other 64-wide calls (few sequences cut into many spans: 2-4 % faster).
+int kernel_family_env()
 {
     const char* env = std::getenv("GTR_GLA_KERNEL");
-    if (env && env[0]) return std::atoi(env) == 2;
-    return d_k == 32;
+    return env && env[0] ? std::atoi(env) : 0;
 }
+constexpr int kSpanFamilyMaxSpans = 16;
 
 long long resident_cap_from_env()
 {
@@ -203,8 +205,12 @@ Choice choose(const Shape& s, bool is_fp32, int policy, int var = 0)
         c.kernel = kFused;
         const int span = (policy == GTR_GLA_POLICY_FUSED_ONE) ? 1 : span_override_from_env();
         c.plan.family = 0;
-        if (!lowrank && gtrgla::span_supported(s) && span_kernels_allowed(s.d_k))
-            c.plan = gtrgla::span_plan(s, span, resident_cap_from_env(), var);
+        const int fam = kernel_family_env();
+        if (!lowrank && gtrgla::span_supported(s) && (fam == 2 || fam == 0)) {
+            const FusedPlan p = gtrgla::span_plan(s, span, resident_cap_from_env(), var);
+            if (fam == 2 || s.d_k == 32 || (p.family == 2 && p.n_spans <= kSpanFamilyMaxSpans))
+                c.plan = p;
+        }
         if (c.plan.family != 2) c.plan = gtrgla::fused_plan(s, span, rk_override_from_env(), var);
         c.base_bytes = gtrgla::fused_workspace_bytes(s, c.plan);
     } else {

@@ -271,8 +271,9 @@ int gtr_gla_get_policy(void);
  * may be NULL. kernel_out: 1 generic; 2 fused (one-chunk, parked or streamed
  * spans) and 3 fused with register-kept spans; 4 the span kernels (spans of
  * 1..7 chunks, outputs kept in registers through the exchange), the default
- * for d_k = 32 (the environment variable GTR_GLA_KERNEL = 2 takes them for
- * d_k = 64 too, 1 takes kernels 2 and 3 for both).
+ * for d_k = 32, and for d_k = 64 when each sequence takes at most 16 spans
+ * (many short sequences); the environment variable GTR_GLA_KERNEL = 2 takes
+ * them for every d_k = 64 call, 1 takes kernels 2 and 3 for both key widths.
  * span_out: chunks per workgroup (fused) or 1. grid_out: workgroups of the
  * main kernel (of one launch, when the sequences need several).
  */

@@ -31,12 +31,12 @@ BASE = gla_synth.WORKLOADS["img640"]
 TINY = gla_synth.WORKLOADS["tiny"]
 # (name, workload, policy, span env, register-kept env, kernel-family env)
 CASES = [
-    ("fused-one", BASE.with_(H=3, seed=51), gla.POLICY_AUTO, None, None, None),
+    ("fused-one", BASE.with_(H=3, seed=51), gla.POLICY_AUTO, None, None, "1"),
     ("fused-parked", BASE.with_(B=2, H=2, grid_h=30, grid_w=30, seed=52), gla.POLICY_FUSED, "4", None,
-     None),
-    ("fused-rk", BASE.with_(B=2, H=2, grid_h=30, grid_w=30, seed=53), gla.POLICY_FUSED, "3", "1", None),
+     "1"),
+    ("fused-rk", BASE.with_(B=2, H=2, grid_h=30, grid_w=30, seed=53), gla.POLICY_FUSED, "3", "1", "1"),
     ("fused-streamed", BASE.with_(H=2, grid_h=40, grid_w=40, seed=54), gla.POLICY_FUSED, "3", None,
-     None),
+     "1"),
     ("generic-fp16", BASE.with_(H=2, grid_h=24, grid_w=20, seed=55), gla.POLICY_GENERIC, None, None,
      None),
     ("generic-fp32", TINY.with_(d_k=64, d_v=64, grid_h=20, grid_w=21, H=2, seed=56),

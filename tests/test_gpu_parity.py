@@ -107,14 +107,15 @@ def test_generic_policy_parity(name, d):
 
 
 @pytest.mark.parametrize("name,plan", [("img640", (2, 1, 150)), ("img1024", (3, 2, 384)),
-                                       ("batched640", (3, 3, 432)), ("long2048", (3, 7, 444)),
+                                       ("batched640", (4, 3, 432)), ("long2048", (3, 7, 444)),
                                        ("img640_dk32", (4, 1, 150))])
 def test_default_plans(name, plan):
     """The launch policy's choice for the benchmark workloads (kernel 2: one
     chunk per workgroup while the grid fits at two per CU; kernel 3: the
     shortest register-kept span whose grid is resident; kernel 4, the span
-    kernels, for 32-wide keys). The grids assume the MI355X's 256 CUs and take
-    at most 7/8 of the resident slots."""
+    kernels, for 32-wide keys, and for 64-wide keys when a sequence takes at
+    most 16 spans: batched640's 48 sequences of 9 spans). The grids assume the
+    MI355X's 256 CUs and take at most 7/8 of the resident slots."""
     w = gla_synth.WORKLOADS[name]
     assert gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, w.chunk, 0) == plan
 
