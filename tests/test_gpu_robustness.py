@@ -285,3 +285,41 @@ def test_span_key_widths_alternate_on_one_workspace(own_ws):
             o, s = gla.forward(*x, w.grid_h, w.grid_w, d)
         torch.cuda.synchronize()
         check_oracle(arrays, w, d, o, s)
+
+
+def test_mixed_call_history_matches_the_oracle():
+    """A call history that mixes kernel families, key widths, shapes of equal
+    and unequal exchange layouts, scan orders and the two streams' library
+    workspaces, each call checked against the oracle (a repeat of the same call
+    cannot show stale exchange words: they would hold the same values)."""
+    shapes = {
+        "a64": ALT64, "a32": ALT32,
+        "b64": ALT64.with_(name="b64", grid_h=34, grid_w=30, seed=97),      # the same layout as a64
+        "c64": ALT64.with_(name="c64", B=1, H=4, grid_h=20, grid_w=40, seed=98),
+    }
+    data = {k: gla_synth.generate(w) for k, w in shapes.items()}
+    side = torch.cuda.Stream()
+    history = [("a64", 0, None, None), ("b64", 3, None, None), ("a32", 1, None, None),
+               ("a64", 2, "2", None), ("c64", 3, None, None), ("a64", 1, "1", None),
+               ("b64", 0, None, side), ("a32", 3, "2", side), ("a64", 3, None, side),
+               ("a64", 2, None, None), ("c64", 0, "2", None), ("a32", 2, None, None),
+               ("b64", 1, None, None), ("a64", 0, "2", None)]
+    for i, (name, d, family, stream) in enumerate(history):
+        w, arrays = shapes[name], data[name]
+        if family is None:
+            os.environ.pop("GTR_GLA_KERNEL", None)
+        else:
+            os.environ["GTR_GLA_KERNEL"] = family
+        plan = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 64, 0)
+        print(f"[case] history call {i}: {name} dir={d} family={family} "
+              f"stream={'side' if stream is not None else 'default'} plan={plan}", flush=True)
+        x = [dev(a) for a in arrays]
+        if stream is None:
+            o, s = gla.forward(*x, w.grid_h, w.grid_w, d)
+            torch.cuda.synchronize()
+        else:
+            stream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(stream):
+                o, s = gla.forward(*x, w.grid_h, w.grid_w, d)
+            stream.synchronize()
+        check_oracle(arrays, w, d, o, s)
