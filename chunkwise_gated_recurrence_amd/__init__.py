@@ -288,8 +288,8 @@ def gtr_gla_get_policy() -> int:
 def gtr_gla_plan(B, H, grid_h, grid_w, d_k, d_v, chunk, is_fp32,
                  lowrank: bool = False) -> Tuple[int, int, int]:
     """(kernel, span, grid) of the launch a call would make: kernel 1 generic, 2 fused,
-    3 fused with the outputs kept in registers (long sequences). lowrank: of a
-    gtr_gla_fwd_lowrank call (gtr_gla_plan_lowrank)."""
+    3 fused with the outputs kept in registers (long sequences), 4 the span
+    kernels. lowrank: of a gtr_gla_fwd_lowrank call (gtr_gla_plan_lowrank)."""
     kern, span, grid = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     lib = load_library()
     fn = lib.gtr_gla_plan_lowrank if lowrank else lib.gtr_gla_plan

@@ -323,3 +323,59 @@ def test_mixed_call_history_matches_the_oracle():
                 o, s = gla.forward(*x, w.grid_h, w.grid_w, d)
             stream.synchronize()
         check_oracle(arrays, w, d, o, s)
+
+
+@pytest.mark.parametrize("span,rk,family", [("1", None, "1"), ("2", "1", "1"), ("1", None, "2"),
+                                            ("3", None, "2")],
+                         ids=["one_chunk", "register_kept", "span1", "span3"])
+def test_multi_launch_with_initial_state_and_gate(span, rk, family):
+    """The multi-launch loop with the optional inputs that are indexed per
+    sequence (initial states, final states) or per token (the output gate): the
+    later launches must take their sequences' rows, not the first launch's."""
+    w = MULTI
+    os.environ["GTR_GLA_SPAN"] = span
+    if rk:
+        os.environ["GTR_GLA_RK"] = rk
+    os.environ["GTR_GLA_MAX_RESIDENT"] = "6"
+    os.environ["GTR_GLA_KERNEL"] = family
+    kern, sp, grid = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 64, 0)
+    n_spans = -(-(-(-w.L // 64)) // sp)
+    assert grid < w.B * w.H * n_spans, (kern, sp, grid)
+    arrays = gla_synth.generate(w)
+    rng = np.random.default_rng(94)
+    S0 = (0.5 * rng.standard_normal((w.B, w.H, w.d_k, w.d_v))).astype(np.float32)
+    gate = (2.0 * rng.standard_normal((w.B, w.L, w.H, w.d_v))).astype(np.float16)
+    nw = rng.uniform(0.5, 1.5, w.d_v).astype(np.float32)
+    x = [dev(a) for a in arrays]
+    for d in range(4):
+        print(f"[case] multi-launch with additions span={span} family={family} dir={d}", flush=True)
+        y, s = gla.forward(*x, w.grid_h, w.grid_w, d, initial_state=dev(S0), gate=dev(gate),
+                           norm_weight=dev(nw), norm_eps=1e-5)
+        torch.cuda.synchronize()
+        o_ref, s_ref = oracle.recurrent_init(*arrays, S0, w.grid_h, w.grid_w, d)
+        y_ref = oracle.rmsnorm_gate(o_ref, gate, nw, 1e-5)
+        ey = oracle.rel_err(y.cpu().numpy().astype(np.float64), y_ref)
+        es = oracle.rel_err(s.cpu().numpy(), s_ref)
+        assert ey <= TOL and es <= TOL, (ey, es)
+
+
+def test_multi_launch_lowrank():
+    """The low-rank gate (projection per token, gate per head) across several
+    launches of the fused kernels."""
+    w = MULTI
+    C = 96
+    os.environ["GTR_GLA_MAX_RESIDENT"] = "6"
+    os.environ["GTR_GLA_SPAN"] = "1"
+    kern, sp, grid = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, 64, 0,
+                                      lowrank=True)
+    n_spans = -(-(-(-w.L // 64)) // sp)
+    assert grid < w.B * w.H * n_spans, (kern, sp, grid)
+    q, k, v, _ = gla_synth.generate(w)
+    xin, w1, w2, bias = gla_synth.generate_lowrank(w, C, 95)
+    lg = oracle.lowrank_gate(xin, w1, w2, bias, 1.0 / 16).reshape(w.B, w.L, w.H, w.d_k)
+    for d in range(4):
+        print(f"[case] multi-launch lowrank dir={d}", flush=True)
+        out, fs = gla.forward_lowrank(dev(q), dev(k), dev(v), dev(xin), dev(w1), dev(w2), dev(bias),
+                                      w.grid_h, w.grid_w, d, inv_tau=1.0 / 16)
+        torch.cuda.synchronize()
+        check_oracle((q, k, v, lg), w, d, out, fs)
