@@ -258,7 +258,10 @@ struct Lds {
     } stage[NS];
     unsigned int tags[kMaxSpans];   // expected tag of every span slot of the sequence
     unsigned int hdr[4];        // the workspace header, staged at the start
-    int stale, expired, poison;
+    // the owners' poll rounds: per-wave "a word was stale" and the deadline,
+    // double-buffered by round parity (one barrier per round)
+    int stale_w[2][4], expired_r[2];
+    int poison;
 
     static constexpr int kTin = kDV * DK * 2;   // incoming state, fp16 [j][permuted i]
     __device__ unsigned char* region() { return reinterpret_cast<unsigned char*>(&stage[0]); }
@@ -836,6 +839,7 @@ __device__ bool exchange(const SpanArgs& a, L& sm, int local_seq, int seq, int j
         const __amdgpu_buffer_rsrc_t rf = final_rsrc<DK>(a, seq);
         float* dl = reinterpret_cast<float*>(sm.region());   // decays [ns][nr] (<= 256)
         const int nd = ns << lr;
+        int round = 0;   // poll rounds, counted across the passes (the flags' parity)
         for (int ps = 0; ps < f.n_pass; ++ps) {
             const int el = ((ps << f.lp) + pc) << 2;         // my piece, in the slice
             const int e = (j << lo) + el;                      // ... in the state
@@ -881,15 +885,19 @@ __device__ bool exchange(const SpanArgs& a, L& sm, int local_seq, int seq, int j
                         if (dk < nd) dl[dk] = ll_value(wd[x]);
                     }
                 }
-                if (tid == 0) {
-                    sm.stale = 0;
-                    sm.expired = (now_ticks() - t_start) > a.wait_ticks ? 1 : 0;
-                }
+                // Round r writes the flags of parity r & 1 and reads them after
+                // the one barrier; a wave writes that parity again only in round
+                // r + 2, after the barrier of round r + 1, which every wave
+                // reaches only after reading round r's flags.
+                const int pr = round & 1;
+                const bool wave_ok = __all(mine);   // (every lane active)
+                if (lane == 0) sm.stale_w[pr][w] = wave_ok ? 0 : 1;
+                if (tid == 0) sm.expired_r[pr] = (now_ticks() - t_start) > a.wait_ticks ? 1 : 0;
                 lds_barrier();
-                if (!__all(mine) && lane == 0) sm.stale = 1;
-                lds_barrier();
-                const bool stale = sm.stale != 0, expired = sm.expired != 0;
-                lds_barrier();   // every thread has read the flags before they are reset
+                const bool stale =
+                    (sm.stale_w[pr][0] | sm.stale_w[pr][1] | sm.stale_w[pr][2] | sm.stale_w[pr][3]) != 0;
+                const bool expired = sm.expired_r[pr] != 0;
+                ++round;
                 if (!stale) break;
                 if (expired) {
                     gave_up = true;
