@@ -2,7 +2,10 @@
 gtr_gla_fwd (library-allocated workspace) through the C ABI: two calls in a
 row, the second with a smaller input, each bit for bit equal to the existing
 entry point (the same kernels and plan) and within the fp16 bar of the
-oracle; the scratch re-initialises itself across the layout change."""
+oracle; the scratch re-initialises itself across the layout change. Then the
+same small shape at d_k = 32 and again at d_k = 64 (the span kernels, equal
+spans and sequences per launch, exchange slots of different sizes), in other
+scan orders, so that the scratch's layout follows the key width too."""
 import ctypes
 
 import numpy as np
@@ -19,6 +22,7 @@ pytestmark = pytest.mark.gpu
 BIG = gla_synth.WORKLOADS["img640"].with_(name="noalloc_big", seed=97)        # 6 heads, 40x40
 SMALL = gla_synth.WORKLOADS["img640"].with_(name="noalloc_small", H=2, grid_h=24, grid_w=20,
                                             seed=98)
+SMALL32 = SMALL.with_(name="noalloc_small32", d_k=32, seed=99)
 
 
 def _call(fn, x, w, d, o, s):
@@ -31,7 +35,7 @@ def _call(fn, x, w, d, o, s):
 
 def test_noalloc_matches_the_allocating_entry_point():
     assert torch.cuda.is_available(), "the gpu tests need an MI355X"
-    for w, d in ((BIG, 2), (SMALL, 1)):
+    for w, d in ((BIG, 2), (SMALL, 1), (SMALL32, 3), (SMALL, 0)):
         arrays = gla_synth.generate(w)
         x = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in arrays]
         o_ref = torch.empty((w.B, w.L, w.H, w.d_v), dtype=torch.float16, device="cuda")
